@@ -1,0 +1,226 @@
+"""Python binding of libcbattn.so: ragged paged attention and the paged KV-cache write on MI355X.
+
+Each function here has the name of the C entry point it calls (see include/cbattn.h) and does
+argument marshalling only: it checks dtypes, devices and contiguity of torch tensors, passes
+their device pointers and the current HIP stream, and turns a non-zero status into CBError.
+Every step of the computation runs in the library's HIP kernels. There is no fallback: if the
+library is missing or fails to load, importing this package raises.
+
+    import ragged_paged_kv_amd as cb
+    cb.cb_slot_mapping(cu, kv_lens, tables, slots, block_size)
+    cb.cb_cache_write(k, v, slots, k_cache, v_cache)
+    ws = cb.alloc_workspace(...)
+    cb.cb_paged_attention(q, cu, kv_lens, tables, k_cache, v_cache, out, scale, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from ._build import LIB_PATH
+
+__all__ = [
+    "CBError", "LIB_PATH", "lib", "cb_status_string", "cb_last_error", "cb_slot_mapping",
+    "cb_cache_write", "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens",
+    "cb_paged_attention", "cb_split_kv_reduce", "cb_validate_batch", "alloc_workspace",
+    "EXPORTED_SYMBOLS",
+]
+
+EXPORTED_SYMBOLS = (
+    "cb_status_string", "cb_last_error", "cb_slot_mapping", "cb_cache_write",
+    "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens", "cb_paged_attention",
+    "cb_split_kv_reduce", "cb_validate_batch",
+)
+
+
+class CBError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {cb_status_string(status)} ({status}): {detail}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built. Build it with `python ragged_paged_kv_amd/_build.py` "
+            "(needs ROCm hipcc).")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_sig = {
+    "cb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "cb_last_error": (ctypes.c_char_p, []),
+    "cb_slot_mapping": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p]),
+    "cb_cache_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _p]),
+    "cb_paged_attention_workspace_size": (_sz, [_i32] * 9),
+    "cb_paged_attention_split_tokens": (_i32, [_i32] * 4),
+    "cb_paged_attention": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _f, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, _i64, _i32, _i32, _i32, _p, _sz, _p]),
+    "cb_split_kv_reduce": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
+    "cb_validate_batch": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _i32]),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def cb_status_string(status: int) -> str:
+    return lib.cb_status_string(int(status)).decode()
+
+
+def cb_last_error() -> str:
+    return lib.cb_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise CBError(status, where, cb_last_error())
+
+
+# ---------------------------------------------------------------------------------------------
+# torch marshalling (torch is imported lazily so that the host-only entry points work without it)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name, dtype, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def cb_slot_mapping(cu_seqlens_q, kv_lens, block_tables, slot_mapping, block_size: int,
+                    stream=None):
+    torch = _torch()
+    S = kv_lens.shape[0]
+    T = slot_mapping.shape[0]
+    _check(lib.cb_slot_mapping(_dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1),
+                               _dev(kv_lens, "kv_lens", torch.int32, 1),
+                               _dev(block_tables, "block_tables", torch.int32, 2), S, T,
+                               block_tables.shape[1], int(block_size),
+                               _dev(slot_mapping, "slot_mapping", torch.int32, 1), _stream(stream)),
+           "cb_slot_mapping")
+
+
+def cb_cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    torch = _torch()
+    T, Hkv, D = k.shape
+    NB, bs = k_cache.shape[0], k_cache.shape[1]
+    if tuple(v.shape) != (T, Hkv, D) or tuple(k_cache.shape) != (NB, bs, Hkv, D) \
+            or tuple(v_cache.shape) != tuple(k_cache.shape) or slot_mapping.shape[0] != T:
+        raise ValueError("cb_cache_write: inconsistent shapes")
+    _check(lib.cb_cache_write(_dev(k, "k", torch.bfloat16, 3), _dev(v, "v", torch.bfloat16, 3),
+                              _dev(slot_mapping, "slot_mapping", torch.int32, 1),
+                              _dev(k_cache, "k_cache", torch.bfloat16, 4),
+                              _dev(v_cache, "v_cache", torch.bfloat16, 4), T, Hkv, D, bs, NB,
+                              _stream(stream)),
+           "cb_cache_write")
+
+
+def cb_paged_attention_workspace_size(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                                      block_size, max_q_len, max_kv_len, kv_split_tokens=0) -> int:
+    return int(lib.cb_paged_attention_workspace_size(num_seqs, num_tokens, num_q_heads,
+                                                     num_kv_heads, head_dim, block_size,
+                                                     max_q_len, max_kv_len, kv_split_tokens))
+
+
+def cb_paged_attention_split_tokens(num_seqs, num_kv_heads, max_kv_len, kv_split_tokens=0) -> int:
+    return int(lib.cb_paged_attention_split_tokens(num_seqs, num_kv_heads, max_kv_len,
+                                                   kv_split_tokens))
+
+
+def alloc_workspace(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                    max_q_len, max_kv_len, kv_split_tokens=0, device="cuda"):
+    """A uint8 device tensor of the size cb_paged_attention needs (torch allocations are
+    at least 256-byte aligned)."""
+    n = cb_paged_attention_workspace_size(num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                                          head_dim, block_size, max_q_len, max_kv_len,
+                                          kv_split_tokens)
+    return _torch().empty(max(n, 256), dtype=_torch().uint8, device=device)
+
+
+def cb_paged_attention(q_packed, cu_seqlens_q, kv_lens, block_tables, k_cache, v_cache, out,
+                       scale: float, max_q_len: int, max_kv_len: int, workspace,
+                       kv_split_tokens: int = 0, stream=None):
+    torch = _torch()
+    T, Hq, D = q_packed.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    S = kv_lens.shape[0]
+    if tuple(out.shape) != (T, Hq, D) or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or k_cache.shape[3] != D or cu_seqlens_q.shape[0] != S + 1 \
+            or block_tables.shape[0] != S:
+        raise ValueError("cb_paged_attention: inconsistent shapes")
+    _check(lib.cb_paged_attention(
+        _dev(q_packed, "q_packed", torch.bfloat16, 3),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1), _dev(kv_lens, "kv_lens", torch.int32, 1),
+        _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(k_cache, "k_cache", torch.bfloat16, 4), _dev(v_cache, "v_cache", torch.bfloat16, 4),
+        _dev(out, "out", torch.bfloat16, 3), float(scale), S, T, Hq, Hkv, D, bs,
+        block_tables.shape[1], NB, int(max_q_len), int(max_kv_len), int(kv_split_tokens),
+        _dev(workspace, "workspace", torch.uint8, 1), workspace.numel(), _stream(stream)),
+        "cb_paged_attention")
+
+
+def cb_split_kv_reduce(o_part, lse_part, num_splits, out, stream=None):
+    torch = _torch()
+    T, Hq, ms, D = o_part.shape
+    if tuple(lse_part.shape) != (T, Hq, ms) or tuple(out.shape) != (T, Hq, D) \
+            or num_splits.shape[0] != T:
+        raise ValueError("cb_split_kv_reduce: inconsistent shapes")
+    _check(lib.cb_split_kv_reduce(_dev(o_part, "o_part", torch.float32, 4),
+                                  _dev(lse_part, "lse_part", torch.float32, 3),
+                                  _dev(num_splits, "num_splits", torch.int32, 1),
+                                  _dev(out, "out", torch.bfloat16, 3), T, Hq, D, ms,
+                                  _stream(stream)),
+           "cb_split_kv_reduce")
+
+
+def _host_i32(a, name):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def cb_validate_batch(cu_seqlens_q, kv_lens, block_tables, slot_mapping, block_size: int,
+                      num_blocks: int, max_q_len: int, max_kv_len: int, raise_on_error=True):
+    """Host-only precondition check on host arrays (numpy or CPU tensors). Returns the status
+    (0 when valid); raises CBError instead when raise_on_error."""
+    cu, pcu = _host_i32(cu_seqlens_q, "cu_seqlens_q")
+    kv, pkv = _host_i32(kv_lens, "kv_lens")
+    bt, pbt = _host_i32(block_tables, "block_tables")
+    sl, psl = _host_i32(slot_mapping, "slot_mapping")
+    S = kv.shape[0]
+    T = int(cu[-1]) if sl is None else sl.shape[0]
+    mb = bt.shape[1] if bt.ndim == 2 else 0
+    st = lib.cb_validate_batch(pcu, pkv, pbt, psl, S, T, mb, int(block_size), int(num_blocks),
+                               int(max_q_len), int(max_kv_len))
+    if raise_on_error:
+        _check(st, "cb_validate_batch")
+    return int(st)

@@ -1,0 +1,837 @@
+// Ragged paged attention for gfx950 (CDNA4): planning prepass, decode / split-KV kernel,
+// prefill-chunk kernel and the log-sum-exp merge.
+//
+// What is computed (the pages give no formula; scaled dot-product softmax attention is the
+// reading): the token at position p of sequence s attends to keys 0..p of s only — ragged
+// batching with a block-diagonal mask ("Continuous batching from first principles",
+// Takeaways) and chunked prefill attending to a cache that already holds earlier chunks
+// ("3.3 Batching & Memory Management", section "Chunked prefill"). Keys and values are
+// gathered through the block table ("PagedAttention: block tables").
+//
+// Work split. A sequence whose rows (new tokens x query heads per KV head, G = Hq/Hkv) fit in
+// one 16-row MFMA tile (q * G <= 16) is decode-type: its KV range is cut into partitions of P
+// tokens, one workgroup per (partition, KV head); several partitions are merged afterwards by
+// log-sum-exp. Longer chunks are prefill-type: one workgroup per (128-row query tile, KV head)
+// over the whole causal key range, with K/V tiles staged in LDS and shared by 4 waves.
+//
+// MFMA orientation (both kernels). v_mfma_f32_16x16x32_bf16 with
+//   S^T[key][row]  = K[key][:] . Q[row][:]        (A = K rows, B = Q^T, contraction over dims)
+//   O^T[dim][row] += V^T[dim][key] . P^T[key][row] (A = V^T,   B = P^T, contraction over keys)
+// Output lane (n, g) = (lane % 16, lane / 16) holds column n (a query row) and rows 4g..4g+3,
+// so each lane carries one query row: the running max / sum are lane-local after a 2-step
+// cross-group reduction, and the rescale of O needs no data movement. The contraction index
+// may be permuted freely as long as A and B agree: lane group g takes dims [g*D/4, (g+1)*D/4)
+// of Q and K (contiguous 16-byte loads), and keys {16j + 4g + i} of P and V, which is exactly
+// where the S^T tile leaves them, so P feeds the second MFMA without a shuffle. V arrives with
+// 8 dims of one key per 16 bytes; 8 such rows are transposed in registers with byte permutes
+// into the 8-keys-per-dim operand.
+//
+// Masking is by select before the exponential (never by multiplying with 0), and V rows of
+// keys at or past the range end are zeroed, so NaN or stale data in unread slots (block tails,
+// unassigned blocks) cannot reach the output.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "cb_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running maxima start at this finite floor so that exp2(m_old - m_new) never sees inf - inf.
+constexpr float kMaxFloor = -1e30f;
+constexpr int kMaxSplitTokens = 4096;
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = kPrefillWaves * 32;  // query rows (token x head) per prefill tile
+constexpr int kDecodeWaves = 4;
+
+struct Work {
+  int32_t seq;
+  int32_t idx;  // KV partition (decode) or query tile (prefill)
+};
+
+__device__ inline f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float xor_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ inline float xor_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+// Fragments of one 32-key step for one lane.
+template <int D>
+struct KVFrag {
+  static constexpr int KSTEPS = D / 32;  // MFMA k-steps over the head dimension
+  static constexpr int DW = D / 32;      // 32-bit words of V per key per lane (D/16 bf16)
+  bf16x8 k[2][KSTEPS];                   // K: key group j (16 keys), k-step kk
+  uint32_t v[8][DW];                     // V: key e = 16*(e/4) + 4g + e%4, dims n*D/16 ..
+};
+
+// Online-softmax update of one 16-row tile for one 32-key step.
+//   acc[j][i]: S^T for key k0 + 16j + 4g + i of this lane's row.
+// Keys >= kend or > last_key are masked. Returns P^T (bf16) in the B-operand layout.
+template <int NO>
+__device__ inline bf16x8 softmax_step(const f32x4 (&acc)[2], int k0, int kend, int last_key,
+                                      float scale_log2, int g, float& m, float& l,
+                                      f32x4 (&o)[NO]) {
+  float s[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = k0 + 16 * j + 4 * g + i;
+      const float v = acc[j][i] * scale_log2;
+      const float sv = (key < kend && key <= last_key) ? v : -INFINITY;
+      s[4 * j + i] = sv;
+      mx = fmaxf(mx, sv);
+    }
+  }
+  mx = xor_max(mx);
+  const float m_new = fmaxf(m, mx);
+  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+  float rs = 0.f;
+  bf16x8 pb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = __builtin_amdgcn_exp2f(s[e] - m_new);
+    rs += p;
+    pb[e] = (__bf16)p;
+  }
+  rs = xor_sum(rs);
+  l = l * alpha + rs;
+  m = m_new;
+#pragma unroll
+  for (int t = 0; t < NO; ++t) o[t] *= alpha;
+  return pb;
+}
+
+// V^T operand of output tile jt: element e = V[key e][dim n*D/16 + jt], from 8 keys' words.
+template <int D>
+__device__ inline bf16x8 vt_operand(const uint32_t (&v)[8][D / 32], int jt) {
+  const int w = jt >> 1;
+  uint32_t d[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const uint32_t lo = v[2 * a][w], hi = v[2 * a + 1][w];
+    d[a] = (jt & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+  }
+  return __builtin_bit_cast(bf16x8, d);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Planning prepass: per-sequence work items, compacted with a block-wide scan.
+
+// A sequence breaking the contract (q = 0, kv_len < q, more KV than its table row addresses,
+// a decode-type q beyond max_q_len, more partitions than max_kv_len allows) gets no work item,
+// so nothing is read or written out of bounds; its output rows are then left unwritten.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu,
+                                                    const int32_t* __restrict__ kv_lens,
+                                                    int32_t num_seqs, int32_t G, int32_t P,
+                                                    int32_t qmaxd, int32_t max_splits,
+                                                    int32_t bq, int32_t bs, int32_t max_blocks,
+                                                    Work* __restrict__ dec,
+                                                    int64_t dec_cap, Work* __restrict__ pre,
+                                                    int64_t pre_cap, int32_t* __restrict__ counts) {
+  __shared__ int32_t sd[1024];
+  __shared__ int32_t sp[1024];
+  __shared__ int32_t base[2];
+  const int tid = threadIdx.x;
+  if (tid == 0) base[0] = base[1] = 0;
+  __syncthreads();
+  for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
+    const int s = s0 + tid;
+    int nd = 0, np = 0;
+    if (s < num_seqs) {
+      const int q = cu[s + 1] - cu[s];
+      const int L = kv_lens[s];
+      if (q > 0 && L >= q && (L + bs - 1) / bs <= max_blocks) {
+        if (q * G <= 16) {
+          nd = (L + P - 1) / P;
+          if (q > qmaxd || nd > max_splits) nd = 0;
+        } else {
+          np = (q + bq - 1) / bq;
+        }
+      }
+    }
+    sd[tid] = nd;
+    sp[tid] = np;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int a = tid >= off ? sd[tid - off] : 0;
+      const int b = tid >= off ? sp[tid - off] : 0;
+      __syncthreads();
+      sd[tid] += a;
+      sp[tid] += b;
+      __syncthreads();
+    }
+    const int64_t ed = (int64_t)base[0] + sd[tid] - nd;
+    const int64_t ep = (int64_t)base[1] + sp[tid] - np;
+    for (int k = 0; k < nd; ++k)
+      if (ed + k < dec_cap) dec[ed + k] = Work{s, k};
+    // a sequence's last query tiles see the most keys: emit them first
+    for (int k = 0; k < np; ++k)
+      if (ep + k < pre_cap) pre[ep + k] = Work{s, np - 1 - k};
+    __syncthreads();
+    if (tid == 1023) {
+      base[0] += sd[1023];
+      base[1] += sp[1023];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    counts[0] = (int32_t)min((int64_t)base[0], dec_cap);
+    counts[1] = (int32_t)min((int64_t)base[1], pre_cap);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode / split-KV kernel: one workgroup of 4 waves per (KV partition, KV head). Waves take
+// interleaved 32-key steps of the partition and merge through LDS at the end. K/V fragments
+// are loaded straight from HBM into registers (16-byte loads), one step ahead.
+
+template <int D>
+__device__ inline void load_step(KVFrag<D>& f, const __bf16* __restrict__ kc,
+                                 const __bf16* __restrict__ vc, int64_t row0, int64_t row1,
+                                 int Hkv, int n, int g) {
+  // row_j = (block_j * bs + offset_j) * Hkv + kvh: cache row of the first key of group j
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t r = (j ? row1 : row0) + (int64_t)n * Hkv;
+    const bf16x8* p = reinterpret_cast<const bf16x8*>(kc + r * D + g * (D / 4));
+#pragma unroll
+    for (int kk = 0; kk < KVFrag<D>::KSTEPS; ++kk) f.k[j][kk] = p[kk];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t r = ((e >> 2) ? row1 : row0) + (int64_t)(4 * g + (e & 3)) * Hkv;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(vc + r * D + n * (D / 16));
+    if constexpr (D == 128) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      f.v[e][0] = x.x; f.v[e][1] = x.y; f.v[e][2] = x.z; f.v[e][3] = x.w;
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      f.v[e][0] = x.x; f.v[e][1] = x.y;
+    }
+  }
+}
+
+// Consumes the fragment (its V words are zeroed in place past the range end).
+template <int D>
+__device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], int k0,
+                                    int kend, int last_key, float scale_log2, int g, float& m,
+                                    float& l, f32x4 (&o)[D / 16]) {
+  constexpr int KSTEPS = D / 32;
+  f32x4 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) acc[j] = mfma16x16x32(f.k[j][kk], qf[kk], acc[j]);
+  }
+  const bf16x8 pb = softmax_step<D / 16>(acc, k0, kend, last_key, scale_log2, g, m, l, o);
+  // zero V of keys past the range end (their slots may hold anything, NaN included)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int key = k0 + 16 * (e >> 2) + 4 * g + (e & 3);
+    if (key >= kend) {
+#pragma unroll
+      for (int w = 0; w < D / 32; ++w) f.v[e][w] = 0u;
+    }
+  }
+#pragma unroll
+  for (int jt = 0; jt < D / 16; ++jt) o[jt] = mfma16x16x32(vt_operand<D>(f.v, jt), pb, o[jt]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
+    const __bf16* __restrict__ q, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables,
+    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
+    __bf16* __restrict__ out, float* __restrict__ o_part, float* __restrict__ lse_part,
+    const Work* __restrict__ items, const int32_t* __restrict__ counts, int32_t Hq, int32_t Hkv,
+    int32_t bs, int32_t max_blocks_per_seq, int32_t P, int32_t max_splits, int32_t qmaxd,
+    float scale_log2) {
+  constexpr int NW = kDecodeWaves;
+  constexpr int KSTEPS = D / 32;
+  constexpr int NO = D / 16;  // output tiles (dims) per row
+  constexpr int OSTRIDE = D + 4;
+  __shared__ int32_t sm_bt[kMaxSplitTokens / 16 + 2];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[NW][16][OSTRIDE];
+
+  const int item = blockIdx.x / Hkv;
+  const int kvh = blockIdx.x - item * Hkv;
+  if (item >= counts[0]) return;
+  const Work w = items[item];
+  const int s = w.seq, split = w.idx;
+  const int G = Hq / Hkv;
+  const int q0 = cu[s];
+  const int qn = cu[s + 1] - q0;
+  const int L = kv_lens[s];
+  const int kb = split * P;
+  const int ke = min(L, kb + P);
+  const int nsplit = (L + P - 1) / P;
+  const int rows = qn * G;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+
+  // block-table entries of this partition -> LDS
+  const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
+  const int jb0 = kb / bs;
+  const int nbt = (ke + bs - 1) / bs - jb0;
+  for (int i = tid; i < nbt; i += NW * 64) sm_bt[i] = bt_row[jb0 + i];
+
+  // Q^T operand: lane column n is query row n = (token n / G, head n % G)
+  bf16x8 qf[KSTEPS];
+  int last_key = -1;
+  if (n < rows) {
+    const int qi = n / G, hh = n - (n / G) * G;
+    const bf16x8* p = reinterpret_cast<const bf16x8*>(
+        q + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + g * (D / 4));
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = p[kk];
+    last_key = L - qn + qi;
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
+  }
+  __syncthreads();
+
+  float m = kMaxFloor, l = 0.f;
+  f32x4 o[NO];
+#pragma unroll
+  for (int t = 0; t < NO; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // cache row (in units of D elements) of the first key of a 16-key group starting at key k
+  auto group_row = [&](int k) -> int64_t {
+    const int kk = k < ke ? k : kb;  // groups wholly past the end alias the first group
+    const int blk = sm_bt[kk / bs - jb0];
+    return ((int64_t)blk * bs + (kk % bs)) * Hkv + kvh;
+  };
+
+  const int stride = 32 * NW;
+  int k0 = kb + 32 * wave;
+  if (k0 < ke) {
+    KVFrag<D> fa, fb;
+    load_step<D>(fa, k_cache, v_cache, group_row(k0), group_row(k0 + 16), Hkv, n, g);
+    while (true) {
+      const int k1 = k0 + stride;
+      if (k1 < ke) load_step<D>(fb, k_cache, v_cache, group_row(k1), group_row(k1 + 16), Hkv, n, g);
+      compute_step<D>(fa, qf, k0, ke, last_key, scale_log2, g, m, l, o);
+      if (k1 >= ke) break;
+      const int k2 = k1 + stride;
+      if (k2 < ke) load_step<D>(fa, k_cache, v_cache, group_row(k2), group_row(k2 + 16), Hkv, n, g);
+      compute_step<D>(fb, qf, k1, ke, last_key, scale_log2, g, m, l, o);
+      if (k2 >= ke) break;
+      k0 = k2;
+    }
+  }
+
+  // merge the waves: each writes its row statistics and O rows (lane (n, g) holds row n,
+  // dims (4g + i) * NO + jt for output tile jt and accumulator element i)
+  if (g == 0) {
+    sm_m[wave][n] = m;
+    sm_l[wave][n] = l;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float* dst = &sm_o[wave][n][(4 * g + i) * NO];
+#pragma unroll
+    for (int jt = 0; jt < NO; ++jt) dst[jt] = o[jt][i];
+  }
+  __syncthreads();
+
+  // 256 threads: row = tid / 16, dims [c * NO, (c+1) * NO)
+  const int row = tid >> 4, c = tid & 15;
+  if (row >= rows) return;
+  float M = kMaxFloor;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][row]);
+  float lsum = 0.f;
+  float acc[NO];
+#pragma unroll
+  for (int i = 0; i < NO; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    const float sc = __builtin_amdgcn_exp2f(sm_m[ww][row] - M);
+    lsum += sc * sm_l[ww][row];
+#pragma unroll
+    for (int i = 0; i < NO; ++i) acc[i] += sc * sm_o[ww][row][c * NO + i];
+  }
+  const int qi = row / G, hh = row - (row / G) * G;
+  const int h = kvh * G + hh;
+  if (nsplit == 1) {
+    const float inv = 1.f / lsum;
+    __bf16 r[NO];
+#pragma unroll
+    for (int i = 0; i < NO; ++i) r[i] = (__bf16)(acc[i] * inv);
+    __bf16* dst = out + ((int64_t)(q0 + qi) * Hq + h) * D + c * NO;
+    if constexpr (NO == 8) *reinterpret_cast<bf16x8*>(dst) = __builtin_bit_cast(bf16x8, r);
+    else *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, r);
+  } else {
+    const int64_t prow = (int64_t)s * qmaxd + qi;
+    const int64_t base = (prow * Hq + h) * max_splits + split;
+    const bool empty = !(lsum > 0.f);
+    const float inv = empty ? 0.f : 1.f / lsum;
+    float* dst = o_part + base * D + c * NO;
+#pragma unroll
+    for (int i = 0; i < NO; ++i) dst[i] = acc[i] * inv;
+    if (c == 0) lse_part[base] = empty ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Prefill kernel: one workgroup of 4 waves per (query tile of 128 rows, KV head). Each wave owns
+// 32 rows (two 16-row MFMA tiles). K/V tiles of 32 keys are gathered through the block table
+// into LDS by all 256 threads (16-byte loads, double buffered; block ids fetched two steps
+// ahead) and read by every wave.
+
+template <int D>
+struct PrefillSmem {
+  static constexpr int STRIDE = D + 8;  // bf16 elements per LDS row (16-byte pad)
+  __bf16 k[2][32][STRIDE];
+  __bf16 v[2][32][STRIDE];
+};
+
+template <int D>
+__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
+    const __bf16* __restrict__ q, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables,
+    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
+    __bf16* __restrict__ out, const Work* __restrict__ items, const int32_t* __restrict__ counts,
+    int32_t Hq, int32_t Hkv, int32_t bs, int32_t max_blocks_per_seq, int32_t bq,
+    float scale_log2) {
+  constexpr int KSTEPS = D / 32;
+  constexpr int NO = D / 16;
+  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
+  constexpr int RPP = kPrefillWaves * 64 / CPR;  // key rows loaded per pass
+  constexpr int PASSES = 32 / RPP;
+  __shared__ __attribute__((aligned(16))) PrefillSmem<D> sm;
+
+  const int item = blockIdx.x / Hkv;
+  const int kvh = blockIdx.x - item * Hkv;
+  if (item >= counts[1]) return;
+  const Work w = items[item];
+  const int s = w.seq, qt = w.idx;
+  const int G = Hq / Hkv;
+  const int q0 = cu[s];
+  const int qn = cu[s + 1] - q0;
+  const int L = kv_lens[s];
+  const int tok0 = qt * bq;
+  const int tok_end = min(qn, tok0 + bq);
+  const int kend = L - qn + tok_end;  // keys [0, kend) are visible to some row of the tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+
+  // Q^T operands of this wave's two row tiles
+  bf16x8 qf[2][KSTEPS];
+  int last_key[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int R = wave * 32 + nt * 16 + n;
+    const int qi = tok0 + R / G, hh = R - (R / G) * G;
+    if (qi < tok_end) {
+      const bf16x8* p = reinterpret_cast<const bf16x8*>(
+          q + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + g * (D / 4));
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qf[nt][kk] = p[kk];
+      last_key[nt] = L - qn + qi;
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[nt][kk][e] = (__bf16)0.f;
+      last_key[nt] = -1;
+    }
+  }
+
+  // loader role of this thread: key row lr + pass * RPP of each step, 16-byte chunk lc
+  const int lr = tid / CPR, lc = tid - (tid / CPR) * CPR;
+  const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
+  auto fetch_block = [&](int step, int pass) -> int {
+    const int key = step * 32 + lr + pass * RPP;
+    return key < kend ? bt_row[key / bs] : -1;
+  };
+  uint4 rk[PASSES], rv[PASSES];
+  auto fetch_kv = [&](int step, const int (&blk)[PASSES]) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int key = step * 32 + lr + ps * RPP;
+      if (blk[ps] >= 0) {
+        const int64_t row = ((int64_t)blk[ps] * bs + key % bs) * Hkv + kvh;
+        rk[ps] = *reinterpret_cast<const uint4*>(k_cache + row * D + lc * 8);
+        rv[ps] = *reinterpret_cast<const uint4*>(v_cache + row * D + lc * 8);
+      } else {
+        rk[ps] = make_uint4(0, 0, 0, 0);
+        rv[ps] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      *reinterpret_cast<uint4*>(&sm.k[buf][lr + ps * RPP][lc * 8]) = rk[ps];
+      *reinterpret_cast<uint4*>(&sm.v[buf][lr + ps * RPP][lc * 8]) = rv[ps];
+    }
+  };
+
+  const int nsteps = (kend + 31) / 32;
+  int blk1[PASSES], blk2[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) blk1[ps] = fetch_block(0, ps);
+  fetch_kv(0, blk1);
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) blk1[ps] = nsteps > 1 ? fetch_block(1, ps) : -1;
+  stash(0);
+  __syncthreads();
+
+  float m[2] = {kMaxFloor, kMaxFloor}, l[2] = {0.f, 0.f};
+  f32x4 o[2][NO];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int t = 0; t < NO; ++t) o[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nsteps;
+    if (more) {
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) blk2[ps] = st + 2 < nsteps ? fetch_block(st + 2, ps) : -1;
+      fetch_kv(st + 1, blk1);
+    }
+    const int k0 = st * 32;
+    // S^T = K Q^T for both row tiles; the K fragment is shared
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * j + n][g * (D / 4) + 8 * kk]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[nt][j] = mfma16x16x32(kf, qf[nt][kk], acc[nt][j]);
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      pb[nt] = softmax_step<NO>(acc[nt], k0, kend, last_key[nt], scale_log2, g, m[nt], l[nt], o[nt]);
+    // V^T operands from LDS: 8 keys x (D/16 dims) per lane, transposed in registers
+    uint32_t vw[8][D / 32];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kr = 16 * (e >> 2) + 4 * g + (e & 3);
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(&sm.v[buf][kr][n * (D / 16)]);
+#pragma unroll
+      for (int ww = 0; ww < D / 32; ++ww) vw[e][ww] = p[ww];
+    }
+#pragma unroll
+    for (int jt = 0; jt < NO; ++jt) {
+      const bf16x8 vt = vt_operand<D>(vw, jt);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) o[nt][jt] = mfma16x16x32(vt, pb[nt], o[nt][jt]);
+    }
+    if (more) {
+      stash(buf ^ 1);
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) blk1[ps] = blk2[ps];
+    }
+    __syncthreads();
+  }
+
+  // normalise and store: lane (n, g) holds row n, dims (4g + i) * NO + jt
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int R = wave * 32 + nt * 16 + n;
+    const int qi = tok0 + R / G, hh = R - (R / G) * G;
+    if (qi >= tok_end) continue;
+    const float inv = 1.f / l[nt];
+    __bf16* dst = out + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __bf16 r[NO];
+#pragma unroll
+      for (int jt = 0; jt < NO; ++jt) r[jt] = (__bf16)(o[nt][jt][i] * inv);
+      if constexpr (NO == 8)
+        *reinterpret_cast<bf16x8*>(dst + (4 * g + i) * NO) = __builtin_bit_cast(bf16x8, r);
+      else
+        *reinterpret_cast<uint2*>(dst + (4 * g + i) * NO) = __builtin_bit_cast(uint2, r);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Log-sum-exp merge of KV partitions. One workgroup per partial row; D/8 threads per head.
+// INTERNAL: partial row = (sequence, token of the sequence), count derived from kv_lens.
+// Otherwise: partial row = packed token, count from num_splits.
+
+template <int D, bool INTERNAL>
+__global__ __launch_bounds__(256) void reduce_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    const int32_t* __restrict__ num_splits, __bf16* __restrict__ out, int32_t Hq,
+    int32_t max_splits, const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_lens,
+    int32_t qmaxd, int32_t G, int32_t P) {
+  constexpr int TPH = D / 8;
+  const int64_t prow = blockIdx.x;
+  int64_t t;
+  int ns;
+  if constexpr (INTERNAL) {
+    const int s = (int)(prow / qmaxd), qi = (int)(prow - (prow / qmaxd) * qmaxd);
+    const int qn = cu[s + 1] - cu[s];
+    if (qi >= qn || qn * G > 16 || qn > qmaxd) return;
+    ns = (kv_lens[s] + P - 1) / P;
+    if (ns <= 1 || ns > max_splits) return;  // single partition: written directly
+    t = cu[s] + qi;
+  } else {
+    t = prow;
+    ns = min(num_splits[t], max_splits);
+    if (ns <= 0) return;
+  }
+  const int c = threadIdx.x % TPH;
+  for (int h = threadIdx.x / TPH; h < Hq; h += 256 / TPH) {
+    const int64_t base = (prow * Hq + h) * max_splits;
+    float M = -INFINITY;
+    for (int k = 0; k < ns; ++k) M = fmaxf(M, lse_part[base + k]);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    float wsum = 0.f;
+    if (M != -INFINITY) {
+      for (int k = 0; k < ns; ++k) {
+        const float lk = lse_part[base + k];
+        if (lk == -INFINITY) continue;  // empty partition: no weight, its o is not read
+        const float wk = __builtin_amdgcn_exp2f((lk - M) * kLog2e);
+        wsum += wk;
+        const float4* p = reinterpret_cast<const float4*>(o_part + (base + k) * D + c * 8);
+        const float4 a = p[0], b = p[1];
+        acc[0] += wk * a.x; acc[1] += wk * a.y; acc[2] += wk * a.z; acc[3] += wk * a.w;
+        acc[4] += wk * b.x; acc[5] += wk * b.y; acc[6] += wk * b.z; acc[7] += wk * b.w;
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    __bf16 r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)(acc[i] * inv);
+    *reinterpret_cast<bf16x8*>(out + (t * Hq + h) * D + c * 8) = __builtin_bit_cast(bf16x8, r);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host side
+
+struct Plan {
+  int32_t G = 0, P = 0, max_splits = 0, qmaxd = 0, bq = 0;
+  int64_t dec_cap = 0, pre_cap = 0;
+  size_t off_counts = 0, off_dec = 0, off_pre = 0, off_opart = 0, off_lse = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t requested) {
+  if (requested > 0) {
+    int32_t p = (int32_t)cb::ceil_div(requested, 32) * 32;
+    return p > kMaxSplitTokens ? kMaxSplitTokens : p;
+  }
+  // aim at ~16k (partition, KV head) workgroups over the batch's upper-bound key count
+  const int64_t keys = (int64_t)max_kv_len * num_seqs * Hkv;
+  int64_t p = 256;
+  while (p < kMaxSplitTokens && keys / p > 16384) p *= 2;
+  return (int32_t)p;
+}
+
+Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, int32_t D,
+               int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens) {
+  Plan p;
+  p.G = Hq / Hkv;
+  p.P = choose_split(num_seqs, Hkv, max_kv_len, kv_split_tokens);
+  p.max_splits = (int32_t)cb::ceil_div(max_kv_len, p.P);
+  const int32_t dec_q = 16 / p.G;  // longest decode-type chunk
+  p.qmaxd = max_q_len < dec_q ? max_q_len : dec_q;
+  p.bq = kPrefillRows / p.G;
+  p.dec_cap = (int64_t)num_seqs * p.max_splits;
+  p.pre_cap = (max_q_len > dec_q) ? (int64_t)num_tokens / p.bq + num_seqs : 0;
+  size_t off = 0;
+  p.off_counts = off;
+  off = align256(off + 16);
+  p.off_dec = off;
+  off = align256(off + sizeof(Work) * (size_t)p.dec_cap);
+  p.off_pre = off;
+  off = align256(off + sizeof(Work) * (size_t)p.pre_cap);
+  const size_t nrows = p.max_splits > 1 ? (size_t)num_seqs * p.qmaxd * Hq * p.max_splits : 0;
+  p.off_opart = off;
+  off = align256(off + sizeof(float) * nrows * D);
+  p.off_lse = off;
+  off = align256(off + sizeof(float) * nrows);
+  p.total = off;
+  return p;
+}
+
+bool supported_ratio(int32_t G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+
+}  // namespace
+
+extern "C" int32_t cb_paged_attention_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                                   int32_t max_kv_len, int32_t kv_split_tokens) {
+  return choose_split(num_seqs, num_kv_heads, max_kv_len, kv_split_tokens);
+}
+
+extern "C" size_t cb_paged_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t head_dim, int32_t block_size,
+                                                    int32_t max_q_len, int32_t max_kv_len,
+                                                    int32_t kv_split_tokens) {
+  (void)block_size;
+  if (num_seqs <= 0 || num_tokens <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      max_q_len <= 0 || max_kv_len <= 0)
+    return 0;
+  return make_plan(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_q_len,
+                   max_kv_len, kv_split_tokens < 0 ? 0 : kv_split_tokens)
+      .total;
+}
+
+extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlens_q,
+                                  const int32_t* kv_lens, const int32_t* block_tables,
+                                  const void* k_cache, const void* v_cache, void* out, float scale,
+                                  int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  using cb::fail;
+  const int E = CB_ERR_INVALID_ARG;
+  if (block_size < 4) return fail(E, "block_size must be at least 4, got " + std::to_string(block_size));
+  if (num_seqs < 0 || num_tokens < 0) return fail(E, "negative num_seqs or num_tokens");
+  if (num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1) return fail(E, "head counts and head_dim must be positive");
+  if (num_q_heads % num_kv_heads != 0) return fail(E, "num_q_heads must be a multiple of num_kv_heads");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(E, "scale must be finite and positive");
+  if (kv_split_tokens < 0) return fail(E, "kv_split_tokens must be >= 0");
+  if (head_dim != 64 && head_dim != 128) return fail(CB_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!supported_ratio(num_q_heads / num_kv_heads))
+    return fail(CB_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16");
+  if (block_size % 16 != 0) return fail(CB_ERR_UNSUPPORTED, "block_size must be a multiple of 16");
+  if (num_seqs == 0 || num_tokens == 0) return cb::ok();
+  if (!q_packed || !cu_seqlens_q || !kv_lens || !block_tables || !k_cache || !v_cache || !out)
+    return fail(E, "cb_paged_attention: NULL pointer argument");
+  if (!cb::aligned16(q_packed) || !cb::aligned16(k_cache) || !cb::aligned16(v_cache) || !cb::aligned16(out))
+    return fail(E, "q_packed, caches and out must be 16-byte aligned");
+  if (max_blocks_per_seq < 1 || num_blocks < 1) return fail(E, "max_blocks_per_seq and num_blocks must be >= 1");
+  if (max_q_len < 1 || max_kv_len < 1) return fail(E, "max_q_len and max_kv_len must be >= 1");
+  if (max_kv_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(E, "max_kv_len exceeds the block-table capacity max_blocks_per_seq * block_size");
+  const Plan p = make_plan(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_q_len,
+                           max_kv_len, kv_split_tokens);
+  if (!workspace || workspace_bytes < p.total)
+    return fail(CB_ERR_WORKSPACE, "workspace needs " + std::to_string(p.total) + " bytes, got " +
+                                      std::to_string(workspace_bytes));
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(E, "workspace must be 256-byte aligned");
+  if ((int64_t)p.dec_cap * num_kv_heads > INT32_MAX || (int64_t)p.pre_cap * num_kv_heads > INT32_MAX)
+    return fail(CB_ERR_UNSUPPORTED, "batch too large for one launch");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
+  Work* dec = reinterpret_cast<Work*>(ws + p.off_dec);
+  Work* pre = reinterpret_cast<Work*>(ws + p.off_pre);
+  float* o_part = reinterpret_cast<float*>(ws + p.off_opart);
+  float* lse_part = reinterpret_cast<float*>(ws + p.off_lse);
+  const float scale_log2 = scale * kLog2e;
+  const __bf16* qp = static_cast<const __bf16*>(q_packed);
+  const __bf16* kc = static_cast<const __bf16*>(k_cache);
+  const __bf16* vc = static_cast<const __bf16*>(v_cache);
+  __bf16* op = static_cast<__bf16*>(out);
+
+  plan_kernel<<<1, 1024, 0, st>>>(cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd,
+                                  p.max_splits, p.bq, block_size, max_blocks_per_seq, dec,
+                                  p.dec_cap, pre, p.pre_cap, counts);
+  if (p.pre_cap > 0) {
+    const unsigned grid = (unsigned)(p.pre_cap * num_kv_heads);
+    if (head_dim == 128)
+      prefill_kernel<128><<<grid, kPrefillWaves * 64, 0, st>>>(
+          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
+          num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
+    else
+      prefill_kernel<64><<<grid, kPrefillWaves * 64, 0, st>>>(
+          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
+          num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
+  }
+  {
+    const unsigned grid = (unsigned)(p.dec_cap * num_kv_heads);
+    if (head_dim == 128)
+      decode_kernel<128><<<grid, kDecodeWaves * 64, 0, st>>>(
+          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
+          num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits, p.qmaxd,
+          scale_log2);
+    else
+      decode_kernel<64><<<grid, kDecodeWaves * 64, 0, st>>>(
+          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
+          num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits, p.qmaxd,
+          scale_log2);
+  }
+  if (p.max_splits > 1) {
+    const unsigned grid = (unsigned)((int64_t)num_seqs * p.qmaxd);
+    if (head_dim == 128)
+      reduce_kernel<128, true><<<grid, 256, 0, st>>>(o_part, lse_part, nullptr, op, num_q_heads,
+                                                     p.max_splits, cu_seqlens_q, kv_lens, p.qmaxd,
+                                                     p.G, p.P);
+    else
+      reduce_kernel<64, true><<<grid, 256, 0, st>>>(o_part, lse_part, nullptr, op, num_q_heads,
+                                                    p.max_splits, cu_seqlens_q, kv_lens, p.qmaxd,
+                                                    p.G, p.P);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CB_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
+  return cb::ok();
+}
+
+extern "C" int cb_split_kv_reduce(const float* o_part, const float* lse_part,
+                                  const int32_t* num_splits, void* out, int32_t num_tokens,
+                                  int32_t num_q_heads, int32_t head_dim, int32_t max_splits,
+                                  void* stream) {
+  using cb::fail;
+  if (num_tokens < 0 || num_q_heads < 1 || max_splits < 1)
+    return fail(CB_ERR_INVALID_ARG, "cb_split_kv_reduce: bad size argument");
+  if (head_dim != 64 && head_dim != 128) return fail(CB_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_tokens == 0) return cb::ok();
+  if (!o_part || !lse_part || !num_splits || !out)
+    return fail(CB_ERR_INVALID_ARG, "cb_split_kv_reduce: NULL pointer argument");
+  if (!cb::aligned16(o_part) || !cb::aligned16(out))
+    return fail(CB_ERR_INVALID_ARG, "o_part and out must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  __bf16* op = static_cast<__bf16*>(out);
+  if (head_dim == 128)
+    reduce_kernel<128, false><<<num_tokens, 256, 0, st>>>(o_part, lse_part, num_splits, op,
+                                                          num_q_heads, max_splits, nullptr,
+                                                          nullptr, 1, 1, 1);
+  else
+    reduce_kernel<64, false><<<num_tokens, 256, 0, st>>>(o_part, lse_part, num_splits, op,
+                                                         num_q_heads, max_splits, nullptr,
+                                                         nullptr, 1, 1, 1);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CB_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(e));
+  return cb::ok();
+}

@@ -1,0 +1,217 @@
+"""HIP path against the oracle, through the C ABI, on an MI355X.
+
+Slot mapping and the cache write must be bit-exact; attention outputs must satisfy
+|gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise against the float64 oracle. Scaled-down copies of
+the five workloads are compared on every output element; the full-size workloads (in the launch
+configuration the benchmark times) on every decode token and a sample of prefill tokens.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import (Step, assert_close, dev_bf16, dev_i32, host_u16, oracle_step,
+                         readable_mask, say)
+from pins import permute_blocks, tiny_batch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ragged_paged_kv_amd  # noqa: F401  (raises if the library is not built)
+    return torch
+
+
+def check_full(batch, step, tokens=None):
+    sl, (kc, vc), out, _ = oracle_step(batch, tokens=tokens)
+    assert np.array_equal(step.slots_host(), sl), "slot mapping differs from the oracle"
+    assert np.array_equal(host_u16(step.k_cache), kc), "K cache differs from the oracle"
+    assert np.array_equal(host_u16(step.v_cache), vc), "V cache differs from the oracle"
+    got = step.out_f64()
+    if tokens is None:
+        return assert_close(got, out, batch.name)
+    return assert_close(got[tokens], out[tokens], batch.name)
+
+
+SMALL = [1, 2, 3, 4, 5]
+
+
+@pytest.mark.parametrize("n", SMALL)
+@pytest.mark.parametrize("split", [0, 32, 64, 512])
+def test_small_configs_every_element(torch_cuda, n, split):
+    b = synth.make_config(n, small=True)
+    say(f"[parity] small config {n} split {split}: S={b.num_seqs} T={b.num_tokens}")
+    step = Step(b, kv_split_tokens=split).run()
+    check_full(b, step)
+
+
+def _sample_tokens(batch, per_chunk=24, seed=0):
+    rng = np.random.default_rng(seed)
+    cu = batch.cu_seqlens_q
+    toks = []
+    for s in range(batch.num_seqs):
+        q = int(cu[s + 1] - cu[s])
+        if q == 1:
+            toks.append(int(cu[s]))
+        else:
+            pick = {0, 1, q - 2, q - 1} | set(rng.integers(0, q, size=per_chunk).tolist())
+            toks += [int(cu[s]) + i for i in sorted(pick)]
+    return np.array(sorted(set(toks)))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_full_size_configs(torch_cuda, n):
+    b = synth.make_config(n)
+    say(f"[parity] full config {n} ({b.name}): S={b.num_seqs} T={b.num_tokens} "
+        f"sumL={int(b.kv_lens.sum())} blocks={b.num_blocks}")
+    step = Step(b).run()
+    toks = _sample_tokens(b)
+    rep = check_full(b, step, tokens=toks)
+    say(f"[parity] full config {n}: {len(toks)} tokens checked, {rep}")
+
+
+def test_split_matches_unsplit(torch_cuda):
+    b = synth.make_config(4, small=True)
+    outs = []
+    for split in (32, 96, 1024, 4096):
+        outs.append(Step(b, kv_split_tokens=split).run().out_f64())
+    for o in outs[1:]:
+        assert_close(o, outs[-1], "split vs unsplit")
+
+
+def test_block_permutation_bit_identical(torch_cuda):
+    for n in (1, 3, 5):
+        b = synth.make_config(n, small=True)
+        a = Step(b).run().out_u16()
+        p = Step(permute_blocks(b, seed=n)).run().out_u16()
+        assert np.array_equal(a, p), f"config {n}: output changed under a block permutation"
+
+
+def test_deterministic_across_runs(torch_cuda):
+    b = synth.make_config(3, small=True)
+    st = Step(b, kv_split_tokens=64).run()
+    first = st.out_u16()
+    for _ in range(9):
+        st.attention()
+        torch_cuda.cuda.synchronize()
+        assert np.array_equal(st.out_u16(), first)
+
+
+@pytest.mark.parametrize("poison", [0x7F80, 0xFF80, 0xFFFF, 0x7F7F, None])
+def test_unread_slots_do_not_matter(torch_cuda, poison):
+    # Slots past each sequence's length, unassigned blocks: +inf, -inf, NaN, max finite, noise.
+    b = synth.make_config(5, small=True)
+    ref = Step(b).run().out_u16()
+    m = readable_mask(b)
+    import copy
+    b2 = copy.copy(b)
+    rng = np.random.default_rng(1)
+    for name in ("k_cache", "v_cache"):
+        c = getattr(b, name).copy()
+        fill = (rng.integers(0, 1 << 16, size=c.shape, dtype=np.uint32).astype(np.uint16)
+                if poison is None else np.full(c.shape, poison, dtype=np.uint16))
+        c[~m] = fill[~m]
+        setattr(b2, name, c)
+    # the new tokens' slots are unread before the write as well
+    got = Step(b2).run().out_u16()
+    assert np.array_equal(got, ref)
+
+
+def test_split_kv_reduce_entry(torch_cuda):
+    import ragged_paged_kv_amd as cb
+    torch = torch_cuda
+    b = synth.make_config(3, small=True)
+    sl, (kc, vc), ref, _ = oracle_step(b)
+    rng = np.random.default_rng(4)
+    bounds = []
+    for L in b.kv_lens.tolist():
+        cuts = sorted(set(rng.integers(1, L, size=min(L - 1, 5)).tolist())) if L > 1 else []
+        bounds.append([0] + cuts + [L])
+    o, lse, ns = oracle.split_partials(b.q, b.cu_seqlens_q, b.kv_lens, b.block_tables, kc, vc,
+                                       b.scale, bounds)
+    # an empty partition with garbage o must carry no weight
+    o = np.concatenate([o, np.full(o.shape[:2] + (1,) + o.shape[3:], np.nan)], axis=2)
+    lse = np.concatenate([lse, np.full(lse.shape[:2] + (1,), -np.inf)], axis=2)
+    ns = ns + 1
+    ns[5] = 0  # a token that must not be written
+    want = oracle.merge_partials(o, lse, ns)
+    out = torch.full(ref.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    cb.cb_split_kv_reduce(torch.from_numpy(o.astype(np.float32)).cuda(),
+                          torch.from_numpy(lse.astype(np.float32)).cuda(),
+                          dev_i32(ns, "cuda"), out)
+    torch.cuda.synchronize()
+    got = oracle.bf16_to_f64(host_u16(out))
+    keep = ns > 0
+    assert_close(got[keep], want[keep], "reduce vs oracle merge")
+    assert_close(got[keep], ref[keep], "reduce vs unsplit oracle")
+    assert np.all(got[~keep] == 7.0)
+
+
+EDGE = {
+    # (specs, Hq, Hkv, D, bs)
+    "single-key": ([synth.SeqSpec(1, 1)] * 3, 8, 2, 128, 16),
+    "prompt-of-one": ([synth.SeqSpec(1, 1), synth.SeqSpec(40, 40)], 8, 8, 128, 16),
+    "block-edges": ([synth.SeqSpec(1, L) for L in (15, 16, 17, 31, 32, 33, 63, 64, 65)], 32, 8, 128, 16),
+    "split-edges": ([synth.SeqSpec(1, L) for L in (255, 256, 257, 511, 512, 513)], 32, 8, 128, 16),
+    "mha": ([synth.SeqSpec(1, 70), synth.SeqSpec(33, 90)], 4, 4, 128, 16),
+    "gqa16": ([synth.SeqSpec(1, 70), synth.SeqSpec(2, 50), synth.SeqSpec(3, 90)], 32, 2, 128, 32),
+    "d64-gqa8": ([synth.SeqSpec(1, 70), synth.SeqSpec(2, 40), synth.SeqSpec(19, 60)], 16, 2, 64, 16),
+    "spec-decode": ([synth.SeqSpec(q, 100 + q) for q in (1, 2, 3, 4, 5, 8)], 32, 8, 128, 16),
+    "prefill-only": ([synth.SeqSpec(130, 130), synth.SeqSpec(77, 300)], 32, 8, 128, 16),
+    "bs64": ([synth.SeqSpec(1, 200), synth.SeqSpec(50, 150)], 32, 8, 128, 64),
+    "bs256": ([synth.SeqSpec(1, 700), synth.SeqSpec(100, 600)], 32, 8, 128, 256),
+    "long-chunk-offset": ([synth.SeqSpec(200, 1500)], 32, 8, 128, 16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+@pytest.mark.parametrize("split", [0, 32])
+def test_edge_cases(torch_cuda, name, split):
+    specs, Hq, Hkv, D, bs = EDGE[name]
+    b = tiny_batch(list(specs), Hq, Hkv, D, bs, seed=zlib.crc32(name.encode()) % 1000)
+    say(f"[parity] edge {name} split {split}")
+    step = Step(b, kv_split_tokens=split).run()
+    check_full(b, step)
+
+
+def test_loose_upper_bounds(torch_cuda):
+    # host bounds larger than the real maxima only size grids and the workspace
+    b = synth.make_config(3, small=True)
+    # the table must be able to address max_kv_len
+    import copy
+    b2 = copy.copy(b)
+    need = -(-(b.max_kv_len * 2 + 5) // b.block_size)
+    b2.block_tables = np.concatenate(
+        [b.block_tables, np.full((b.num_seqs, need - b.block_tables.shape[1]), -1, np.int32)], axis=1)
+    step = Step(b2, max_q_len=b.max_q_len * 3, max_kv_len=b.max_kv_len * 2 + 5).run()
+    check_full(b2, step)
+
+
+def test_empty_batch_leaves_output(torch_cuda):
+    import ragged_paged_kv_amd as cb
+    torch = torch_cuda
+    b = synth.make_config(1)
+    st = Step(b)
+    q0 = st.q[:0]
+    out0 = torch.empty((0, b.num_q_heads, b.head_dim), dtype=torch.bfloat16, device="cuda")
+    cu0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kv0 = torch.zeros(0, dtype=torch.int32, device="cuda")
+    bt0 = torch.zeros((0, 3), dtype=torch.int32, device="cuda")
+    cb.cb_paged_attention(q0, cu0, kv0, bt0, st.k_cache, st.v_cache, out0, b.scale, 1, 1, st.ws)
+    torch.cuda.synchronize()
+
+
+def test_workspace_too_small_is_rejected(torch_cuda):
+    import ragged_paged_kv_amd as cb
+    b = synth.make_config(2, small=True)
+    st = Step(b)
+    st.ws = st.ws[:64]
+    with pytest.raises(cb.CBError) as e:
+        st.attention()
+    assert e.value.status == -3
