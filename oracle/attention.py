@@ -185,7 +185,9 @@ def split_partials(q, cu_seqlens_q, kv_lens, block_tables, k_cache, v_cache, sca
 
 def merge_partials(o_part, lse_part, num_splits):
     """Log-sum-exp merge: out = sum_k exp(lse_k - M) o_k / sum_k exp(lse_k - M), M = max_k lse_k,
-    over the first num_splits[t] ranges of token t. Rows with num_splits 0 are NaN."""
+    over the non-empty ranges among the first num_splits[t] of token t. A range with
+    lse = -inf saw no key: it has no weight and its o (0/0, undefined) is never used. Rows with
+    num_splits 0 are NaN."""
     T, Hq, nmax, D = o_part.shape
     out = np.full((T, Hq, D), np.nan)
     for t in range(T):
@@ -193,11 +195,13 @@ def merge_partials(o_part, lse_part, num_splits):
         if n <= 0:
             continue
         l_ = lse_part[t, :, :n]
-        M = l_.max(axis=1, keepdims=True)
+        nonempty = l_ > -np.inf
+        M = np.where(nonempty, l_, -np.inf).max(axis=1, keepdims=True)
         M = np.where(np.isfinite(M), M, 0.0)
-        w = np.exp(l_ - M)
+        w = np.where(nonempty, np.exp(np.where(nonempty, l_, 0.0) - M), 0.0)
         den = w.sum(axis=1)
-        num = (w[:, :, None] * o_part[t, :, :n]).sum(axis=1)
+        o = np.where(nonempty[:, :, None], o_part[t, :, :n], 0.0)
+        num = (w[:, :, None] * o).sum(axis=1)
         out[t] = num / np.where(den > 0, den, 1.0)[:, None]
     return out
 

@@ -42,6 +42,11 @@ class CBError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7). Loading torch
+    # first makes the library's HIP dependency bind to that runtime, so torch's allocations,
+    # streams and our kernels share one device context. Loaded the other way round, the process
+    # would hold two HIP runtimes and the second would not see the GPU.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built. Build it with `python ragged_paged_kv_amd/_build.py` "
@@ -84,7 +89,7 @@ def _check(status: int, where: str):
 
 
 # ---------------------------------------------------------------------------------------------
-# torch marshalling (torch is imported lazily so that the host-only entry points work without it)
+# torch marshalling
 
 
 def _torch():

@@ -437,8 +437,8 @@ def pin_split_merge(orc, batch, seed=9):
         m = l_.max(axis=2)
         tot = m + np.log(np.exp(l_ - m[..., None]).sum(axis=2))
         assert np.max(np.abs(tot - lse)) < 1e-12
-    # a range with lse = -inf carries no weight whatever its o holds
-    o2 = np.concatenate([o, np.full(o.shape[:2] + (1,) + o.shape[3:], 1e300)], axis=2)
+    # a range with lse = -inf carries no weight whatever its o holds (NaN, as 0/0 would give)
+    o2 = np.concatenate([o, np.full(o.shape[:2] + (1,) + o.shape[3:], np.nan)], axis=2)
     l2 = np.concatenate([l_, np.full(l_.shape[:2] + (1,), -np.inf)], axis=2)
     merged2 = orc.merge_partials(o2, l2, n + 1)
     assert np.max(np.abs(merged2 - out)) < 1e-12

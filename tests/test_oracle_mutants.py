@@ -41,8 +41,10 @@ MUTANTS = {
     # cache write puts V rows into the K cache
     "write-swap": ("kflat[slot] = k[t]", "kflat[slot] = v[t]", 1),
     # merge forgets the max shift's weight for each range
-    "merge-unweighted": ("num = (w[:, :, None] * o_part[t, :, :n]).sum(axis=1)",
-                         "num = o_part[t, :, :n].sum(axis=1)", 1),
+    "merge-unweighted": ("num = (w[:, :, None] * o).sum(axis=1)", "num = o.sum(axis=1)", 1),
+    # merge lets an empty range's undefined o through
+    "merge-empty-range": ("o = np.where(nonempty[:, :, None], o_part[t, :, :n], 0.0)",
+                          "o = o_part[t, :, :n]", 1),
     # lse misses the max term
     "lse-no-max": ("lse = np.where(empty, -np.inf, m[:, 0] + np.log(np.where(empty, 1.0, ssum)))",
                    "lse = np.where(empty, -np.inf, np.log(np.where(empty, 1.0, ssum)))", 1),
