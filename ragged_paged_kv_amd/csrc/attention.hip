@@ -20,8 +20,9 @@
 // Output lane (n, g) = (lane % 16, lane / 16) holds column n (a query row) and rows 4g..4g+3,
 // so each lane carries one query row: the running max / sum are lane-local after a 2-step
 // cross-group reduction, and the rescale of O needs no data movement. The contraction index
-// may be permuted freely as long as A and B agree: lane group g takes dims [g*D/4, (g+1)*D/4)
-// of Q and K (contiguous 16-byte loads), and keys {16j + 4g + i} of P and V, which is exactly
+// may be permuted freely as long as A and B agree: in k-step kk lane group g takes an 8-dim chunk
+// of Q and K (decode: dims [32 kk + 8 g, +8), prefill: [g D/4 + 8 kk, +8); 16-byte loads), and
+// keys {16j + 4g + i} of P and V, which is exactly
 // where the S^T tile leaves them, so P feeds the second MFMA without a shuffle. V arrives with
 // 8 dims of one key per 16 bytes; 8 such rows are transposed in registers with byte permutes
 // into the 8-keys-per-dim operand.
@@ -31,6 +32,8 @@
 // unassigned blocks) cannot reach the output.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <string>
 
@@ -40,12 +43,14 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Running maxima start at this finite floor so that exp2(m_old - m_new) never sees inf - inf.
 constexpr float kMaxFloor = -1e30f;
-constexpr int kMaxSplitTokens = 4096;
+constexpr int kMaxSplitTokens = 2048;  // partition size cap: <= 129 table entries at bs 16
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRows = kPrefillWaves * 32;  // query rows (token x head) per prefill tile
 constexpr int kDecodeWaves = 4;
@@ -136,6 +141,33 @@ __device__ inline bf16x8 vt_operand(const uint32_t (&v)[8][D / 32], int jt) {
 // A sequence breaking the contract (q = 0, kv_len < q, more KV than its table row addresses,
 // a decode-type q beyond max_q_len, more partitions than max_kv_len allows) gets no work item,
 // so nothing is read or written out of bounds; its output rows are then left unwritten.
+//
+// Decode items are ordered longest first, so that the work queue ends on short items: every
+// full P-token partition first (in sequence order), then each sequence's last, partial
+// partition, bucketed by decreasing length. Prefill items: a sequence's last query tiles (they
+// see the most keys) first.
+constexpr int kTailBuckets = 32;
+
+__device__ inline int seq_items(const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_lens,
+                                int s, int num_seqs, int G, int P, int qmaxd, int max_splits,
+                                int bq, int bs, int max_blocks, int& nfull, int& rem, int& np) {
+  nfull = 0;
+  rem = 0;
+  np = 0;
+  if (s >= num_seqs) return 0;
+  const int q = cu[s + 1] - cu[s];
+  const int L = kv_lens[s];
+  if (q <= 0 || L < q || (L + bs - 1) / bs > max_blocks) return 0;
+  if (q * G <= 16) {
+    if (q > qmaxd || (L + P - 1) / P > max_splits) return 0;
+    nfull = L / P;
+    rem = L - nfull * P;
+  } else {
+    np = (q + bq - 1) / bq;
+  }
+  return 1;
+}
+
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu,
                                                     const int32_t* __restrict__ kv_lens,
                                                     int32_t num_seqs, int32_t G, int32_t P,
@@ -147,25 +179,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   __shared__ int32_t sd[1024];
   __shared__ int32_t sp[1024];
   __shared__ int32_t base[2];
+  __shared__ int32_t tail_count[kTailBuckets];
+  __shared__ int32_t tail_next[kTailBuckets];
   const int tid = threadIdx.x;
   if (tid == 0) base[0] = base[1] = 0;
+  if (tid < kTailBuckets) tail_count[tid] = tail_next[tid] = 0;
   __syncthreads();
+  // pass 1: full partitions and prefill tiles by prefix sums; count tails per length bucket
   for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
     const int s = s0 + tid;
-    int nd = 0, np = 0;
-    if (s < num_seqs) {
-      const int q = cu[s + 1] - cu[s];
-      const int L = kv_lens[s];
-      if (q > 0 && L >= q && (L + bs - 1) / bs <= max_blocks) {
-        if (q * G <= 16) {
-          nd = (L + P - 1) / P;
-          if (q > qmaxd || nd > max_splits) nd = 0;
-        } else {
-          np = (q + bq - 1) / bq;
-        }
-      }
-    }
-    sd[tid] = nd;
+    int nfull, rem, np;
+    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, nfull, rem, np);
+    if (rem > 0) atomicAdd(&tail_count[(P - rem) * kTailBuckets / P], 1);
+    sd[tid] = nfull;
     sp[tid] = np;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -176,11 +202,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       sp[tid] += b;
       __syncthreads();
     }
-    const int64_t ed = (int64_t)base[0] + sd[tid] - nd;
+    const int64_t ed = (int64_t)base[0] + sd[tid] - nfull;
     const int64_t ep = (int64_t)base[1] + sp[tid] - np;
-    for (int k = 0; k < nd; ++k)
+    for (int k = 0; k < nfull; ++k)
       if (ed + k < dec_cap) dec[ed + k] = Work{s, k};
-    // a sequence's last query tiles see the most keys: emit them first
     for (int k = 0; k < np; ++k)
       if (ep + k < pre_cap) pre[ep + k] = Work{s, np - 1 - k};
     __syncthreads();
@@ -190,48 +215,82 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     }
     __syncthreads();
   }
+  // bucket offsets after the full partitions (bucket 0 holds the longest tails)
   if (tid == 0) {
-    counts[0] = (int32_t)min((int64_t)base[0], dec_cap);
+    int acc = base[0];
+    for (int b = 0; b < kTailBuckets; ++b) {
+      tail_next[b] = acc;
+      acc += tail_count[b];
+    }
+    counts[0] = (int32_t)min((int64_t)acc, dec_cap);
     counts[1] = (int32_t)min((int64_t)base[1], pre_cap);
+    counts[2] = 0;  // decode work-queue head
+  }
+  __syncthreads();
+  // pass 2: place the tails
+  for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
+    const int s = s0 + tid;
+    int nfull, rem, np;
+    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, nfull, rem, np);
+    if (rem > 0) {
+      const int64_t pos = atomicAdd(&tail_next[(P - rem) * kTailBuckets / P], 1);
+      if (pos < dec_cap) dec[pos] = Work{s, nfull};
+    }
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode / split-KV kernel: one workgroup of 4 waves per (KV partition, KV head). Waves take
-// interleaved 32-key steps of the partition and merge through LDS at the end. K/V fragments
-// are loaded straight from HBM into registers (16-byte loads), one step ahead.
+// Decode / split-KV kernel. Persistent waves, each working alone: a wave takes one
+// (KV partition, KV head) item at a time from a queue and streams its keys 32 at a time. K/V
+// fragments go straight from HBM into registers with 16-byte loads, one step ahead of the
+// MFMAs; the partition's block ids sit one per lane and are broadcast with readlane. No LDS and
+// no barriers, so a wave's start-up and write-out overlap with the other waves' streaming.
 
+// K/V are streamed once per call: non-temporal loads keep them from displacing reusable lines.
+__device__ inline u32x4 ld_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ inline u32x2 ld_stream8(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+// Issue the loads of one 32-key step into registers. K: lane (n, g) reads dims [32 kk + 8 g, +8)
+// of key 16 j + n, so one instruction covers 64 contiguous bytes of each of 16 key rows and the
+// next one completes each 128-byte line: ordinary cached loads. V: lane (c = n, g) reads chunk n
+// of key 16 (e / 4) + 4 g + e % 4, whole 256-byte rows per instruction: streaming loads.
+// row_j = (block_j * bs + offset_j) * Hkv + kvh is the cache row of the first key of group j.
 template <int D>
 __device__ inline void load_step(KVFrag<D>& f, const __bf16* __restrict__ kc,
                                  const __bf16* __restrict__ vc, int64_t row0, int64_t row1,
                                  int Hkv, int n, int g) {
-  // row_j = (block_j * bs + offset_j) * Hkv + kvh: cache row of the first key of group j
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int64_t r = (j ? row1 : row0) + (int64_t)n * Hkv;
-    const bf16x8* p = reinterpret_cast<const bf16x8*>(kc + r * D + g * (D / 4));
+    const __bf16* p = kc + r * D + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < KVFrag<D>::KSTEPS; ++kk) f.k[j][kk] = p[kk];
+    for (int kk = 0; kk < KVFrag<D>::KSTEPS; ++kk)
+      f.k[j][kk] = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int64_t r = ((e >> 2) ? row1 : row0) + (int64_t)(4 * g + (e & 3)) * Hkv;
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(vc + r * D + n * (D / 16));
+    const __bf16* p = vc + r * D + n * (D / 16);
     if constexpr (D == 128) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      const u32x4 x = ld_stream16(p);
       f.v[e][0] = x.x; f.v[e][1] = x.y; f.v[e][2] = x.z; f.v[e][3] = x.w;
     } else {
-      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      const u32x2 x = ld_stream8(p);
       f.v[e][0] = x.x; f.v[e][1] = x.y;
     }
   }
 }
 
-// Consumes the fragment (its V words are zeroed in place past the range end).
+// One 32-key step: S^T = K Q^T, online softmax, O^T += V^T P^T. Consumes the fragment: V words
+// of keys past the range end are zeroed in place (their slots may hold anything, NaN included).
 template <int D>
-__device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], int k0,
-                                    int kend, int last_key, float scale_log2, int g, float& m,
-                                    float& l, f32x4 (&o)[D / 16]) {
+__device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], int k0, int kend,
+                                    int last_key, float scale_log2, int g, float& m, float& l,
+                                    f32x4 (&o)[D / 16]) {
   constexpr int KSTEPS = D / 32;
   f32x4 acc[2];
 #pragma unroll
@@ -241,7 +300,6 @@ __device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], in
     for (int kk = 0; kk < KSTEPS; ++kk) acc[j] = mfma16x16x32(f.k[j][kk], qf[kk], acc[j]);
   }
   const bf16x8 pb = softmax_step<D / 16>(acc, k0, kend, last_key, scale_log2, g, m, l, o);
-  // zero V of keys past the range end (their slots may hold anything, NaN included)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int key = k0 + 16 * (e >> 2) + 4 * g + (e & 3);
@@ -254,146 +312,141 @@ __device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], in
   for (int jt = 0; jt < D / 16; ++jt) o[jt] = mfma16x16x32(vt_operand<D>(f.v, jt), pb, o[jt]);
 }
 
+// Block id of key k (uniform) from the partition's table entries held one per lane in three
+// registers (entry jb0 + 64 r + lane in bt[r]).
+__device__ inline int block_of(const int (&bt)[3], int jj) {
+  const int v = jj < 64 ? bt[0] : (jj < 128 ? bt[1] : bt[2]);
+  return __builtin_amdgcn_readlane(v, jj & 63);
+}
+
 template <int D>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_kernel(
     const __bf16* __restrict__ q, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables,
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     __bf16* __restrict__ out, float* __restrict__ o_part, float* __restrict__ lse_part,
-    const Work* __restrict__ items, const int32_t* __restrict__ counts, int32_t Hq, int32_t Hkv,
-    int32_t bs, int32_t max_blocks_per_seq, int32_t P, int32_t max_splits, int32_t qmaxd,
+    const Work* __restrict__ items, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ queue, int32_t Hq, int32_t Hkv, int32_t bs,
+    int32_t max_blocks_per_seq, int32_t P, int32_t max_splits, int32_t qmaxd,
     float scale_log2) {
-  constexpr int NW = kDecodeWaves;
   constexpr int KSTEPS = D / 32;
   constexpr int NO = D / 16;  // output tiles (dims) per row
-  constexpr int OSTRIDE = D + 4;
-  __shared__ int32_t sm_bt[kMaxSplitTokens / 16 + 2];
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[NW][16][OSTRIDE];
-
-  const int item = blockIdx.x / Hkv;
-  const int kvh = blockIdx.x - item * Hkv;
-  if (item >= counts[0]) return;
-  const Work w = items[item];
-  const int s = w.seq, split = w.idx;
-  const int G = Hq / Hkv;
-  const int q0 = cu[s];
-  const int qn = cu[s + 1] - q0;
-  const int L = kv_lens[s];
-  const int kb = split * P;
-  const int ke = min(L, kb + P);
-  const int nsplit = (L + P - 1) / P;
-  const int rows = qn * G;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
+  const int G = Hq / Hkv;
+  const int total = counts[0] * Hkv;
 
-  // block-table entries of this partition -> LDS
-  const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
-  const int jb0 = kb / bs;
-  const int nbt = (ke + bs - 1) / bs - jb0;
-  for (int i = tid; i < nbt; i += NW * 64) sm_bt[i] = bt_row[jb0 + i];
+  // Each wave pulls (partition, KV head) items until the queue is exhausted; every wave leaves
+  // the loop once the shared counter passes `total`.
+  while (true) {
+    int idx = 0;
+    if (lane == 0) idx = atomicAdd(queue, 1);
+    idx = __builtin_amdgcn_readfirstlane(idx);
+    if (idx >= total) break;
+    const int e = idx / Hkv;
+    const int kvh = idx - e * Hkv;
+    const Work w = items[e];
+    const int s = w.seq, split = w.idx;
+    const int q0 = cu[s];
+    const int qn = cu[s + 1] - q0;
+    const int L = kv_lens[s];
+    const int kb = split * P;
+    const int ke = min(L, kb + P);
+    const int nsplit = (L + P - 1) / P;
+    const int rows = qn * G;
 
-  // Q^T operand: lane column n is query row n = (token n / G, head n % G)
-  bf16x8 qf[KSTEPS];
-  int last_key = -1;
-  if (n < rows) {
-    const int qi = n / G, hh = n - (n / G) * G;
-    const bf16x8* p = reinterpret_cast<const bf16x8*>(
-        q + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + g * (D / 4));
+    // block-table entries of this partition, one per lane
+    const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
+    const int jb0 = kb / bs;
+    const int nbt = (ke + bs - 1) / bs - jb0;
+    int bt[3];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = p[kk];
-    last_key = L - qn + qi;
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
-  }
-  __syncthreads();
+    for (int r = 0; r < 3; ++r) {
+      const int j = 64 * r + lane;
+      bt[r] = j < nbt ? bt_row[jb0 + j] : 0;
+    }
 
-  float m = kMaxFloor, l = 0.f;
-  f32x4 o[NO];
+    // Q^T operand: lane column n is query row n = (token n / G, head n % G)
+    bf16x8 qf[KSTEPS];
+    int last_key = -1;
+    if (n < rows) {
+      const int qi = n / G, hh = n - (n / G) * G;
+      const __bf16* pq = q + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + g * 8;
 #pragma unroll
-  for (int t = 0; t < NO; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(pq + 32 * kk);
+      last_key = L - qn + qi;
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) qf[kk][x] = (__bf16)0.f;
+    }
 
-  // cache row (in units of D elements) of the first key of a 16-key group starting at key k
-  auto group_row = [&](int k) -> int64_t {
-    const int kk = k < ke ? k : kb;  // groups wholly past the end alias the first group
-    const int blk = sm_bt[kk / bs - jb0];
-    return ((int64_t)blk * bs + (kk % bs)) * Hkv + kvh;
-  };
+    float m = kMaxFloor, l = 0.f;
+    f32x4 o[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int stride = 32 * NW;
-  int k0 = kb + 32 * wave;
-  if (k0 < ke) {
+    // cache row (units of D elements) of the first key of the 16-key group starting at key k;
+    // groups wholly past the range end alias the first group (loaded, then masked)
+    auto group_row = [&](int k) -> int64_t {
+      const int kk = k < ke ? k : kb;
+      const int blk = block_of(bt, kk / bs - jb0);
+      return ((int64_t)blk * bs + (kk % bs)) * Hkv + kvh;
+    };
+
+    int k0 = kb;
     KVFrag<D> fa, fb;
     load_step<D>(fa, k_cache, v_cache, group_row(k0), group_row(k0 + 16), Hkv, n, g);
     while (true) {
-      const int k1 = k0 + stride;
+      const int k1 = k0 + 32;
       if (k1 < ke) load_step<D>(fb, k_cache, v_cache, group_row(k1), group_row(k1 + 16), Hkv, n, g);
       compute_step<D>(fa, qf, k0, ke, last_key, scale_log2, g, m, l, o);
       if (k1 >= ke) break;
-      const int k2 = k1 + stride;
+      const int k2 = k1 + 32;
       if (k2 < ke) load_step<D>(fa, k_cache, v_cache, group_row(k2), group_row(k2 + 16), Hkv, n, g);
       compute_step<D>(fb, qf, k1, ke, last_key, scale_log2, g, m, l, o);
       if (k2 >= ke) break;
       k0 = k2;
     }
-  }
 
-  // merge the waves: each writes its row statistics and O rows (lane (n, g) holds row n,
-  // dims (4g + i) * NO + jt for output tile jt and accumulator element i)
-  if (g == 0) {
-    sm_m[wave][n] = m;
-    sm_l[wave][n] = l;
-  }
+    // lane (n, g) holds row n, dims (4g + i) * NO + jt
+    if (n < rows) {
+      const int qi = n / G, hh = n - (n / G) * G;
+      const int h = kvh * G + hh;
+      if (nsplit == 1) {
+        const float inv = 1.f / l;
+        __bf16* dst = out + ((int64_t)(q0 + qi) * Hq + h) * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float* dst = &sm_o[wave][n][(4 * g + i) * NO];
+        for (int i = 0; i < 4; ++i) {
+          __bf16 r[NO];
 #pragma unroll
-    for (int jt = 0; jt < NO; ++jt) dst[jt] = o[jt][i];
-  }
-  __syncthreads();
-
-  // 256 threads: row = tid / 16, dims [c * NO, (c+1) * NO)
-  const int row = tid >> 4, c = tid & 15;
-  if (row >= rows) return;
-  float M = kMaxFloor;
+          for (int jt = 0; jt < NO; ++jt) r[jt] = (__bf16)(o[jt][i] * inv);
+          if constexpr (NO == 8)
+            *reinterpret_cast<bf16x8*>(dst + (4 * g + i) * NO) = __builtin_bit_cast(bf16x8, r);
+          else
+            *reinterpret_cast<uint2*>(dst + (4 * g + i) * NO) = __builtin_bit_cast(uint2, r);
+        }
+      } else {
+        const int64_t prow = (int64_t)s * qmaxd + qi;
+        const int64_t base = (prow * Hq + h) * max_splits + split;
+        const bool empty = !(l > 0.f);
+        const float inv = empty ? 0.f : 1.f / l;
+        float* dst = o_part + base * D;
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][row]);
-  float lsum = 0.f;
-  float acc[NO];
+        for (int i = 0; i < 4; ++i) {
+          float r[NO];
 #pragma unroll
-  for (int i = 0; i < NO; ++i) acc[i] = 0.f;
+          for (int jt = 0; jt < NO; ++jt) r[jt] = o[jt][i] * inv;
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww) {
-    const float sc = __builtin_amdgcn_exp2f(sm_m[ww][row] - M);
-    lsum += sc * sm_l[ww][row];
-#pragma unroll
-    for (int i = 0; i < NO; ++i) acc[i] += sc * sm_o[ww][row][c * NO + i];
-  }
-  const int qi = row / G, hh = row - (row / G) * G;
-  const int h = kvh * G + hh;
-  if (nsplit == 1) {
-    const float inv = 1.f / lsum;
-    __bf16 r[NO];
-#pragma unroll
-    for (int i = 0; i < NO; ++i) r[i] = (__bf16)(acc[i] * inv);
-    __bf16* dst = out + ((int64_t)(q0 + qi) * Hq + h) * D + c * NO;
-    if constexpr (NO == 8) *reinterpret_cast<bf16x8*>(dst) = __builtin_bit_cast(bf16x8, r);
-    else *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, r);
-  } else {
-    const int64_t prow = (int64_t)s * qmaxd + qi;
-    const int64_t base = (prow * Hq + h) * max_splits + split;
-    const bool empty = !(lsum > 0.f);
-    const float inv = empty ? 0.f : 1.f / lsum;
-    float* dst = o_part + base * D + c * NO;
-#pragma unroll
-    for (int i = 0; i < NO; ++i) dst[i] = acc[i] * inv;
-    if (c == 0) lse_part[base] = empty ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+          for (int c = 0; c < NO; c += 4)
+            *reinterpret_cast<float4*>(dst + (4 * g + i) * NO + c) =
+                make_float4(r[c], r[c + 1], r[c + 2], r[c + 3]);
+        }
+        if (g == 0) lse_part[base] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+      }
+    }
   }
 }
 
@@ -585,18 +638,57 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// Log-sum-exp merge of KV partitions. One workgroup per partial row; D/8 threads per head.
+// Log-sum-exp merge of KV partitions. One thread per (partial row, head, 8-dim chunk).
 // INTERNAL: partial row = (sequence, token of the sequence), count derived from kv_lens.
 // Otherwise: partial row = packed token, count from num_splits.
+// The first kReduceBatch partitions' lse and o are loaded together with the count (slots past
+// the count are read but never used), so a typical row costs one memory round trip.
+constexpr int kReduceBatch = 8;
+
+template <int D>
+__device__ inline void merge_accumulate(const float4 (&a)[kReduceBatch], const float4 (&b)[kReduceBatch],
+                                        const float (&lk)[kReduceBatch], int kmax, float M,
+                                        float& wsum, float (&acc)[8]) {
+#pragma unroll
+  for (int k = 0; k < kReduceBatch; ++k) {
+    // an empty partition (lse = -inf) has no weight and its o is never used
+    if (k < kmax && lk[k] != -INFINITY) {
+      const float wk = __builtin_amdgcn_exp2f((lk[k] - M) * kLog2e);
+      wsum += wk;
+      acc[0] += wk * a[k].x; acc[1] += wk * a[k].y; acc[2] += wk * a[k].z; acc[3] += wk * a[k].w;
+      acc[4] += wk * b[k].x; acc[5] += wk * b[k].y; acc[6] += wk * b[k].z; acc[7] += wk * b[k].w;
+    }
+  }
+}
 
 template <int D, bool INTERNAL>
 __global__ __launch_bounds__(256) void reduce_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
     const int32_t* __restrict__ num_splits, __bf16* __restrict__ out, int32_t Hq,
-    int32_t max_splits, const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_lens,
-    int32_t qmaxd, int32_t G, int32_t P) {
-  constexpr int TPH = D / 8;
-  const int64_t prow = blockIdx.x;
+    int32_t max_splits, int64_t nrows, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ kv_lens, int32_t qmaxd, int32_t G, int32_t P) {
+  constexpr int CH = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)Hq * CH;
+  const int64_t prow = gid / per_row;
+  if (prow >= nrows) return;
+  const int rem = (int)(gid - prow * per_row);
+  const int h = rem / CH, c = rem - (rem / CH) * CH;
+  const int64_t base = (prow * Hq + h) * max_splits;
+  const int nb = min(max_splits, kReduceBatch);
+  float lk[kReduceBatch];
+  float4 a[kReduceBatch], b[kReduceBatch];
+#pragma unroll
+  for (int k = 0; k < kReduceBatch; ++k) {
+    if (k < nb) {
+      lk[k] = lse_part[base + k];
+      const float4* p = reinterpret_cast<const float4*>(o_part + (base + k) * D + c * 8);
+      a[k] = p[0];
+      b[k] = p[1];
+    } else {
+      lk[k] = -INFINITY;
+    }
+  }
   int64_t t;
   int ns;
   if constexpr (INTERNAL) {
@@ -611,33 +703,35 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     ns = min(num_splits[t], max_splits);
     if (ns <= 0) return;
   }
-  const int c = threadIdx.x % TPH;
-  for (int h = threadIdx.x / TPH; h < Hq; h += 256 / TPH) {
-    const int64_t base = (prow * Hq + h) * max_splits;
-    float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, lse_part[base + k]);
-    float acc[8];
+  float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    float wsum = 0.f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < ns; ++k) {
-        const float lk = lse_part[base + k];
-        if (lk == -INFINITY) continue;  // empty partition: no weight, its o is not read
-        const float wk = __builtin_amdgcn_exp2f((lk - M) * kLog2e);
-        wsum += wk;
-        const float4* p = reinterpret_cast<const float4*>(o_part + (base + k) * D + c * 8);
-        const float4 a = p[0], b = p[1];
-        acc[0] += wk * a.x; acc[1] += wk * a.y; acc[2] += wk * a.z; acc[3] += wk * a.w;
-        acc[4] += wk * b.x; acc[5] += wk * b.y; acc[6] += wk * b.z; acc[7] += wk * b.w;
+  for (int k = 0; k < kReduceBatch; ++k)
+    if (k < ns) M = fmaxf(M, lk[k]);
+  for (int k = kReduceBatch; k < ns; ++k) M = fmaxf(M, lse_part[base + k]);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    merge_accumulate<D>(a, b, lk, ns, M, wsum, acc);
+    for (int k0 = kReduceBatch; k0 < ns; k0 += kReduceBatch) {
+#pragma unroll
+      for (int k = 0; k < kReduceBatch; ++k) {
+        if (k0 + k < ns) {
+          lk[k] = lse_part[base + k0 + k];
+          const float4* p = reinterpret_cast<const float4*>(o_part + (base + k0 + k) * D + c * 8);
+          a[k] = p[0];
+          b[k] = p[1];
+        }
       }
+      merge_accumulate<D>(a, b, lk, ns - k0, M, wsum, acc);
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    __bf16 r[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (__bf16)(acc[i] * inv);
-    *reinterpret_cast<bf16x8*>(out + (t * Hq + h) * D + c * 8) = __builtin_bit_cast(bf16x8, r);
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  __bf16 r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x8*>(out + (t * Hq + h) * D + c * 8) = __builtin_bit_cast(bf16x8, r);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -656,10 +750,10 @@ int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t 
     int32_t p = (int32_t)cb::ceil_div(requested, 32) * 32;
     return p > kMaxSplitTokens ? kMaxSplitTokens : p;
   }
-  // aim at ~16k (partition, KV head) workgroups over the batch's upper-bound key count
+  // aim at ~8k (partition, KV head) items over the batch's upper-bound key count
   const int64_t keys = (int64_t)max_kv_len * num_seqs * Hkv;
   int64_t p = 256;
-  while (p < kMaxSplitTokens && keys / p > 16384) p *= 2;
+  while (p < kMaxSplitTokens && keys / p > 8192) p *= 2;
   return (int32_t)p;
 }
 
@@ -691,6 +785,26 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, in
 }
 
 bool supported_ratio(int32_t G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+
+// Compute units of the current device, queried once per device.
+bool device_cus(int* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return true;
+    }
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+    return false;
+  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  *out = v;
+  return true;
+}
 
 }  // namespace
 
@@ -780,28 +894,37 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
           num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
   }
   {
-    const unsigned grid = (unsigned)(p.dec_cap * num_kv_heads);
+    // persistent: two 4-wave workgroups per compute unit (2 waves per SIMD), never more
+    // workgroups than a quarter of the items
+    int cus = 0;
+    if (!device_cus(&cus)) return fail(CB_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
+    const int64_t items = p.dec_cap * num_kv_heads;
+    const unsigned grid = (unsigned)std::max<int64_t>(
+        1, std::min<int64_t>((items + kDecodeWaves - 1) / kDecodeWaves, 2 * (int64_t)cus));
+    int32_t* queue = counts + 2;
     if (head_dim == 128)
       decode_kernel<128><<<grid, kDecodeWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
-          num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits, p.qmaxd,
-          scale_log2);
+          queue, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits,
+          p.qmaxd, scale_log2);
     else
       decode_kernel<64><<<grid, kDecodeWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
-          num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits, p.qmaxd,
-          scale_log2);
+          queue, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits,
+          p.qmaxd, scale_log2);
   }
   if (p.max_splits > 1) {
-    const unsigned grid = (unsigned)((int64_t)num_seqs * p.qmaxd);
+    const int64_t nrows = (int64_t)num_seqs * p.qmaxd;
+    const int64_t threads = nrows * num_q_heads * (head_dim / 8);
+    const unsigned grid = (unsigned)((threads + 255) / 256);
     if (head_dim == 128)
       reduce_kernel<128, true><<<grid, 256, 0, st>>>(o_part, lse_part, nullptr, op, num_q_heads,
-                                                     p.max_splits, cu_seqlens_q, kv_lens, p.qmaxd,
-                                                     p.G, p.P);
+                                                     p.max_splits, nrows, cu_seqlens_q, kv_lens,
+                                                     p.qmaxd, p.G, p.P);
     else
       reduce_kernel<64, true><<<grid, 256, 0, st>>>(o_part, lse_part, nullptr, op, num_q_heads,
-                                                    p.max_splits, cu_seqlens_q, kv_lens, p.qmaxd,
-                                                    p.G, p.P);
+                                                    p.max_splits, nrows, cu_seqlens_q, kv_lens,
+                                                    p.qmaxd, p.G, p.P);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(CB_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
@@ -823,14 +946,17 @@ extern "C" int cb_split_kv_reduce(const float* o_part, const float* lse_part,
     return fail(CB_ERR_INVALID_ARG, "o_part and out must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   __bf16* op = static_cast<__bf16*>(out);
+  const int64_t threads = (int64_t)num_tokens * num_q_heads * (head_dim / 8);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return fail(CB_ERR_UNSUPPORTED, "cb_split_kv_reduce: too many rows");
   if (head_dim == 128)
-    reduce_kernel<128, false><<<num_tokens, 256, 0, st>>>(o_part, lse_part, num_splits, op,
-                                                          num_q_heads, max_splits, nullptr,
-                                                          nullptr, 1, 1, 1);
+    reduce_kernel<128, false><<<(unsigned)grid, 256, 0, st>>>(
+        o_part, lse_part, num_splits, op, num_q_heads, max_splits, num_tokens, nullptr, nullptr,
+        1, 1, 1);
   else
-    reduce_kernel<64, false><<<num_tokens, 256, 0, st>>>(o_part, lse_part, num_splits, op,
-                                                         num_q_heads, max_splits, nullptr,
-                                                         nullptr, 1, 1, 1);
+    reduce_kernel<64, false><<<(unsigned)grid, 256, 0, st>>>(
+        o_part, lse_part, num_splits, op, num_q_heads, max_splits, num_tokens, nullptr, nullptr,
+        1, 1, 1);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(CB_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(e));
   return cb::ok();

@@ -111,7 +111,7 @@ def test_workspace_size_and_split_choice():
     p = cb.cb_paged_attention_split_tokens(256, 8, 4096)
     assert p % 32 == 0 and 256 <= p <= 4096
     assert cb.cb_paged_attention_split_tokens(4, 2, 40, 100) == 128   # rounded up to 32
-    assert cb.cb_paged_attention_split_tokens(4, 2, 40, 100000) == 4096
+    assert cb.cb_paged_attention_split_tokens(4, 2, 40, 100000) == 2048
     one = cb.cb_paged_attention_workspace_size(4, 27, 4, 2, 64, 16, 24, 40, 64)
     assert one > 0
     assert cb.cb_paged_attention_workspace_size(0, 0, 4, 2, 64, 16, 1, 1) == 0
