@@ -464,7 +464,8 @@ struct PrefillSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
+__global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(
     const __bf16* __restrict__ q, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables,
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
