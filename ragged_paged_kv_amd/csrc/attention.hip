@@ -60,19 +60,45 @@ struct Work {
   int32_t idx;  // KV partition (decode) or query tile (prefill)
 };
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// LDS transpose read of 4 x 16-bit per lane: within each 16-lane group, lane 4a + b receives
+// element b of the 8-byte reads of lanes a, 4 + a, 8 + a and 12 + a (in that order).
+__device__ inline s16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+template <bool B>
+struct Tag {
+  static constexpr bool value = B;
+};
+
 __device__ inline f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ inline float xor_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// Reductions over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with the row-swap
+// permutes: permlane16_swap(x, x) yields the values of the even and the odd 16-lane row of each
+// row pair, permlane32_swap(x, x) those of the lower and the upper 32 lanes.
+__device__ inline float group_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ inline float xor_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+__device__ inline float group_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+
+// The running reference max of a row moves only when a chunk's max exceeds it by more than this
+// (log2 units): probabilities are then bounded by 2^8, and the rescale of O is skipped for most
+// chunks. The result is unchanged: numerator and denominator share the reference.
+constexpr float kRescaleSlack = 8.f;
 
 // Fragments of one 32-key step for one lane.
 template <int D>
@@ -84,54 +110,59 @@ struct KVFrag {
 };
 
 // Online-softmax update of one 16-row tile for one 32-key step.
-//   acc[j][i]: S^T for key k0 + 16j + 4g + i of this lane's row.
-// Keys >= kend or > last_key are masked. Returns P^T (bf16) in the B-operand layout.
-template <int NO>
+//   acc[j][i]: raw score (Q.K) for key k0 + 16j + 4g + i of this lane's row; c = scale * log2(e).
+// With MASK, keys >= kend or > last_key are masked (select to -inf); without it the caller
+// guarantees every key of the step is visible to every row that is written out.
+// m is the row's reference max in scaled log2 units, l its running sum. Returns P^T (bf16) in
+// the B-operand layout.
+template <int NO, bool MASK>
 __device__ inline bf16x8 softmax_step(const f32x4 (&acc)[2], int k0, int kend, int last_key,
-                                      float scale_log2, int g, float& m, float& l,
-                                      f32x4 (&o)[NO]) {
+                                      float c, int g, float& m, float& l, f32x4 (&o)[NO]) {
   float s[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = k0 + 16 * j + 4 * g + i;
-      const float v = acc[j][i] * scale_log2;
-      const float sv = (key < kend && key <= last_key) ? v : -INFINITY;
-      s[4 * j + i] = sv;
-      mx = fmaxf(mx, sv);
+      float v = acc[j][i];
+      if (MASK) {
+        const int key = k0 + 16 * j + 4 * g + i;
+        v = (key < kend && key <= last_key) ? v : -INFINITY;
+      }
+      s[4 * j + i] = v;
+      mx = fmaxf(mx, v);
     }
   }
-  mx = xor_max(mx);
-  const float m_new = fmaxf(m, mx);
-  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+  const float m_chunk = group_max(mx) * c;  // c > 0; -inf stays -inf
+  if (__builtin_amdgcn_ballot_w64(m_chunk > m + kRescaleSlack) != 0) {  // wave-uniform
+    const float m_new = fmaxf(m, m_chunk);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int t = 0; t < NO; ++t) o[t] *= alpha;
+    m = m_new;
+  }
   float rs = 0.f;
   bf16x8 pb;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = __builtin_amdgcn_exp2f(s[e] - m_new);
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -m));
     rs += p;
     pb[e] = (__bf16)p;
   }
-  rs = xor_sum(rs);
-  l = l * alpha + rs;
-  m = m_new;
-#pragma unroll
-  for (int t = 0; t < NO; ++t) o[t] *= alpha;
+  l += group_sum(rs);
   return pb;
 }
 
 // V^T operand of output tile jt: element e = V[key e][dim n*D/16 + jt], from 8 keys' words.
+// perm(hi, lo, 0x05040100) = lo16(lo) | lo16(hi) << 16; perm(hi, lo, 0x07060302) = the high halves.
 template <int D>
 __device__ inline bf16x8 vt_operand(const uint32_t (&v)[8][D / 32], int jt) {
   const int w = jt >> 1;
+  const uint32_t sel = (jt & 1) ? 0x07060302u : 0x05040100u;
   uint32_t d[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const uint32_t lo = v[2 * a][w], hi = v[2 * a + 1][w];
-    d[a] = (jt & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-  }
+  for (int a = 0; a < 4; ++a) d[a] = __builtin_amdgcn_perm(v[2 * a + 1][w], v[2 * a][w], sel);
   return __builtin_bit_cast(bf16x8, d);
 }
 
@@ -287,10 +318,12 @@ __device__ inline void load_step(KVFrag<D>& f, const __bf16* __restrict__ kc,
 
 // One 32-key step: S^T = K Q^T, online softmax, O^T += V^T P^T. Consumes the fragment: V words
 // of keys past the range end are zeroed in place (their slots may hold anything, NaN included).
+// first_last_key: the smallest last visible key over the rows written out (wave-uniform); steps
+// wholly below it and inside the range need no mask.
 template <int D>
 __device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], int k0, int kend,
-                                    int last_key, float scale_log2, int g, float& m, float& l,
-                                    f32x4 (&o)[D / 16]) {
+                                    int last_key, int first_last_key, float scale_log2, int g,
+                                    float& m, float& l, f32x4 (&o)[D / 16]) {
   constexpr int KSTEPS = D / 32;
   f32x4 acc[2];
 #pragma unroll
@@ -299,7 +332,10 @@ __device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], in
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) acc[j] = mfma16x16x32(f.k[j][kk], qf[kk], acc[j]);
   }
-  const bf16x8 pb = softmax_step<D / 16>(acc, k0, kend, last_key, scale_log2, g, m, l, o);
+  const bool interior = k0 + 32 <= kend && k0 + 31 <= first_last_key;
+  const bf16x8 pb =
+      interior ? softmax_step<D / 16, false>(acc, k0, kend, last_key, scale_log2, g, m, l, o)
+               : softmax_step<D / 16, true>(acc, k0, kend, last_key, scale_log2, g, m, l, o);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int key = k0 + 16 * (e >> 2) + 4 * g + (e & 3);
@@ -387,6 +423,7 @@ void decode_kernel(
     f32x4 o[NO];
 #pragma unroll
     for (int t = 0; t < NO; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int first_last_key = L - qn;  // last visible key of the item's first token
 
     // cache row (units of D elements) of the first key of the 16-key group starting at key k;
     // groups wholly past the range end alias the first group (loaded, then masked)
@@ -402,11 +439,11 @@ void decode_kernel(
     while (true) {
       const int k1 = k0 + 32;
       if (k1 < ke) load_step<D>(fb, k_cache, v_cache, group_row(k1), group_row(k1 + 16), Hkv, n, g);
-      compute_step<D>(fa, qf, k0, ke, last_key, scale_log2, g, m, l, o);
+      compute_step<D>(fa, qf, k0, ke, last_key, first_last_key, scale_log2, g, m, l, o);
       if (k1 >= ke) break;
       const int k2 = k1 + 32;
       if (k2 < ke) load_step<D>(fa, k_cache, v_cache, group_row(k2), group_row(k2 + 16), Hkv, n, g);
-      compute_step<D>(fb, qf, k1, ke, last_key, scale_log2, g, m, l, o);
+      compute_step<D>(fb, qf, k1, ke, last_key, first_last_key, scale_log2, g, m, l, o);
       if (k2 >= ke) break;
       k0 = k2;
     }
@@ -456,14 +493,19 @@ void decode_kernel(
 // into LDS by all 256 threads (16-byte loads, double buffered; block ids fetched two steps
 // ahead) and read by every wave.
 
-template <int D>
+template <int D, int KS>
 struct PrefillSmem {
   static constexpr int STRIDE = D + 8;  // bf16 elements per LDS row (16-byte pad)
-  __bf16 k[2][32][STRIDE];
-  __bf16 v[2][32][STRIDE];
+  __bf16 k[2][KS][STRIDE];
+  __bf16 v[2][KS][STRIDE];
 };
 
-template <int D>
+#ifndef CB_PREFILL_KS
+#define CB_PREFILL_KS 32
+#endif
+constexpr int kPrefillKeys = CB_PREFILL_KS;  // keys per LDS tile (one barrier per tile)
+
+template <int D, int KS>
 __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(
     const __bf16* __restrict__ q, const int32_t* __restrict__ cu,
@@ -476,8 +518,9 @@ void prefill_kernel(
   constexpr int NO = D / 16;
   constexpr int CPR = D / 8;                   // 16-byte chunks per key row
   constexpr int RPP = kPrefillWaves * 64 / CPR;  // key rows loaded per pass
-  constexpr int PASSES = 32 / RPP;
-  __shared__ __attribute__((aligned(16))) PrefillSmem<D> sm;
+  constexpr int PASSES = KS / RPP;
+  using SmemT = PrefillSmem<D, KS>;
+  __shared__ __attribute__((aligned(16))) SmemT sm;
 
   const int item = blockIdx.x / Hkv;
   const int kvh = blockIdx.x - item * Hkv;
@@ -493,7 +536,8 @@ void prefill_kernel(
   const int kend = L - qn + tok_end;  // keys [0, kend) are visible to some row of the tile
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
 
   // Q^T operands of this wave's two row tiles
@@ -518,27 +562,60 @@ void prefill_kernel(
     }
   }
 
-  // loader role of this thread: key row lr + pass * RPP of each step, 16-byte chunk lc
+  // smallest last visible key over this wave's rows (its first row's token); rows past tok_end
+  // have zero Q, finite scores and are never written
+  const int wave_first_last_key = L - qn + tok0 + wave * 32 / G;
+
+  // loader role of this thread: key row lr + pass * RPP of each tile, 16-byte chunk lc. A pass
+  // covers whole 16-key groups (RPP is a multiple of 16), each inside one block, so the block id
+  // and in-block offset of a group are wave-uniform; only the row within the group is per lane.
+  static_assert(RPP % 16 == 0, "a load pass must cover whole 16-key groups");
   const int lr = tid / CPR, lc = tid - (tid / CPR) * CPR;
   const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
-  auto fetch_block = [&](int step, int pass) -> int {
-    const int key = step * 32 + lr + pass * RPP;
-    return key < kend ? bt_row[key / bs] : -1;
+  const int64_t lane_off = (int64_t)(lr & 15) * Hkv * D + lc * 8;  // row within group, chunk
+  const int lane_grp = lr >> 4;                                       // group within the pass
+  // cache row (units of D elements) of the first key of each 16-key group of pass ps of a tile;
+  // groups at or past kend are not read (-1)
+  auto group_base = [&](int step, int ps, int grp) -> int64_t {
+    const int key = step * KS + ps * RPP + 16 * grp;
+    if (key >= kend) return -1;
+    const int blk = bt_row[key / bs];
+    return ((int64_t)blk * bs + key % bs) * Hkv + kvh;
   };
+  constexpr int GPP = RPP / 16;  // 16-key groups per pass
   uint4 rk[PASSES], rv[PASSES];
-  auto fetch_kv = [&](int step, const int (&blk)[PASSES]) {
+  // stage the loads of tile `step`; base[ps][grp] from group_base (scalar). Only the last tile
+  // (TAIL) holds keys >= kend: their rows read as zero, so that a masked probability (0) never
+  // meets an unwritten V value.
+  auto fetch_kv = [&](auto tail_tag, int step, const int64_t (&base)[PASSES][GPP]) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
-      const int key = step * 32 + lr + ps * RPP;
-      if (blk[ps] >= 0) {
-        const int64_t row = ((int64_t)blk[ps] * bs + key % bs) * Hkv + kvh;
-        rk[ps] = *reinterpret_cast<const uint4*>(k_cache + row * D + lc * 8);
-        rv[ps] = *reinterpret_cast<const uint4*>(v_cache + row * D + lc * 8);
+      int64_t b = base[ps][0];
+#pragma unroll
+      for (int gi = 1; gi < GPP; ++gi)
+        if (lane_grp == gi) b = base[ps][gi];
+      if (!TAIL || step * KS + ps * RPP + lr < kend) {
+        const int64_t off = b * D + lane_off;
+        rk[ps] = *reinterpret_cast<const uint4*>(k_cache + off);
+        rv[ps] = *reinterpret_cast<const uint4*>(v_cache + off);
       } else {
         rk[ps] = make_uint4(0, 0, 0, 0);
         rv[ps] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  auto fetch = [&](int step, const int64_t (&base)[PASSES][GPP]) {
+    if ((step + 1) * KS <= kend)
+      fetch_kv(Tag<false>{}, step, base);
+    else
+      fetch_kv(Tag<true>{}, step, base);
+  };
+  auto fetch_bases = [&](int step, int64_t (&base)[PASSES][GPP]) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+      for (int gi = 0; gi < GPP; ++gi) base[ps][gi] = group_base(step, ps, gi);
   };
   auto stash = [&](int buf) {
 #pragma unroll
@@ -548,13 +625,11 @@ void prefill_kernel(
     }
   };
 
-  const int nsteps = (kend + 31) / 32;
-  int blk1[PASSES], blk2[PASSES];
-#pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) blk1[ps] = fetch_block(0, ps);
-  fetch_kv(0, blk1);
-#pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) blk1[ps] = nsteps > 1 ? fetch_block(1, ps) : -1;
+  const int nsteps = (kend + KS - 1) / KS;
+  int64_t base1[PASSES][GPP], base2[PASSES][GPP];
+  fetch_bases(0, base1);
+  fetch(0, base1);
+  fetch_bases(nsteps > 1 ? 1 : 0, base1);
   stash(0);
   __syncthreads();
 
@@ -565,76 +640,87 @@ void prefill_kernel(
 #pragma unroll
     for (int t = 0; t < NO; ++t) o[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int st = 0; st < nsteps; ++st) {
+  // one tile: prefetch the next into registers, compute this one from LDS, stash the next
+  auto tile = [&](auto mask_tag, int st) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = st & 1;
     const bool more = st + 1 < nsteps;
     if (more) {
-#pragma unroll
-      for (int ps = 0; ps < PASSES; ++ps) blk2[ps] = st + 2 < nsteps ? fetch_block(st + 2, ps) : -1;
-      fetch_kv(st + 1, blk1);
+      fetch_bases(st + 2 < nsteps ? st + 2 : st + 1, base2);
+      fetch(st + 1, base1);
     }
-    const int k0 = st * 32;
-    // S^T = K Q^T for both row tiles; the K fragment is shared
-    f32x4 acc[2][2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int c = 0; c < KS / 32; ++c) {
+      const int k0 = st * KS + 32 * c;
+      const int kr0 = 32 * c;  // first LDS row of this 32-key chunk
+      // S^T = K Q^T for both row tiles; the K fragment is shared
+      f32x4 acc[2][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 2; ++j) acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * j + n][g * (D / 4) + 8 * kk]);
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt][j] = mfma16x16x32(kf, qf[nt][kk], acc[nt][j]);
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(&sm.k[buf][kr0 + 16 * j + n][g * (D / 4) + 8 * kk]);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[nt][j] = mfma16x16x32(kf, qf[nt][kk], acc[nt][j]);
+        }
       }
-    }
-    bf16x8 pb[2];
+      bf16x8 pb[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      pb[nt] = softmax_step<NO>(acc[nt], k0, kend, last_key[nt], scale_log2, g, m[nt], l[nt], o[nt]);
-    // V^T operands from LDS: 8 keys x (D/16 dims) per lane, transposed in registers
-    uint32_t vw[8][D / 32];
+      for (int nt = 0; nt < 2; ++nt)
+        pb[nt] = softmax_step<NO, MASK>(acc[nt], k0, kend, last_key[nt], scale_log2, g, m[nt],
+                                        l[nt], o[nt]);
+      // V^T operands by transposing LDS reads. Lanes 4j + a of lane group g read key
+      // kr0 + 16h + 4g + j, dims (D/4)a + 4jt .. +3; lane 4a + b of the group receives element b
+      // of those four reads: dim (D/4)a + 4jt + b for keys 16h + 4g + j, j = 0..3, which is the
+      // key order of P^T's elements.
+      const __bf16* vb = &sm.v[buf][kr0 + 4 * g + (n >> 2)][(D / 4) * (n & 3)];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int kr = 16 * (e >> 2) + 4 * g + (e & 3);
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(&sm.v[buf][kr][n * (D / 16)]);
+      for (int jt = 0; jt < NO; ++jt) {
+        const s16x4 lo = lds_read_tr16(vb + 4 * jt);
+        const s16x4 hi = lds_read_tr16(vb + 16 * SmemT::STRIDE + 4 * jt);
+        const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int ww = 0; ww < D / 32; ++ww) vw[e][ww] = p[ww];
-    }
-#pragma unroll
-    for (int jt = 0; jt < NO; ++jt) {
-      const bf16x8 vt = vt_operand<D>(vw, jt);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) o[nt][jt] = mfma16x16x32(vt, pb[nt], o[nt][jt]);
+        for (int nt = 0; nt < 2; ++nt) o[nt][jt] = mfma16x16x32(vt, pb[nt], o[nt][jt]);
+      }
     }
     if (more) {
       stash(buf ^ 1);
 #pragma unroll
-      for (int ps = 0; ps < PASSES; ++ps) blk1[ps] = blk2[ps];
+      for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+        for (int gi = 0; gi < GPP; ++gi) base1[ps][gi] = base2[ps][gi];
     }
     __syncthreads();
-  }
+  };
 
-  // normalise and store: lane (n, g) holds row n, dims (4g + i) * NO + jt
+  // Tiles whose keys are all visible to every row of this wave run without the mask; the rest
+  // (the causal diagonal and the range end) with it. The split point differs between waves,
+  // but every wave runs all nsteps tiles, so the barriers pair up in order.
+  const int n_open = min(nsteps, min(kend, wave_first_last_key + 1) / KS);
+  int st = 0;
+  for (; st < n_open; ++st) tile(Tag<false>{}, st);
+  for (; st < nsteps; ++st) tile(Tag<true>{}, st);
+
+  // normalise and store: lane (n, g) holds row n, dims (D/4)g + 4jt + i (D/4 contiguous dims)
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int R = wave * 32 + nt * 16 + n;
     const int qi = tok0 + R / G, hh = R - (R / G) * G;
     if (qi >= tok_end) continue;
     const float inv = 1.f / l[nt];
-    __bf16* dst = out + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D;
+    __bf16 r[D / 4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __bf16 r[NO];
+    for (int jt = 0; jt < NO; ++jt)
 #pragma unroll
-      for (int jt = 0; jt < NO; ++jt) r[jt] = (__bf16)(o[nt][jt][i] * inv);
-      if constexpr (NO == 8)
-        *reinterpret_cast<bf16x8*>(dst + (4 * g + i) * NO) = __builtin_bit_cast(bf16x8, r);
-      else
-        *reinterpret_cast<uint2*>(dst + (4 * g + i) * NO) = __builtin_bit_cast(uint2, r);
-    }
+      for (int i = 0; i < 4; ++i) r[4 * jt + i] = (__bf16)(o[nt][jt][i] * inv);
+    uint4* dst = reinterpret_cast<uint4*>(out + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + (D / 4) * g);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) dst[c] = __builtin_bit_cast(uint4, *reinterpret_cast<const bf16x8*>(&r[8 * c]));
   }
 }
 
@@ -886,11 +972,11 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
   if (p.pre_cap > 0) {
     const unsigned grid = (unsigned)(p.pre_cap * num_kv_heads);
     if (head_dim == 128)
-      prefill_kernel<128><<<grid, kPrefillWaves * 64, 0, st>>>(
+      prefill_kernel<128, kPrefillKeys><<<grid, kPrefillWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
           num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
     else
-      prefill_kernel<64><<<grid, kPrefillWaves * 64, 0, st>>>(
+      prefill_kernel<64, kPrefillKeys><<<grid, kPrefillWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
           num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
   }
