@@ -51,8 +51,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Running maxima start at this finite floor so that exp2(m_old - m_new) never sees inf - inf.
 constexpr float kMaxFloor = -1e30f;
 constexpr int kMaxSplitTokens = 2048;  // partition size cap: <= 129 table entries at bs 16
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRows = kPrefillWaves * 32;  // query rows (token x head) per prefill tile
+#ifndef CB_PREFILL_WAVES
+#define CB_PREFILL_WAVES 8
+#endif
+#ifndef CB_PREFILL_TILES
+#define CB_PREFILL_TILES 2
+#endif
+constexpr int kPrefillWaves = CB_PREFILL_WAVES;
+constexpr int kPrefillTiles = CB_PREFILL_TILES;  // 16-row MFMA tiles per prefill wave
+constexpr int kPrefillRows = kPrefillWaves * 16 * kPrefillTiles;  // query rows (token x head) per tile
+// two waves per SIMD at two row tiles per wave; with more, the wave needs the whole register file
+constexpr int kPrefillWavesPerSimd = kPrefillTiles > 2 ? 1 : 2;
 constexpr int kDecodeWaves = 4;
 
 struct Work {
@@ -72,6 +81,10 @@ __device__ inline s16x4 lds_read_tr16(const __bf16* p) {
 template <bool B>
 struct Tag {
   static constexpr bool value = B;
+};
+template <int X>
+struct Int {
+  static constexpr int value = X;
 };
 
 __device__ inline f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -109,31 +122,33 @@ struct KVFrag {
   uint32_t v[8][DW];                     // V: key e = 16*(e/4) + 4g + e%4, dims n*D/16 ..
 };
 
-// Online-softmax update of one 16-row tile for one 32-key step.
+// Online softmax of one 16-row tile over one 32-key chunk, in three parts.
 //   acc[j][i]: raw score (Q.K) for key k0 + 16j + 4g + i of this lane's row; c = scale * log2(e).
-// With MASK, keys >= kend or > last_key are masked (select to -inf); without it the caller
-// guarantees every key of the step is visible to every row that is written out.
-// m is the row's reference max in scaled log2 units, l its running sum. Returns P^T (bf16) in
-// the B-operand layout.
-template <int NO, bool MASK>
-__device__ inline bf16x8 softmax_step(const f32x4 (&acc)[2], int k0, int kend, int last_key,
-                                      float c, int g, float& m, float& l, f32x4 (&o)[NO]) {
-  float s[8];
+// m is the row's reference max in scaled log2 units, l its running sum, o its output rows.
+
+// Row max of the chunk (scaled). With MASK, keys >= kend or > last_key are first set to -inf in
+// acc; without it the caller guarantees every key of the chunk is visible to every row that is
+// written out.
+template <bool MASK>
+__device__ inline float chunk_max(f32x4 (&acc)[2], int k0, int kend, int last_key, float c, int g) {
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = acc[j][i];
       if (MASK) {
         const int key = k0 + 16 * j + 4 * g + i;
-        v = (key < kend && key <= last_key) ? v : -INFINITY;
+        acc[j][i] = (key < kend && key <= last_key) ? acc[j][i] : -INFINITY;
       }
-      s[4 * j + i] = v;
-      mx = fmaxf(mx, v);
+      mx = fmaxf(mx, acc[j][i]);
     }
   }
-  const float m_chunk = group_max(mx) * c;  // c > 0; -inf stays -inf
+  return group_max(mx) * c;  // c > 0; -inf stays -inf
+}
+
+// Move the reference max when the chunk's max exceeds it by more than kRescaleSlack.
+template <int NO>
+__device__ inline void rescale_lazy(float m_chunk, float& m, float& l, f32x4 (&o)[NO]) {
   if (__builtin_amdgcn_ballot_w64(m_chunk > m + kRescaleSlack) != 0) {  // wave-uniform
     const float m_new = fmaxf(m, m_chunk);
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);
@@ -142,16 +157,29 @@ __device__ inline bf16x8 softmax_step(const f32x4 (&acc)[2], int k0, int kend, i
     for (int t = 0; t < NO; ++t) o[t] *= alpha;
     m = m_new;
   }
+}
+
+// Probabilities of the chunk against the reference max, added to l; returns P^T (bf16) in the
+// B-operand layout. Masked scores are -inf and give 0.
+__device__ inline bf16x8 chunk_exp(const f32x4 (&acc)[2], float c, float m, float& l) {
   float rs = 0.f;
   bf16x8 pb;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -m));
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e >> 2][e & 3], c, -m));
     rs += p;
     pb[e] = (__bf16)p;
   }
   l += group_sum(rs);
   return pb;
+}
+
+template <int NO, bool MASK>
+__device__ inline bf16x8 softmax_step(f32x4 (&acc)[2], int k0, int kend, int last_key,
+                                      float c, int g, float& m, float& l, f32x4 (&o)[NO]) {
+  const float m_chunk = chunk_max<MASK>(acc, k0, kend, last_key, c, g);
+  rescale_lazy<NO>(m_chunk, m, l, o);
+  return chunk_exp(acc, c, m, l);
 }
 
 // V^T operand of output tile jt: element e = V[key e][dim n*D/16 + jt], from 8 keys' words.
@@ -490,23 +518,25 @@ void decode_kernel(
 // ---------------------------------------------------------------------------------------------
 // Prefill kernel: one workgroup of 4 waves per (query tile of 128 rows, KV head). Each wave owns
 // 32 rows (two 16-row MFMA tiles). K/V tiles of 32 keys are gathered through the block table
-// into LDS by all 256 threads (16-byte loads, double buffered; block ids fetched two steps
-// ahead) and read by every wave.
+// into LDS by all 256 threads and read by every wave. Three LDS tiles are in flight, so a wave
+// can overlap its matrix and vector work: while the exponentials of tile t run on the VALU, the
+// S^T = K Q^T products of tile t + 1 run on the matrix cores, and the P V products of tile t run
+// beside the row maxima of tile t + 1. Tile t + 2 is loaded into registers meanwhile and stored
+// to LDS at the end of the step.
 
-template <int D, int KS>
+constexpr int kPrefillKeys = 32;  // keys per LDS tile (one barrier per tile)
+constexpr int kPrefillBufs = 3;   // LDS tiles: being computed, ready, being filled
+
+template <int D>
 struct PrefillSmem {
-  static constexpr int STRIDE = D + 8;  // bf16 elements per LDS row (16-byte pad)
-  __bf16 k[2][KS][STRIDE];
-  __bf16 v[2][KS][STRIDE];
+  static constexpr int STRIDE = D + 8;  // bf16 per LDS row (16-byte pad)
+  __bf16 k[kPrefillBufs][kPrefillKeys][STRIDE];
+  __bf16 v[kPrefillBufs][kPrefillKeys][STRIDE];
 };
 
-#ifndef CB_PREFILL_KS
-#define CB_PREFILL_KS 32
-#endif
-constexpr int kPrefillKeys = CB_PREFILL_KS;  // keys per LDS tile (one barrier per tile)
-
-template <int D, int KS>
-__global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D>
+__global__ __launch_bounds__(kPrefillWaves * 64)
+__attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
 void prefill_kernel(
     const __bf16* __restrict__ q, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables,
@@ -514,12 +544,19 @@ void prefill_kernel(
     __bf16* __restrict__ out, const Work* __restrict__ items, const int32_t* __restrict__ counts,
     int32_t Hq, int32_t Hkv, int32_t bs, int32_t max_blocks_per_seq, int32_t bq,
     float scale_log2) {
+  constexpr int KS = kPrefillKeys;
+  constexpr int NT = kPrefillTiles;  // 16-row MFMA tiles per wave
   constexpr int KSTEPS = D / 32;
   constexpr int NO = D / 16;
-  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
-  constexpr int RPP = kPrefillWaves * 64 / CPR;  // key rows loaded per pass
+  constexpr int CPR = D / 8;  // 16-byte chunks per key row
+  // threads that load K/V (a whole number of waves) and key rows they cover per pass
+  constexpr int LOADERS = kPrefillWaves * 64 < KS * CPR ? kPrefillWaves * 64 : KS * CPR;
+  constexpr int RPP = LOADERS / CPR;
   constexpr int PASSES = KS / RPP;
-  using SmemT = PrefillSmem<D, KS>;
+  constexpr int GPP = RPP / 16;                  // 16-key groups per pass
+  static_assert(RPP % 16 == 0 && KS % RPP == 0 && LOADERS % 64 == 0,
+                "a load pass must cover whole 16-key groups");
+  using SmemT = PrefillSmem<D>;
   __shared__ __attribute__((aligned(16))) SmemT sm;
 
   const int item = blockIdx.x / Hkv;
@@ -541,11 +578,11 @@ void prefill_kernel(
   const int n = lane & 15, g = lane >> 4;
 
   // Q^T operands of this wave's two row tiles
-  bf16x8 qf[2][KSTEPS];
-  int last_key[2];
+  bf16x8 qf[NT][KSTEPS];
+  int last_key[NT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int R = wave * 32 + nt * 16 + n;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int R = wave * (16 * NT) + nt * 16 + n;
     const int qi = tok0 + R / G, hh = R - (R / G) * G;
     if (qi < tok_end) {
       const bf16x8* p = reinterpret_cast<const bf16x8*>(
@@ -564,17 +601,19 @@ void prefill_kernel(
 
   // smallest last visible key over this wave's rows (its first row's token); rows past tok_end
   // have zero Q, finite scores and are never written
-  const int wave_first_last_key = L - qn + tok0 + wave * 32 / G;
+  const int wave_first_last_key = L - qn + tok0 + wave * (16 * NT) / G;
 
-  // loader role of this thread: key row lr + pass * RPP of each tile, 16-byte chunk lc. A pass
-  // covers whole 16-key groups (RPP is a multiple of 16), each inside one block, so the block id
-  // and in-block offset of a group are wave-uniform; only the row within the group is per lane.
-  static_assert(RPP % 16 == 0, "a load pass must cover whole 16-key groups");
-  const int lr = tid / CPR, lc = tid - (tid / CPR) * CPR;
+  // Loader role of this thread: key row lr + pass * RPP of each tile, 16-byte chunk lc. A pass
+  // covers whole 16-key groups, each inside one block, so the block id and in-block offset of a
+  // group are wave-uniform; only the row within the group is per lane. When the tile has fewer
+  // chunks than the workgroup has threads, the extra threads repeat the first ones (same loads,
+  // same LDS stores), so that every wave runs the same load pipeline.
+  const int ltid = LOADERS < kPrefillWaves * 64 ? tid % LOADERS : tid;
+  const int lr = ltid / CPR, lc = ltid - (ltid / CPR) * CPR;
   const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
   const int64_t lane_off = (int64_t)(lr & 15) * Hkv * D + lc * 8;  // row within group, chunk
   const int lane_grp = lr >> 4;                                       // group within the pass
-  // cache row (units of D elements) of the first key of each 16-key group of pass ps of a tile;
+  // cache row (units of D elements) of the first key of 16-key group grp of pass ps of a tile;
   // groups at or past kend are not read (-1)
   auto group_base = [&](int step, int ps, int grp) -> int64_t {
     const int key = step * KS + ps * RPP + 16 * grp;
@@ -582,134 +621,188 @@ void prefill_kernel(
     const int blk = bt_row[key / bs];
     return ((int64_t)blk * bs + key % bs) * Hkv + kvh;
   };
-  constexpr int GPP = RPP / 16;  // 16-key groups per pass
-  uint4 rk[PASSES], rv[PASSES];
-  // stage the loads of tile `step`; base[ps][grp] from group_base (scalar). Only the last tile
-  // (TAIL) holds keys >= kend: their rows read as zero, so that a masked probability (0) never
-  // meets an unwritten V value.
-  auto fetch_kv = [&](auto tail_tag, int step, const int64_t (&base)[PASSES][GPP]) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      int64_t b = base[ps][0];
-#pragma unroll
-      for (int gi = 1; gi < GPP; ++gi)
-        if (lane_grp == gi) b = base[ps][gi];
-      if (!TAIL || step * KS + ps * RPP + lr < kend) {
-        const int64_t off = b * D + lane_off;
-        rk[ps] = *reinterpret_cast<const uint4*>(k_cache + off);
-        rv[ps] = *reinterpret_cast<const uint4*>(v_cache + off);
-      } else {
-        rk[ps] = make_uint4(0, 0, 0, 0);
-        rv[ps] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto fetch = [&](int step, const int64_t (&base)[PASSES][GPP]) {
-    if ((step + 1) * KS <= kend)
-      fetch_kv(Tag<false>{}, step, base);
-    else
-      fetch_kv(Tag<true>{}, step, base);
-  };
   auto fetch_bases = [&](int step, int64_t (&base)[PASSES][GPP]) {
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps)
 #pragma unroll
       for (int gi = 0; gi < GPP; ++gi) base[ps][gi] = group_base(step, ps, gi);
   };
-  auto stash = [&](int buf) {
+  // Two register sets stage tile loads: tile t goes through set t % 2, so the loads of a tile
+  // have two steps to arrive before they are stored to LDS. Every step loads and stores a tile
+  // (past the last tile, the last one again, into a buffer nobody reads), so the number of
+  // loads in flight is the same on every path.
+  uint4 rk[2][PASSES], rv[2][PASSES];
+  // Load tile `step` into register set X. Groups past kend read the tile's first group instead
+  // (always valid); those rows are zeroed when stored.
+  auto fetch = [&](auto set_tag, int step, const int64_t (&base)[PASSES][GPP]) {
+    constexpr int X = decltype(set_tag)::value;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
-      *reinterpret_cast<uint4*>(&sm.k[buf][lr + ps * RPP][lc * 8]) = rk[ps];
-      *reinterpret_cast<uint4*>(&sm.v[buf][lr + ps * RPP][lc * 8]) = rv[ps];
+      int64_t b = base[ps][0];
+#pragma unroll
+      for (int gi = 1; gi < GPP; ++gi)
+        if (lane_grp == gi) b = base[ps][gi];
+      if (b < 0) b = base[0][0];
+      const int64_t off = b * D + lane_off;
+      rk[X][ps] = *reinterpret_cast<const uint4*>(k_cache + off);
+      rv[X][ps] = *reinterpret_cast<const uint4*>(v_cache + off);
     }
   };
-
-  const int nsteps = (kend + KS - 1) / KS;
-  int64_t base1[PASSES][GPP], base2[PASSES][GPP];
-  fetch_bases(0, base1);
-  fetch(0, base1);
-  fetch_bases(nsteps > 1 ? 1 : 0, base1);
-  stash(0);
-  __syncthreads();
-
-  float m[2] = {kMaxFloor, kMaxFloor}, l[2] = {0.f, 0.f};
-  f32x4 o[2][NO];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int t = 0; t < NO; ++t) o[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // one tile: prefetch the next into registers, compute this one from LDS, stash the next
-  auto tile = [&](auto mask_tag, int st) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = st & 1;
-    const bool more = st + 1 < nsteps;
-    if (more) {
-      fetch_bases(st + 2 < nsteps ? st + 2 : st + 1, base2);
-      fetch(st + 1, base1);
-    }
-#pragma unroll
-    for (int c = 0; c < KS / 32; ++c) {
-      const int k0 = st * KS + 32 * c;
-      const int kr0 = 32 * c;  // first LDS row of this 32-key chunk
-      // S^T = K Q^T for both row tiles; the K fragment is shared
-      f32x4 acc[2][2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(&sm.k[buf][kr0 + 16 * j + n][g * (D / 4) + 8 * kk]);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[nt][j] = mfma16x16x32(kf, qf[nt][kk], acc[nt][j]);
-        }
-      }
-      bf16x8 pb[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        pb[nt] = softmax_step<NO, MASK>(acc[nt], k0, kend, last_key[nt], scale_log2, g, m[nt],
-                                        l[nt], o[nt]);
-      // V^T operands by transposing LDS reads. Lanes 4j + a of lane group g read key
-      // kr0 + 16h + 4g + j, dims (D/4)a + 4jt .. +3; lane 4a + b of the group receives element b
-      // of those four reads: dim (D/4)a + 4jt + b for keys 16h + 4g + j, j = 0..3, which is the
-      // key order of P^T's elements.
-      const __bf16* vb = &sm.v[buf][kr0 + 4 * g + (n >> 2)][(D / 4) * (n & 3)];
-#pragma unroll
-      for (int jt = 0; jt < NO; ++jt) {
-        const s16x4 lo = lds_read_tr16(vb + 4 * jt);
-        const s16x4 hi = lds_read_tr16(vb + 16 * SmemT::STRIDE + 4 * jt);
-        const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[nt][jt] = mfma16x16x32(vt, pb[nt], o[nt][jt]);
-      }
-    }
-    if (more) {
-      stash(buf ^ 1);
+  // Store register set X (tile `step`) to LDS buffer buf. In the last tile, rows at or past kend
+  // are stored as zero, so that a masked probability (0) never meets an unwritten V value.
+  auto stash = [&](auto set_tag, int buf, int step) {
+    constexpr int X = decltype(set_tag)::value;
+    if ((step + 1) * KS > kend) {  // wave-uniform
 #pragma unroll
       for (int ps = 0; ps < PASSES; ++ps)
-#pragma unroll
-        for (int gi = 0; gi < GPP; ++gi) base1[ps][gi] = base2[ps][gi];
+        if (step * KS + ps * RPP + lr >= kend) {
+          rk[X][ps] = make_uint4(0, 0, 0, 0);
+          rv[X][ps] = make_uint4(0, 0, 0, 0);
+        }
     }
-    __syncthreads();
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      *reinterpret_cast<uint4*>(&sm.k[buf][lr + ps * RPP][lc * 8]) = rk[X][ps];
+      *reinterpret_cast<uint4*>(&sm.v[buf][lr + ps * RPP][lc * 8]) = rv[X][ps];
+    }
   };
 
-  // Tiles whose keys are all visible to every row of this wave run without the mask; the rest
-  // (the causal diagonal and the range end) with it. The split point differs between waves,
-  // but every wave runs all nsteps tiles, so the barriers pair up in order.
+  // S^T = K Q^T of LDS tile `buf` for both row tiles (the K fragment is shared):
+  // acc[nt][j][i] is the score of key 16j + 4g + i of the tile for row n of row tile nt.
+  auto qk = [&](int buf, f32x4 (&acc)[NT][2]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * j + n][g * (D / 4) + 8 * kk]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][j] = mfma16x16x32(kf, qf[nt][kk], acc[nt][j]);
+      }
+  };
+  // O^T += V^T P^T of LDS tile `buf`. The V^T operands come from transposing LDS reads: lanes
+  // 4j + a of lane group g read key 16h + 4g + j, dims (D/4)a + 4jt .. +3; lane 4a + b of the
+  // group receives element b of those four reads, i.e. dim (D/4)a + 4jt + b for keys
+  // 16h + 4g + j, j = 0..3, which is the key order of P^T's elements.
+  f32x4 o[NT][NO];
+  auto pv = [&](int buf, const bf16x8 (&pb)[NT]) {
+    const __bf16* vb = &sm.v[buf][4 * g + (n >> 2)][(D / 4) * (n & 3)];
+#pragma unroll
+    for (int jt = 0; jt < NO; ++jt) {
+      const s16x4 lo = lds_read_tr16(vb + 4 * jt);
+      const s16x4 hi = lds_read_tr16(vb + 16 * SmemT::STRIDE + 4 * jt);
+      const bf16x8 vt =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt][jt] = mfma16x16x32(vt, pb[nt], o[nt][jt]);
+    }
+  };
+
+  float m[NT], l[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = kMaxFloor;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NO; ++t) o[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Tiles whose keys are all visible to every row of this wave take no mask; the rest (the
+  // causal diagonal and the range end) do. The split differs between waves, but every wave runs
+  // the same steps, so the barriers pair up in order.
+  const int nsteps = (kend + KS - 1) / KS;  // >= 1
   const int n_open = min(nsteps, min(kend, wave_first_last_key + 1) / KS);
+
+  // prologue: tiles 0 and 1 into LDS, tile 2 into register set 0, bases of tile 3 (tile
+  // indices past the last tile stand for the last tile)
+  const int last_tile = nsteps - 1;
+  int64_t base_a[PASSES][GPP], base_b[PASSES][GPP];
+  fetch_bases(0, base_a);
+  fetch(Int<0>{}, 0, base_a);
+  fetch_bases(min(1, last_tile), base_b);
+  fetch(Int<1>{}, min(1, last_tile), base_b);
+  stash(Int<0>{}, 0, 0);
+  stash(Int<1>{}, 1, min(1, last_tile));
+  fetch_bases(min(2, last_tile), base_a);
+  fetch(Int<0>{}, min(2, last_tile), base_a);
+  fetch_bases(min(3, last_tile), base_a);
+  __syncthreads();
+
+  f32x4 acc[NT][2];
+  qk(0, acc);
+  {
+    float mc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      mc[nt] = n_open > 0 ? chunk_max<false>(acc[nt], 0, kend, last_key[nt], scale_log2, g)
+                          : chunk_max<true>(acc[nt], 0, kend, last_key[nt], scale_log2, g);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) rescale_lazy<NO>(mc[nt], m[nt], l[nt], o[nt]);
+  }
+
+  // step st < nsteps - 1: tile st is in LDS buffer cur with its scores (masked) in acc and its
+  // reference max settled; tile st + 1 is in buffer nxt; buffer fil receives tile st + 2 from
+  // register set P = st % 2, and tile st + 3 is loaded into the other set.
+  int cur = 0, nxt = 1, fil = 2;
+  auto step = [&](auto mask_tag, auto parity_tag, int st) {
+    constexpr bool MASK_NEXT = decltype(mask_tag)::value;
+    constexpr int P = decltype(parity_tag)::value;
+    fetch(Int<1 - P>{}, min(st + 3, last_tile), base_a);
+    fetch_bases(min(st + 4, last_tile), base_b);
+    f32x4 acc_n[NT][2];
+    qk(nxt, acc_n);
+    bf16x8 pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) pb[nt] = chunk_exp(acc[nt], scale_log2, m[nt], l[nt]);
+    pv(cur, pb);
+    float mc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      mc[nt] = chunk_max<MASK_NEXT>(acc_n[nt], (st + 1) * KS, kend, last_key[nt], scale_log2, g);
+    stash(Int<P>{}, fil, min(st + 2, last_tile));
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+      for (int gi = 0; gi < GPP; ++gi) base_a[ps][gi] = base_b[ps][gi];
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      rescale_lazy<NO>(mc[nt], m[nt], l[nt], o[nt]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[nt][j] = acc_n[nt][j];
+    }
+    const int t = cur;
+    cur = nxt;
+    nxt = fil;
+    fil = t;
+  };
+  // steps [st, end) with the register-set parity known at compile time
   int st = 0;
-  for (; st < n_open; ++st) tile(Tag<false>{}, st);
-  for (; st < nsteps; ++st) tile(Tag<true>{}, st);
+  auto run = [&](auto mask_tag, int end) {
+    if ((st & 1) && st < end) step(mask_tag, Int<1>{}, st++);
+    for (; st + 1 < end; st += 2) {
+      step(mask_tag, Int<0>{}, st);
+      step(mask_tag, Int<1>{}, st + 1);
+    }
+    if (st < end) step(mask_tag, Int<0>{}, st++);
+  };
+  run(Tag<false>{}, n_open - 1);
+  run(Tag<true>{}, nsteps - 1);
+  {
+    bf16x8 pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) pb[nt] = chunk_exp(acc[nt], scale_log2, m[nt], l[nt]);
+    pv(cur, pb);
+  }
 
   // normalise and store: lane (n, g) holds row n, dims (D/4)g + 4jt + i (D/4 contiguous dims)
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int R = wave * 32 + nt * 16 + n;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int R = wave * (16 * NT) + nt * 16 + n;
     const int qi = tok0 + R / G, hh = R - (R / G) * G;
     if (qi >= tok_end) continue;
     const float inv = 1.f / l[nt];
@@ -972,11 +1065,11 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
   if (p.pre_cap > 0) {
     const unsigned grid = (unsigned)(p.pre_cap * num_kv_heads);
     if (head_dim == 128)
-      prefill_kernel<128, kPrefillKeys><<<grid, kPrefillWaves * 64, 0, st>>>(
+      prefill_kernel<128><<<grid, kPrefillWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
           num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
     else
-      prefill_kernel<64, kPrefillKeys><<<grid, kPrefillWaves * 64, 0, st>>>(
+      prefill_kernel<64><<<grid, kPrefillWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
           num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
   }
