@@ -124,11 +124,13 @@ struct KVFrag {
 
 // Online softmax of one 16-row tile over one 32-key chunk, in three parts.
 //   acc[j][i]: raw score (Q.K) for key k0 + 16j + 4g + i of this lane's row; c = scale * log2(e).
-// m is the row's reference max in scaled log2 units, l its running sum, o its output rows.
+// m is the row's reference max in scaled log2 units (the same in the row's four lanes), l this
+// lane's part of the row's running sum (the row sum is the sum over the four lanes, taken once
+// at the end: every rescale multiplies all four parts by the same factor), o its output rows.
 
-// Row max of the chunk (scaled). With MASK, keys >= kend or > last_key are first set to -inf in
-// acc; without it the caller guarantees every key of the chunk is visible to every row that is
-// written out.
+// This lane's max over its 8 keys of the chunk (scaled). With MASK, keys >= kend or > last_key are
+// first set to -inf in acc; without it the caller guarantees every key of the chunk is visible to
+// every row that is written out.
 template <bool MASK>
 __device__ inline float chunk_max(f32x4 (&acc)[2], int k0, int kend, int last_key, float c, int g) {
   float mx = -INFINITY;
@@ -143,14 +145,15 @@ __device__ inline float chunk_max(f32x4 (&acc)[2], int k0, int kend, int last_ke
       mx = fmaxf(mx, acc[j][i]);
     }
   }
-  return group_max(mx) * c;  // c > 0; -inf stays -inf
+  return mx * c;  // c > 0; -inf stays -inf
 }
 
-// Move the reference max when the chunk's max exceeds it by more than kRescaleSlack.
+// Move the reference max when some lane's chunk max exceeds it by more than kRescaleSlack; only
+// then is the row max over the four lanes taken.
 template <int NO>
-__device__ inline void rescale_lazy(float m_chunk, float& m, float& l, f32x4 (&o)[NO]) {
-  if (__builtin_amdgcn_ballot_w64(m_chunk > m + kRescaleSlack) != 0) {  // wave-uniform
-    const float m_new = fmaxf(m, m_chunk);
+__device__ inline void rescale_lazy(float m_lane, float& m, float& l, f32x4 (&o)[NO]) {
+  if (__builtin_amdgcn_ballot_w64(m_lane > m + kRescaleSlack) != 0) {  // wave-uniform
+    const float m_new = fmaxf(m, group_max(m_lane));
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);
     l *= alpha;
 #pragma unroll
@@ -159,8 +162,8 @@ __device__ inline void rescale_lazy(float m_chunk, float& m, float& l, f32x4 (&o
   }
 }
 
-// Probabilities of the chunk against the reference max, added to l; returns P^T (bf16) in the
-// B-operand layout. Masked scores are -inf and give 0.
+// Probabilities of the chunk against the reference max, added to this lane's part of the sum;
+// returns P^T (bf16) in the B-operand layout. Masked scores are -inf and give 0.
 __device__ inline bf16x8 chunk_exp(const f32x4 (&acc)[2], float c, float m, float& l) {
   float rs = 0.f;
   bf16x8 pb;
@@ -170,7 +173,7 @@ __device__ inline bf16x8 chunk_exp(const f32x4 (&acc)[2], float c, float m, floa
     rs += p;
     pb[e] = (__bf16)p;
   }
-  l += group_sum(rs);
+  l += rs;
   return pb;
 }
 
@@ -476,6 +479,7 @@ void decode_kernel(
       k0 = k2;
     }
 
+    l = group_sum(l);  // the row's sum (all lanes take part)
     // lane (n, g) holds row n, dims (4g + i) * NO + jt
     if (n < rows) {
       const int qi = n / G, hh = n - (n / G) * G;
@@ -799,6 +803,8 @@ void prefill_kernel(
     pv(cur, pb);
   }
 
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) l[nt] = group_sum(l[nt]);  // row sums (all lanes take part)
   // normalise and store: lane (n, g) holds row n, dims (D/4)g + 4jt + i (D/4 contiguous dims)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
