@@ -4,15 +4,27 @@
 A step = cb_slot_mapping + cb_cache_write + cb_paged_attention (planning prepass, decode/split-KV
 and prefill kernels, log-sum-exp merge) over one synthetic packed batch, inputs resident in HBM.
 Default workload: the Llama-3-8B-shaped decode batch (32 q-heads, 8 KV heads, head_dim 128,
-block 16, 256 sequences with KV length uniform in [128, 4096], physical blocks shuffled).
+block 16, 256 sequences with KV length uniform in [128, 4096], physical blocks shuffled); the
+mixed continuous batch of the same model shape (64 decode tokens + 1984 prefill-chunk tokens) is
+measured after it and reported under "mixed_batch".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
 
 Prints ONE JSON line on stdout; progress goes to stderr.
-value = algorithmic bytes of the step / step time (GB/s). The roofline object covers the
-attention entry point's kernels, timed with HIP events on the stream they run on.
+value = algorithmic bytes of the step / step time (GB/s) for the decode workloads, tokens/s for
+the mixed ones. The roofline object covers the dominant kernel (the decode kernel, HBM-bound, or
+the prefill-chunk kernel, MFMA-bound), timed with HIP events that the library records around
+that kernel on the stream it runs on (cb_time_next_kernel).
+
+Measurement helpers (not part of the timed run):
+    python bench.py --copy-calibration            # plain device copy of known size, for counters
+    python bench.py --traffic-summary FETCH WRITE CFETCH CWRITE [--config N]
+        reads rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench (FETCH, WRITE)
+        and of the copy calibration (CFETCH, CWRITE) and writes the per-launch HBM traffic of the
+        dominant kernel to profiles/.
 """
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -25,6 +37,8 @@ sys.path.insert(0, ROOT)
 METRIC = "ragged paged-attn decode KV GB/s (% HBM peak) + mixed-batch tokens/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+DECODE_CONFIGS = (1, 2, 4)
+COPY_BYTES = 2 << 30  # copy calibration: bytes read and bytes written
 
 
 def log(*a):
@@ -49,10 +63,13 @@ def work_of(b):
     write = 2 * (2 * T * Hkv * D * 2) + 4 * T      # K/V rows read + written, slots read
     slots = 4 * T + 4 * T + 4 * (2 * S + 1)        # table entries read, slots written
     pairs = q * (L - q) + q * (q + 1) // 2         # unmasked (query, key) pairs
+    # decode kernel alone: the decode rows' K/V, q and output rows, block-table entries
+    dec_bytes = int((L[decode] * kv_tok).sum() + 2 * q[decode].sum() * Hq * D * 2
+                    + 4 * blocks[decode].sum())
     return {
         "T": T, "S": S,
         "kv_bytes": kv_bytes,
-        "decode_kv_bytes": int((L[decode] * kv_tok).sum()),
+        "decode_kernel_bytes": dec_bytes,
         "attn_bytes": int(attn),
         "step_bytes": int(attn + write + slots),
         "attn_flops": int((4 * D * Hq * pairs).sum()),
@@ -60,17 +77,25 @@ def work_of(b):
     }
 
 
+def traffic_record_path(workload):
+    return os.path.join(ROOT, "profiles", f"paged_attention_{workload}_hbm_traffic.json")
+
+
+def attention_source_sha256():
+    src = open(os.path.join(ROOT, "ragged_paged_kv_amd", "csrc", "attention.hip"), "rb").read()
+    return hashlib.sha256(src).hexdigest()
+
+
 def traffic_from_profile(workload):
-    """HBM bytes per attention call from committed rocprofv3 counter runs, if they were taken on
-    the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"paged_attention_{workload}_hbm_traffic.json")
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = traffic_record_path(workload)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "ragged_paged_kv_amd", "csrc", "attention.hip"), "rb").read()
-    if rec.get("attention_hip_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("attention_hip_sha256") != attention_source_sha256():
         return None
-    return rec.get("bytes_per_call")
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(batch, budget_s=20.0):
@@ -121,40 +146,24 @@ def cpu_baseline(batch, budget_s=20.0):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--split", type=int, default=0, help="KV partition tokens (0 = library choice)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        log(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-            "this hot path has no multi-GPU mode: run with --gpus 1.")
-        sys.exit(2)
-
+def measure(args, config, steps, warmup):
+    """Generate workload `config`, run warmup + timed steps; returns the batch, its work and the
+    timings (step wall time, dominant kernel times from the library's events)."""
     import numpy as np
     import torch
 
     import ragged_paged_kv_amd as cb
     import synth
 
-    if not torch.cuda.is_available():
-        log("bench.py needs a GPU")
-        sys.exit(1)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     t0 = time.perf_counter()
-    b = synth.make_config(args.config)
+    b = synth.make_config(config)
     log(f"[bench] generated {b.name} in {time.perf_counter() - t0:.1f} s: S={b.num_seqs} "
         f"T={b.num_tokens} sumL={int(b.kv_lens.sum())} blocks={b.num_blocks}")
     cb.cb_validate_batch(b.cu_seqlens_q, b.kv_lens, b.block_tables, None, b.block_size,
                          b.num_blocks, b.max_q_len, b.max_kv_len)
     w = work_of(b)
+    kernel = cb.CB_KERNEL_DECODE if config in DECODE_CONFIGS else cb.CB_KERNEL_PREFILL
 
     def up_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -177,40 +186,169 @@ def main():
         cb.cb_cache_write(k, v, slots, kc, vc, stream=stream)
         if ev is not None:
             ev[0].record(stream)
+            cb.cb_time_next_kernel(kernel, ev[2], ev[3], stream=stream)
         cb.cb_paged_attention(q, cu, kvl, bt, kc, vc, out, b.scale, b.max_q_len, b.max_kv_len, ws,
                               kv_split_tokens=args.split, stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
+    for ev in events:  # create the events before the timed region
+        for e in ev:
+            e.record(stream)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    ms_per_step = elapsed / args.steps * 1e3
-    attn_ms = [e0.elapsed_time(e1) for e0, e1 in events]
-    attn_avg_ms = sum(attn_ms) / len(attn_ms)
-    attn_med_ms = sorted(attn_ms)[len(attn_ms) // 2]
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; attention avg {attn_avg_ms:.4f} ms "
-        f"(median {attn_med_ms:.4f}, min {min(attn_ms):.4f}, max {max(attn_ms):.4f})")
+    attn_ms = [e[0].elapsed_time(e[1]) for e in events]
+    kern_ms = [e[2].elapsed_time(e[3]) for e in events]
+    r = {
+        "batch": b, "work": w, "split": split, "kernel": kernel,
+        "ms_per_step": elapsed / steps * 1e3,
+        "attn_ms": sum(attn_ms) / len(attn_ms),
+        "kernel_ms": sum(kern_ms) / len(kern_ms),
+        "kernel_ms_median": sorted(kern_ms)[len(kern_ms) // 2],
+    }
+    log(f"[bench] {b.name}: {steps} steps, {r['ms_per_step']:.4f} ms/step; attention "
+        f"{r['attn_ms']:.4f} ms; {'decode' if kernel == cb.CB_KERNEL_DECODE else 'prefill'} kernel "
+        f"avg {r['kernel_ms']:.4f} ms (median {r['kernel_ms_median']:.4f}, min {min(kern_ms):.4f}, "
+        f"max {max(kern_ms):.4f})")
+    return r
 
-    step_s = ms_per_step / 1e3
-    if args.config in (2, 4):
-        value = w["step_bytes"] / step_s / 1e9
-        unit = "GB/s"
+
+def roofline_of(r):
+    import ragged_paged_kv_amd as cb
+    w, b = r["work"], r["batch"]
+    sec = r["kernel_ms"] / 1e3
+    if r["kernel"] == cb.CB_KERNEL_DECODE:
+        achieved = w["decode_kernel_bytes"] / sec / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(b.name), "kernel": "decode_kernel",
+                "kernel_ms": round(r["kernel_ms"], 5), "bytes_per_launch": w["decode_kernel_bytes"]}
+    achieved = w["prefill_flops"] / sec / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_profile(b.name), "kernel": "prefill_kernel",
+            "kernel_ms": round(r["kernel_ms"], 5), "flops_per_launch": w["prefill_flops"]}
+
+
+def copy_calibration():
+    """A plain elementwise copy kernel (negation) over COPY_BYTES, five times: it reads and writes
+    COPY_BYTES each, so its counters give the scale between FETCH_SIZE / WRITE_SIZE and bytes
+    actually moved. (A same-dtype copy_ would be a DMA transfer, invisible to the counters.)"""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {COPY_BYTES} bytes 5 times")
+
+
+def _pmc_means(d, counter, name_part):
+    import csv
+    import collections
+    vals = collections.defaultdict(list)
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] == counter and name_part in row["Kernel_Name"]:
+                vals[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for a kernel named like {name_part!r} under {d}")
+    name, v = max(vals.items(), key=lambda kv: sum(kv[1]) / len(kv[1]))
+    return name, sum(v) / len(v), len(v)
+
+
+def traffic_summary(args):
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_summary
+    import synth
+    b = synth.make_config(args.config)
+    kname = "decode_kernel" if args.config in DECODE_CONFIGS else "prefill_kernel"
+    kn, fetch_kib, nf = _pmc_means(fetch_dir, "FETCH_SIZE", kname)
+    _, write_kib, nw = _pmc_means(write_dir, "WRITE_SIZE", kname)
+    cn, cfetch_kib, _ = _pmc_means(cfetch_dir, "FETCH_SIZE", "")
+    _, cwrite_kib, _ = _pmc_means(cwrite_dir, "WRITE_SIZE", cn[:40])
+    f_fetch = COPY_BYTES / 1024 / cfetch_kib
+    f_write = COPY_BYTES / 1024 / cwrite_kib
+    fetch_b = fetch_kib * 1024 * f_fetch
+    write_b = write_kib * 1024 * f_write
+    w = work_of(b)
+    alg = w["decode_kernel_bytes"] if kname == "decode_kernel" else None
+    rec = {
+        "workload": b.name, "kernel": kn, "attention_hip_sha256": attention_source_sha256(),
+        "fetch_kib_per_launch": round(fetch_kib, 1), "write_kib_per_launch": round(write_kib, 1),
+        "launches": [nf, nw],
+        "copy_kernel": cn, "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib": round(cfetch_kib, 1), "copy_write_kib": round(cwrite_kib, 1),
+        "fetch_scale": round(f_fetch, 5), "write_scale": round(f_write, 5),
+        "bytes_per_launch": int(fetch_b + write_b),
+        "algorithmic_bytes_per_launch": alg,
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o p --output-format csv -- python3 bench.py "
+            f"--config {args.config} --steps 5 --warmup 2 --no-cpu-baseline --no-mixed",
+            f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o p --output-format csv -- python3 bench.py "
+            f"--config {args.config} --steps 5 --warmup 2 --no-cpu-baseline --no-mixed",
+            f"rocprofv3 --pmc FETCH_SIZE -d {cfetch_dir} -o p --output-format csv -- python3 bench.py --copy-calibration",
+            f"rocprofv3 --pmc WRITE_SIZE -d {cwrite_dir} -o p --output-format csv -- python3 bench.py --copy-calibration",
+            "python3 bench.py --traffic-summary " + " ".join(args.traffic_summary) + f" --config {args.config}",
+        ],
+    }
+    path = traffic_record_path(b.name)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--split", type=int, default=0, help="KV partition tokens (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-batch measurement")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=4, metavar="DIR")
+    args = ap.parse_args()
+
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+            "this hot path has no multi-GPU mode: run with --gpus 1.")
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    r = measure(args, args.config, args.steps, args.warmup)
+    b, w = r["batch"], r["work"]
+    step_s = r["ms_per_step"] / 1e3
+    if args.config in DECODE_CONFIGS:
+        value, unit = w["step_bytes"] / step_s / 1e9, "GB/s"
     else:
-        value = w["T"] / step_s
-        unit = "tokens/s"
-    achieved = w["attn_bytes"] / (attn_avg_ms / 1e3) / 1e9
-    traffic = traffic_from_profile(b.name)
-    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+        value, unit = w["T"] / step_s, "tokens/s"
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -218,7 +356,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -228,19 +366,28 @@ def main():
             "workload": b.name,
             "num_seqs": b.num_seqs, "num_tokens": b.num_tokens, "q_heads": b.num_q_heads,
             "kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
-            "kv_tokens": int(b.kv_lens.sum()), "kv_split_tokens": int(split), "seed": b.seed,
+            "kv_tokens": int(b.kv_lens.sum()), "kv_split_tokens": int(r["split"]), "seed": b.seed,
             "step": "slot_mapping + cache_write + paged_attention",
         },
         "hbm_frac": round(w["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w["T"] / step_s, 1),
-        "attention_ms": round(attn_avg_ms, 5),
+        "attention_ms": round(r["attn_ms"], 5),
         "step_bytes": w["step_bytes"],
         "attention_bytes": w["attn_bytes"],
-        "roofline": roof,
+        "roofline": roofline_of(r),
         "cpu_baseline": None,
     }
     if w["prefill_flops"]:
         res["prefill_flops"] = w["prefill_flops"]
+    if args.config in DECODE_CONFIGS and not args.no_mixed:
+        m = measure(args, 3, max(5, args.steps // 2), max(2, args.warmup // 2))
+        mb = m["batch"]
+        res["mixed_batch"] = {
+            "workload": mb.name, "num_tokens": mb.num_tokens, "num_seqs": mb.num_seqs,
+            "tokens_per_s": round(m["work"]["T"] / (m["ms_per_step"] / 1e3), 1),
+            "ms_per_step": round(m["ms_per_step"], 5),
+            "roofline": roofline_of(m),
+        }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores ...")
         res["cpu_baseline"] = cpu_baseline(b)

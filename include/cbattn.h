@@ -171,6 +171,23 @@ int cb_validate_batch(const int32_t* cu_seqlens_q, const int32_t* kv_lens,
                       int32_t num_tokens, int32_t max_blocks_per_seq, int32_t block_size,
                       int64_t num_blocks, int32_t max_q_len, int32_t max_kv_len);
 
+/*
+ * cb_time_next_kernel — measurement hook: time one kernel of the next attention call.
+ * Not an operation of the method: it serves throughput measurement against a kernel's roofline.
+ * The next cb_paged_attention call made by this thread records `start_event` on its stream right
+ * before it launches kernel `which` and `stop_event` right after (one-shot: that call clears the
+ * request, whether it launches the kernel or not).
+ *   which: CB_KERNEL_DECODE (the decode / split-KV kernel) or CB_KERNEL_PREFILL (the
+ *          prefill-chunk kernel, launched only when the batch holds prefill rows); 0 clears a
+ *          pending request.
+ *   start_event, stop_event: hipEvent_t handles created by the caller (with timing enabled),
+ *          owned by the caller; they must outlive the call they are recorded in.
+ * Errors: CB_ERR_INVALID_ARG for an unknown `which` or a NULL event with which != 0. A failing
+ * hipEventRecord inside the attention call makes that call return CB_ERR_HIP.
+ */
+enum { CB_KERNEL_DECODE = 1, CB_KERNEL_PREFILL = 2 };
+int cb_time_next_kernel(int32_t which, void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,14 +24,14 @@ from ._build import LIB_PATH
 __all__ = [
     "CBError", "LIB_PATH", "lib", "cb_status_string", "cb_last_error", "cb_slot_mapping",
     "cb_cache_write", "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens",
-    "cb_paged_attention", "cb_split_kv_reduce", "cb_validate_batch", "alloc_workspace",
-    "EXPORTED_SYMBOLS",
+    "cb_paged_attention", "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
+    "alloc_workspace", "EXPORTED_SYMBOLS", "CB_KERNEL_DECODE", "CB_KERNEL_PREFILL",
 ]
 
 EXPORTED_SYMBOLS = (
     "cb_status_string", "cb_last_error", "cb_slot_mapping", "cb_cache_write",
     "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens", "cb_paged_attention",
-    "cb_split_kv_reduce", "cb_validate_batch",
+    "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
 )
 
 
@@ -68,7 +68,11 @@ _sig = {
                                           _i32, _i32, _i32, _i64, _i32, _i32, _i32, _p, _sz, _p]),
     "cb_split_kv_reduce": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "cb_validate_batch": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _i32]),
+    "cb_time_next_kernel": (ctypes.c_int, [_i32, _p, _p]),
 }
+
+CB_KERNEL_DECODE = 1
+CB_KERNEL_PREFILL = 2
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(lib, _name)
     _fn.restype = _res
@@ -204,6 +208,26 @@ def cb_split_kv_reduce(o_part, lse_part, num_splits, out, stream=None):
                                   _dev(out, "out", torch.bfloat16, 3), T, Hq, D, ms,
                                   _stream(stream)),
            "cb_split_kv_reduce")
+
+
+def _event_handle(ev, stream):
+    """Raw hipEvent_t of a torch.cuda.Event (torch creates the event on its first record)."""
+    if ev.cuda_event == 0:
+        ev.record(stream)
+    return ctypes.c_void_p(ev.cuda_event)
+
+
+def cb_time_next_kernel(which: int, start=None, stop=None, stream=None):
+    """Have the next cb_paged_attention call of this thread record torch.cuda.Events `start` and
+    `stop` (enable_timing=True) around kernel `which` (CB_KERNEL_DECODE or CB_KERNEL_PREFILL);
+    which=0 clears a pending request."""
+    if which == 0:
+        _check(lib.cb_time_next_kernel(0, None, None), "cb_time_next_kernel")
+        return
+    torch = _torch()
+    st = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib.cb_time_next_kernel(int(which), _event_handle(start, st), _event_handle(stop, st)),
+           "cb_time_next_kernel")
 
 
 def _host_i32(a, name):

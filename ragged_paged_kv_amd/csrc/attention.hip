@@ -1013,6 +1013,30 @@ extern "C" size_t cb_paged_attention_workspace_size(int32_t num_seqs, int32_t nu
       .total;
 }
 
+namespace {
+// pending request of cb_time_next_kernel (per thread, one-shot)
+struct KernelTimer {
+  int which = 0;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local KernelTimer g_timer;
+
+bool record_if(const KernelTimer& tm, int which, bool start, hipStream_t st) {
+  if (tm.which != which) return true;
+  return hipEventRecord(start ? tm.start : tm.stop, st) == hipSuccess;
+}
+}  // namespace
+
+extern "C" int cb_time_next_kernel(int32_t which, void* start_event, void* stop_event) {
+  using cb::fail;
+  if (which != 0 && which != CB_KERNEL_DECODE && which != CB_KERNEL_PREFILL)
+    return fail(CB_ERR_INVALID_ARG, "cb_time_next_kernel: unknown kernel id " + std::to_string(which));
+  if (which != 0 && (!start_event || !stop_event))
+    return fail(CB_ERR_INVALID_ARG, "cb_time_next_kernel: NULL event");
+  g_timer = KernelTimer{which, static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  return cb::ok();
+}
+
 extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlens_q,
                                   const int32_t* kv_lens, const int32_t* block_tables,
                                   const void* k_cache, const void* v_cache, void* out, float scale,
@@ -1023,6 +1047,8 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
                                   void* workspace, size_t workspace_bytes, void* stream) {
   using cb::fail;
   const int E = CB_ERR_INVALID_ARG;
+  const KernelTimer tm = g_timer;  // one-shot: consumed by this call
+  g_timer = KernelTimer{};
   if (block_size < 4) return fail(E, "block_size must be at least 4, got " + std::to_string(block_size));
   if (num_seqs < 0 || num_tokens < 0) return fail(E, "negative num_seqs or num_tokens");
   if (num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1) return fail(E, "head counts and head_dim must be positive");
@@ -1070,6 +1096,7 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
                                   p.dec_cap, pre, p.pre_cap, counts);
   if (p.pre_cap > 0) {
     const unsigned grid = (unsigned)(p.pre_cap * num_kv_heads);
+    if (!record_if(tm, CB_KERNEL_PREFILL, true, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
     if (head_dim == 128)
       prefill_kernel<128><<<grid, kPrefillWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
@@ -1078,6 +1105,7 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
       prefill_kernel<64><<<grid, kPrefillWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
           num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
+    if (!record_if(tm, CB_KERNEL_PREFILL, false, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
   }
   {
     // persistent: two 4-wave workgroups per compute unit (2 waves per SIMD), never more
@@ -1088,6 +1116,7 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
     const unsigned grid = (unsigned)std::max<int64_t>(
         1, std::min<int64_t>((items + kDecodeWaves - 1) / kDecodeWaves, 2 * (int64_t)cus));
     int32_t* queue = counts + 2;
+    if (!record_if(tm, CB_KERNEL_DECODE, true, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
     if (head_dim == 128)
       decode_kernel<128><<<grid, kDecodeWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
@@ -1098,6 +1127,7 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
           queue, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits,
           p.qmaxd, scale_log2);
+    if (!record_if(tm, CB_KERNEL_DECODE, false, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
   }
   if (p.max_splits > 1) {
     const int64_t nrows = (int64_t)num_seqs * p.qmaxd;

@@ -106,6 +106,15 @@ def test_slot_mapping_and_reduce_host_checks():
     assert cb.lib.cb_split_kv_reduce(FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 0, N) == -1
 
 
+def test_kernel_timing_hook_host_checks():
+    assert cb.lib.cb_time_next_kernel(3, FAKE, FAKE) == -1       # unknown kernel
+    assert cb.lib.cb_time_next_kernel(1, N, FAKE) == -1          # NULL event
+    assert cb.lib.cb_time_next_kernel(2, FAKE, N) == -1
+    assert cb.lib.cb_time_next_kernel(0, N, N) == 0              # clear
+    assert cb.lib.cb_time_next_kernel(1, FAKE, FAKE) == 0        # armed ...
+    assert cb.lib.cb_time_next_kernel(0, N, N) == 0              # ... and cleared, nothing recorded
+
+
 def test_workspace_size_and_split_choice():
     # decode-only batch: only partials and the work list
     p = cb.cb_paged_attention_split_tokens(256, 8, 4096)

@@ -215,3 +215,29 @@ def test_workspace_too_small_is_rejected(torch_cuda):
     with pytest.raises(cb.CBError) as e:
         st.attention()
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("which", [1, 2])
+def test_kernel_timing_hook(torch_cuda, which):
+    """The measurement hook records its events around the named kernel and leaves the results
+    unchanged; it is one-shot."""
+    import ragged_paged_kv_amd as cb
+    torch = torch_cuda
+    b = synth.make_config(1)  # decode rows and a prefill chunk: both kernels run
+    ref = Step(b).run().out_u16()
+    st = Step(b)
+    st.slot_mapping()
+    st.cache_write()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cb.cb_time_next_kernel(which, e0, e1)
+    st.attention()
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) > 0.0
+    assert np.array_equal(st.out_u16(), ref)
+    # consumed: a second call records nothing new
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(); f1.record()
+    torch.cuda.synchronize()
+    st.attention()
+    torch.cuda.synchronize()
+    assert np.array_equal(st.out_u16(), ref)
