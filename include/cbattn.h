@@ -35,7 +35,9 @@
  *    kv_lens[s] <= MB * bs; table entries for logical blocks < ceil(kv_lens[s] / bs) lie in
  *    [0, NB) (entries past that are never read and may hold -1); slots are -1 or in
  *    [0, NB * bs) with no slot repeated; kv_lens and q lengths do not exceed max_kv_len and
- *    max_q_len.
+ *    max_q_len. In cb_paged_attention, a sequence whose q or kv length breaks these bounds
+ *    (q = 0, kv_len < q, kv_len > max_kv_len or > MB * bs, a decode-type q > max_q_len) gets no
+ *    work: nothing is read for it and its output rows are left unwritten.
  */
 #ifndef CBATTN_H
 #define CBATTN_H

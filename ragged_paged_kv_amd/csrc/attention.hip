@@ -35,7 +35,10 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "cb_internal.h"
 
@@ -200,9 +203,9 @@ __device__ inline bf16x8 vt_operand(const uint32_t (&v)[8][D / 32], int jt) {
 // ---------------------------------------------------------------------------------------------
 // Planning prepass: per-sequence work items, compacted with a block-wide scan.
 
-// A sequence breaking the contract (q = 0, kv_len < q, more KV than its table row addresses,
-// a decode-type q beyond max_q_len, more partitions than max_kv_len allows) gets no work item,
-// so nothing is read or written out of bounds; its output rows are then left unwritten.
+// A sequence breaking the contract (q = 0, kv_len < q, kv_len beyond max_kv_len, more KV than its
+// table row addresses, a decode-type q beyond max_q_len) gets no work item, so nothing is read
+// or written out of bounds; its output rows are then left unwritten.
 //
 // Decode items are ordered longest first, so that the work queue ends on short items: every
 // full P-token partition first (in sequence order), then each sequence's last, partial
@@ -212,14 +215,15 @@ constexpr int kTailBuckets = 32;
 
 __device__ inline int seq_items(const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_lens,
                                 int s, int num_seqs, int G, int P, int qmaxd, int max_splits,
-                                int bq, int bs, int max_blocks, int& nfull, int& rem, int& np) {
+                                int bq, int bs, int max_blocks, int max_kv, int& nfull, int& rem,
+                                int& np) {
   nfull = 0;
   rem = 0;
   np = 0;
   if (s >= num_seqs) return 0;
   const int q = cu[s + 1] - cu[s];
   const int L = kv_lens[s];
-  if (q <= 0 || L < q || (L + bs - 1) / bs > max_blocks) return 0;
+  if (q <= 0 || L < q || L > max_kv || (L + bs - 1) / bs > max_blocks) return 0;
   if (q * G <= 16) {
     if (q > qmaxd || (L + P - 1) / P > max_splits) return 0;
     nfull = L / P;
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int32_t num_seqs, int32_t G, int32_t P,
                                                     int32_t qmaxd, int32_t max_splits,
                                                     int32_t bq, int32_t bs, int32_t max_blocks,
-                                                    Work* __restrict__ dec,
+                                                    int32_t max_kv, Work* __restrict__ dec,
                                                     int64_t dec_cap, Work* __restrict__ pre,
                                                     int64_t pre_cap, int32_t* __restrict__ counts) {
   __shared__ int32_t sd[1024];
@@ -251,7 +255,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
     const int s = s0 + tid;
     int nfull, rem, np;
-    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, nfull, rem, np);
+    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull,
+              rem, np);
     if (rem > 0) atomicAdd(&tail_count[(P - rem) * kTailBuckets / P], 1);
     sd[tid] = nfull;
     sp[tid] = np;
@@ -293,7 +298,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
     const int s = s0 + tid;
     int nfull, rem, np;
-    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, nfull, rem, np);
+    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull,
+              rem, np);
     if (rem > 0) {
       const int64_t pos = atomicAdd(&tail_next[(P - rem) * kTailBuckets / P], 1);
       if (pos < dec_cap) dec[pos] = Work{s, nfull};
@@ -619,13 +625,31 @@ void prefill_kernel(
   const int lane_grp = lr >> 4;                                       // group within the pass
   // cache row (units of D elements) of the first key of 16-key group grp of pass ps of a tile;
   // groups at or past kend are not read (-1)
+  // Block ids come from a window of the sequence's block-table row held in one register: lane i
+  // has the entry of block w0 + i. A group's id is read with readlane (no memory wait in the
+  // steps); the window moves (one vector load, waited on) once per 64 blocks.
+  const int nbt = (kend + bs - 1) / bs;  // table entries the tile reads
+  int w0 = 0;
+  int win = lane < nbt ? bt_row[lane] : 0;
+  asm volatile("" : : "v"(win));
   auto group_base = [&](int step, int ps, int grp) -> int64_t {
     const int key = step * KS + ps * RPP + 16 * grp;
     if (key >= kend) return -1;
-    const int blk = bt_row[key / bs];
+    const int blk = __builtin_amdgcn_readlane(win, key / bs - w0);
     return ((int64_t)blk * bs + key % bs) * Hkv + kvh;
   };
+  // keep the blocks of tile `step` inside the window (tiles are visited in increasing order)
+  auto slide_window = [&](int step) {
+    const int k_last = min(step * KS + KS, kend) - 1;
+    if (k_last / bs >= w0 + 64) {  // wave-uniform
+      w0 = (step * KS) / bs;
+      win = w0 + lane < nbt ? bt_row[w0 + lane] : 0;
+      // consume the load here, so that no wait for it is left to the reads in every step
+      asm volatile("" : : "v"(win));
+    }
+  };
   auto fetch_bases = [&](int step, int64_t (&base)[PASSES][GPP]) {
+    slide_window(step);
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps)
 #pragma unroll
@@ -992,6 +1016,36 @@ bool device_cus(int* out) {
   return true;
 }
 
+// Second stream for the decode kernel, so that it runs beside the prefill kernel (the one is
+// HBM-bound, the other MFMA-bound): one per (device, caller stream), created on first use, kept
+// until the process ends, default priority. fork / join order it after the planning kernel and
+// before the merge on the caller's stream.
+struct AuxStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+bool aux_stream(hipStream_t st, AuxStream* out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, AuxStream> table;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = table.find({dev, st});
+  if (it != table.end()) {
+    *out = it->second;
+    return true;
+  }
+  AuxStream a;
+  if (hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) != hipSuccess) return false;
+  if (hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess)
+    return false;
+  table[{dev, st}] = a;
+  *out = a;
+  return true;
+}
+
 }  // namespace
 
 extern "C" int32_t cb_paged_attention_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
@@ -1092,8 +1146,17 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
   __bf16* op = static_cast<__bf16*>(out);
 
   plan_kernel<<<1, 1024, 0, st>>>(cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd,
-                                  p.max_splits, p.bq, block_size, max_blocks_per_seq, dec,
+                                  p.max_splits, p.bq, block_size, max_blocks_per_seq, max_kv_len, dec,
                                   p.dec_cap, pre, p.pre_cap, counts);
+  // With prefill work, the decode kernel goes to the second stream and overlaps the prefill.
+  hipStream_t dst = st;
+  AuxStream aux;
+  if (p.pre_cap > 0 && p.dec_cap > 0) {
+    if (!aux_stream(st, &aux)) return fail(CB_ERR_HIP, "creating the decode stream failed");
+    if (hipEventRecord(aux.fork, st) != hipSuccess || hipStreamWaitEvent(aux.stream, aux.fork, 0) != hipSuccess)
+      return fail(CB_ERR_HIP, "decode stream fork failed");
+    dst = aux.stream;
+  }
   if (p.pre_cap > 0) {
     const unsigned grid = (unsigned)(p.pre_cap * num_kv_heads);
     if (!record_if(tm, CB_KERNEL_PREFILL, true, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
@@ -1116,18 +1179,22 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
     const unsigned grid = (unsigned)std::max<int64_t>(
         1, std::min<int64_t>((items + kDecodeWaves - 1) / kDecodeWaves, 2 * (int64_t)cus));
     int32_t* queue = counts + 2;
-    if (!record_if(tm, CB_KERNEL_DECODE, true, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
+    if (!record_if(tm, CB_KERNEL_DECODE, true, dst)) return fail(CB_ERR_HIP, "hipEventRecord failed");
     if (head_dim == 128)
-      decode_kernel<128><<<grid, kDecodeWaves * 64, 0, st>>>(
+      decode_kernel<128><<<grid, kDecodeWaves * 64, 0, dst>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
           queue, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits,
           p.qmaxd, scale_log2);
     else
-      decode_kernel<64><<<grid, kDecodeWaves * 64, 0, st>>>(
+      decode_kernel<64><<<grid, kDecodeWaves * 64, 0, dst>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
           queue, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits,
           p.qmaxd, scale_log2);
-    if (!record_if(tm, CB_KERNEL_DECODE, false, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
+    if (!record_if(tm, CB_KERNEL_DECODE, false, dst)) return fail(CB_ERR_HIP, "hipEventRecord failed");
+  }
+  if (dst != st) {
+    if (hipEventRecord(aux.join, dst) != hipSuccess || hipStreamWaitEvent(st, aux.join, 0) != hipSuccess)
+      return fail(CB_ERR_HIP, "decode stream join failed");
   }
   if (p.max_splits > 1) {
     const int64_t nrows = (int64_t)num_seqs * p.qmaxd;
