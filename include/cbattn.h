@@ -24,8 +24,12 @@
  *        slot_mapping  [T]               int32   slot of each new token, or -1 = do not write
  *        out           [T, Hq, D]        bf16
  *  - The caller owns every buffer. The library allocates no device memory, does not
- *    synchronize, and keeps no pointer after it returns. Work is enqueued on `stream`
- *    (a hipStream_t; NULL means the default stream) in call order.
+ *    synchronize, and keeps no pointer to caller buffers after it returns. Work is enqueued on
+ *    `stream` (a hipStream_t; NULL means the default stream) in call order. For a batch with
+ *    both decode and prefill rows, cb_paged_attention runs its decode kernel on an internal
+ *    second stream (created on first use per device and caller stream, default priority, kept
+ *    until the process ends) that it forks from and joins back into `stream` with events, so
+ *    the call still completes in `stream` order.
  *  - Return value: CB_OK (0) or a negative cb_status. Only host-checkable facts are checked
  *    (null pointers, shape limits, alignment, workspace size); on error nothing is enqueued
  *    and cb_last_error() describes the failure. Data-dependent preconditions (below, and
