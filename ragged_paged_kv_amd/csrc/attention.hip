@@ -213,6 +213,27 @@ __device__ inline bf16x8 vt_operand(const uint32_t (&v)[8][D / 32], int jt) {
 // see the most keys) first.
 constexpr int kTailBuckets = 32;
 
+// Prefill tiles are split along the keys when the batch has too few prefill workgroups to fill
+// the GPU (fewer than two per compute unit): a tile of kend keys becomes ns parts of `chunk`
+// keys (a multiple of 32), one part per kPrefillSplitKeys keys, at most emax parts. Parts write
+// fp32 (o, lse) partials that the log-sum-exp merge combines. Plan and kernel use this same
+// function, so they agree on the parts.
+constexpr int kMaxPreSplits = 4;
+constexpr int kPrefillSplitKeys = 1024;
+// Splitting pays only when the longest prefill tile would outlast the batch's decode work, which
+// otherwise fills the compute units that the long tiles leave idle (the two kernels run side by
+// side). Estimated from measured rates on this GPU: one 32-key step of a prefill workgroup takes
+// about 1.4 us, and the decode kernel streams about 5.5 GB/ms.
+constexpr float kPrefillStepUs = 1.4f;
+constexpr float kDecodeBytesPerUs = 5.5e6f;
+
+__device__ inline void prefill_split(int kend, int emax, int& ns, int& chunk) {
+  int n0 = emax > 1 ? min(emax, (kend + kPrefillSplitKeys - 1) / kPrefillSplitKeys) : 1;
+  if (n0 < 1) n0 = 1;
+  chunk = ((kend + n0 - 1) / n0 + 31) / 32 * 32;
+  ns = (kend + chunk - 1) / chunk;
+}
+
 __device__ inline int seq_items(const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_lens,
                                 int s, int num_seqs, int G, int P, int qmaxd, int max_splits,
                                 int bq, int bs, int max_blocks, int max_kv, int& nfull, int& rem,
@@ -241,23 +262,37 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int32_t bq, int32_t bs, int32_t max_blocks,
                                                     int32_t max_kv, Work* __restrict__ dec,
                                                     int64_t dec_cap, Work* __restrict__ pre,
-                                                    int64_t pre_cap, int32_t* __restrict__ counts) {
+                                                    int64_t pre_cap, int32_t* __restrict__ counts,
+                                                    int32_t Hkv, int32_t cus, int32_t maxs,
+                                                    int32_t num_tokens, int32_t kv_token_bytes,
+                                                    int32_t* __restrict__ nsplit_tok) {
   __shared__ int32_t sd[1024];
   __shared__ int32_t sp[1024];
   __shared__ int32_t base[2];
+  __shared__ int32_t split_on;
+  __shared__ unsigned long long dec_keys;  // sum of decode sequences' lengths
+  __shared__ int32_t max_pre_len;          // longest prefill sequence (its last tile's keys)
   __shared__ int32_t tail_count[kTailBuckets];
   __shared__ int32_t tail_next[kTailBuckets];
   const int tid = threadIdx.x;
-  if (tid == 0) base[0] = base[1] = 0;
+  if (tid == 0) {
+    base[0] = base[1] = 0;
+    dec_keys = 0;
+    max_pre_len = 0;
+  }
   if (tid < kTailBuckets) tail_count[tid] = tail_next[tid] = 0;
+  if (maxs > 1)  // split counts of prefill tokens: 0 until a split tile writes its own
+    for (int t = tid; t < num_tokens; t += 1024) nsplit_tok[t] = 0;
   __syncthreads();
-  // pass 1: full partitions and prefill tiles by prefix sums; count tails per length bucket
+  // pass 1: full partitions by prefix sums; prefill tiles counted; tails counted per bucket
   for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
     const int s = s0 + tid;
     int nfull, rem, np;
     seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull,
               rem, np);
     if (rem > 0) atomicAdd(&tail_count[(P - rem) * kTailBuckets / P], 1);
+    if (nfull + rem > 0) atomicAdd(&dec_keys, (unsigned long long)(nfull * P + rem));
+    if (np > 0) atomicMax(&max_pre_len, kv_lens[s]);
     sd[tid] = nfull;
     sp[tid] = np;
     __syncthreads();
@@ -270,11 +305,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       __syncthreads();
     }
     const int64_t ed = (int64_t)base[0] + sd[tid] - nfull;
-    const int64_t ep = (int64_t)base[1] + sp[tid] - np;
     for (int k = 0; k < nfull; ++k)
       if (ed + k < dec_cap) dec[ed + k] = Work{s, k};
-    for (int k = 0; k < np; ++k)
-      if (ep + k < pre_cap) pre[ep + k] = Work{s, np - 1 - k};
     __syncthreads();
     if (tid == 1023) {
       base[0] += sd[1023];
@@ -290,9 +322,59 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       acc += tail_count[b];
     }
     counts[0] = (int32_t)min((int64_t)acc, dec_cap);
-    counts[1] = (int32_t)min((int64_t)base[1], pre_cap);
     counts[2] = 0;  // decode work-queue head
+    const float t_decode = (float)dec_keys * Hkv * kv_token_bytes / kDecodeBytesPerUs;
+    const float t_longest = (float)((max_pre_len + 31) / 32) * kPrefillStepUs;
+    split_on = (maxs > 1 && (int64_t)base[1] * Hkv < 2 * (int64_t)cus && t_longest > t_decode)
+                   ? 1 : 0;  // split prefill tiles
+    counts[3] = split_on;
   }
+  __syncthreads();
+  const int emax = split_on ? maxs : 1;
+  // prefill items (sequence, tile * kMaxPreSplits + part): a sequence's last tiles first
+  if (tid == 0) base[1] = 0;
+  __syncthreads();
+  for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
+    const int s = s0 + tid;
+    int nfull, rem, np;
+    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull,
+              rem, np);
+    int nit = np, qn = 0, L = 0;
+    if (np > 0 && emax > 1) {  // few tiles (splitting is on): count the parts
+      qn = cu[s + 1] - cu[s];
+      L = kv_lens[s];
+      nit = 0;
+      for (int tl = 0; tl < np; ++tl) {
+        int ns, chunk;
+        prefill_split(L - qn + min(qn, (tl + 1) * bq), emax, ns, chunk);
+        nit += ns;
+      }
+    }
+    sp[tid] = nit;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int b = tid >= off ? sp[tid - off] : 0;
+      __syncthreads();
+      sp[tid] += b;
+      __syncthreads();
+    }
+    int64_t ep = (int64_t)base[1] + sp[tid] - nit;
+    if (emax > 1) {
+      for (int tl = np - 1; tl >= 0; --tl) {
+        int ns, chunk;
+        prefill_split(L - qn + min(qn, (tl + 1) * bq), emax, ns, chunk);
+        for (int part = 0; part < ns; ++part, ++ep)
+          if (ep < pre_cap) pre[ep] = Work{s, tl * kMaxPreSplits + part};
+      }
+    } else {
+      for (int k = 0; k < np; ++k)
+        if (ep + k < pre_cap) pre[ep + k] = Work{s, (np - 1 - k) * kMaxPreSplits};
+    }
+    __syncthreads();
+    if (tid == 1023) base[1] += sp[1023];
+    __syncthreads();
+  }
+  if (tid == 0) counts[1] = (int32_t)min((int64_t)base[1], pre_cap);
   __syncthreads();
   // pass 2: place the tails
   for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
@@ -552,7 +634,8 @@ void prefill_kernel(
     const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables,
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     __bf16* __restrict__ out, const Work* __restrict__ items, const int32_t* __restrict__ counts,
-    int32_t Hq, int32_t Hkv, int32_t bs, int32_t max_blocks_per_seq, int32_t bq,
+    float* __restrict__ o_pre, float* __restrict__ lse_pre, int32_t* __restrict__ nsplit_tok,
+    int32_t maxs, int32_t Hq, int32_t Hkv, int32_t bs, int32_t max_blocks_per_seq, int32_t bq,
     float scale_log2) {
   constexpr int KS = kPrefillKeys;
   constexpr int NT = kPrefillTiles;  // 16-row MFMA tiles per wave
@@ -573,14 +656,19 @@ void prefill_kernel(
   const int kvh = blockIdx.x - item * Hkv;
   if (item >= counts[1]) return;
   const Work w = items[item];
-  const int s = w.seq, qt = w.idx;
+  const int s = w.seq, qt = w.idx / kMaxPreSplits, part = w.idx - qt * kMaxPreSplits;
   const int G = Hq / Hkv;
   const int q0 = cu[s];
   const int qn = cu[s + 1] - q0;
   const int L = kv_lens[s];
   const int tok0 = qt * bq;
   const int tok_end = min(qn, tok0 + bq);
-  const int kend = L - qn + tok_end;  // keys [0, kend) are visible to some row of the tile
+  // keys [0, kend_tile) are visible to some row of the tile; this part covers [kb, kend)
+  const int kend_tile = L - qn + tok_end;
+  int ns, chunk;
+  prefill_split(kend_tile, counts[3] ? maxs : 1, ns, chunk);
+  const int kb = part * chunk;  // a multiple of KS
+  const int kend = min(kend_tile, kb + chunk);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -628,21 +716,21 @@ void prefill_kernel(
   // Block ids come from a window of the sequence's block-table row held in one register: lane i
   // has the entry of block w0 + i. A group's id is read with readlane (no memory wait in the
   // steps); the window moves (one vector load, waited on) once per 64 blocks.
-  const int nbt = (kend + bs - 1) / bs;  // table entries the tile reads
-  int w0 = 0;
-  int win = lane < nbt ? bt_row[lane] : 0;
+  const int nbt = (kend + bs - 1) / bs;  // table entries the part reads
+  int w0 = kb / bs;
+  int win = w0 + lane < nbt ? bt_row[w0 + lane] : 0;
   asm volatile("" : : "v"(win));
   auto group_base = [&](int step, int ps, int grp) -> int64_t {
-    const int key = step * KS + ps * RPP + 16 * grp;
+    const int key = kb + step * KS + ps * RPP + 16 * grp;
     if (key >= kend) return -1;
     const int blk = __builtin_amdgcn_readlane(win, key / bs - w0);
     return ((int64_t)blk * bs + key % bs) * Hkv + kvh;
   };
   // keep the blocks of tile `step` inside the window (tiles are visited in increasing order)
   auto slide_window = [&](int step) {
-    const int k_last = min(step * KS + KS, kend) - 1;
+    const int k_last = min(kb + step * KS + KS, kend) - 1;
     if (k_last / bs >= w0 + 64) {  // wave-uniform
-      w0 = (step * KS) / bs;
+      w0 = (kb + step * KS) / bs;
       win = w0 + lane < nbt ? bt_row[w0 + lane] : 0;
       // consume the load here, so that no wait for it is left to the reads in every step
       asm volatile("" : : "v"(win));
@@ -680,10 +768,10 @@ void prefill_kernel(
   // are stored as zero, so that a masked probability (0) never meets an unwritten V value.
   auto stash = [&](auto set_tag, int buf, int step) {
     constexpr int X = decltype(set_tag)::value;
-    if ((step + 1) * KS > kend) {  // wave-uniform
+    if (kb + (step + 1) * KS > kend) {  // wave-uniform
 #pragma unroll
       for (int ps = 0; ps < PASSES; ++ps)
-        if (step * KS + ps * RPP + lr >= kend) {
+        if (kb + step * KS + ps * RPP + lr >= kend) {
           rk[X][ps] = make_uint4(0, 0, 0, 0);
           rv[X][ps] = make_uint4(0, 0, 0, 0);
         }
@@ -742,8 +830,8 @@ void prefill_kernel(
   // Tiles whose keys are all visible to every row of this wave take no mask; the rest (the
   // causal diagonal and the range end) do. The split differs between waves, but every wave runs
   // the same steps, so the barriers pair up in order.
-  const int nsteps = (kend + KS - 1) / KS;  // >= 1
-  const int n_open = min(nsteps, min(kend, wave_first_last_key + 1) / KS);
+  const int nsteps = (kend - kb + KS - 1) / KS;  // >= 1
+  const int n_open = min(nsteps, max(0, min(kend, wave_first_last_key + 1) - kb) / KS);
 
   // prologue: tiles 0 and 1 into LDS, tile 2 into register set 0, bases of tile 3 (tile
   // indices past the last tile stand for the last tile)
@@ -766,8 +854,8 @@ void prefill_kernel(
     float mc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      mc[nt] = n_open > 0 ? chunk_max<false>(acc[nt], 0, kend, last_key[nt], scale_log2, g)
-                          : chunk_max<true>(acc[nt], 0, kend, last_key[nt], scale_log2, g);
+      mc[nt] = n_open > 0 ? chunk_max<false>(acc[nt], kb, kend, last_key[nt], scale_log2, g)
+                          : chunk_max<true>(acc[nt], kb, kend, last_key[nt], scale_log2, g);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) rescale_lazy<NO>(mc[nt], m[nt], l[nt], o[nt]);
   }
@@ -790,7 +878,7 @@ void prefill_kernel(
     float mc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      mc[nt] = chunk_max<MASK_NEXT>(acc_n[nt], (st + 1) * KS, kend, last_key[nt], scale_log2, g);
+      mc[nt] = chunk_max<MASK_NEXT>(acc_n[nt], kb + (st + 1) * KS, kend, last_key[nt], scale_log2, g);
     stash(Int<P>{}, fil, min(st + 2, last_tile));
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps)
@@ -829,19 +917,35 @@ void prefill_kernel(
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) l[nt] = group_sum(l[nt]);  // row sums (all lanes take part)
-  // normalise and store: lane (n, g) holds row n, dims (D/4)g + 4jt + i (D/4 contiguous dims)
+  if (ns > 1 && part == 0 && kvh == 0)  // the merge finds this tile's tokens by their count
+    for (int i = tid; i < tok_end - tok0; i += kPrefillWaves * 64) nsplit_tok[q0 + tok0 + i] = ns;
+  // normalise and store: lane (n, g) holds row n, dims (D/4)g + 4jt + i (D/4 contiguous dims);
+  // a part of a split tile stores fp32 o and its lse
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int R = wave * (16 * NT) + nt * 16 + n;
     const int qi = tok0 + R / G, hh = R - (R / G) * G;
     if (qi >= tok_end) continue;
+    const int64_t row = (int64_t)(q0 + qi) * Hq + kvh * G + hh;
+    if (ns > 1) {
+      const bool empty = !(l[nt] > 0.f);  // no visible key in this part
+      const float inv = empty ? 0.f : 1.f / l[nt];
+      const int64_t pb = row * maxs + part;
+      float* dst = o_pre + pb * D + (D / 4) * g;
+#pragma unroll
+      for (int jt = 0; jt < NO; ++jt)
+        *reinterpret_cast<float4*>(dst + 4 * jt) =
+            make_float4(o[nt][jt][0] * inv, o[nt][jt][1] * inv, o[nt][jt][2] * inv, o[nt][jt][3] * inv);
+      if (g == 0) lse_pre[pb] = empty ? -INFINITY : (m[nt] + __log2f(l[nt])) * kLn2;
+      continue;
+    }
     const float inv = 1.f / l[nt];
     __bf16 r[D / 4];
 #pragma unroll
     for (int jt = 0; jt < NO; ++jt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[4 * jt + i] = (__bf16)(o[nt][jt][i] * inv);
-    uint4* dst = reinterpret_cast<uint4*>(out + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + (D / 4) * g);
+    uint4* dst = reinterpret_cast<uint4*>(out + row * D + (D / 4) * g);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) dst[c] = __builtin_bit_cast(uint4, *reinterpret_cast<const bf16x8*>(&r[8 * c]));
   }
@@ -871,21 +975,32 @@ __device__ inline void merge_accumulate(const float4 (&a)[kReduceBatch], const f
   }
 }
 
-template <int D, bool INTERNAL>
-__global__ __launch_bounds__(256) void reduce_kernel(
-    const float* __restrict__ o_part, const float* __restrict__ lse_part,
-    const int32_t* __restrict__ num_splits, __bf16* __restrict__ out, int32_t Hq,
-    int32_t max_splits, int64_t nrows, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ kv_lens, int32_t qmaxd, int32_t G, int32_t P) {
+// MODE: kReduceStandalone (cb_split_kv_reduce: split count per token from the caller),
+// kReduceDecode (decode rows of the attention call: count from the sequence's length),
+// kReducePrefill (tokens of split prefill tiles: count written by the prefill kernel; a token
+// with a count below 2 was written directly and is skipped before any partial is read).
+enum { kReduceStandalone = 0, kReduceDecode = 1, kReducePrefill = 2 };
+
+template <int D, int MODE>
+__device__ inline void merge_one(int64_t gid, const float* __restrict__ o_part,
+                                 const float* __restrict__ lse_part,
+                                 const int32_t* __restrict__ num_splits, __bf16* __restrict__ out,
+                                 int32_t Hq, int32_t max_splits, int64_t nrows,
+                                 const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_lens,
+                                 int32_t qmaxd, int32_t G, int32_t P) {
   constexpr int CH = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_row = (int64_t)Hq * CH;
   const int64_t prow = gid / per_row;
   if (prow >= nrows) return;
   const int rem = (int)(gid - prow * per_row);
   const int h = rem / CH, c = rem - (rem / CH) * CH;
   const int64_t base = (prow * Hq + h) * max_splits;
-  const int nb = min(max_splits, kReduceBatch);
+  int ns_pre = 0;
+  if constexpr (MODE == kReducePrefill) {
+    ns_pre = min(num_splits[prow], max_splits);
+    if (ns_pre < 2) return;
+  }
+  const int nb = min(MODE == kReducePrefill ? ns_pre : max_splits, kReduceBatch);
   float lk[kReduceBatch];
   float4 a[kReduceBatch], b[kReduceBatch];
 #pragma unroll
@@ -901,13 +1016,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   }
   int64_t t;
   int ns;
-  if constexpr (INTERNAL) {
+  if constexpr (MODE == kReduceDecode) {
     const int s = (int)(prow / qmaxd), qi = (int)(prow - (prow / qmaxd) * qmaxd);
     const int qn = cu[s + 1] - cu[s];
     if (qi >= qn || qn * G > 16 || qn > qmaxd) return;
     ns = (kv_lens[s] + P - 1) / P;
     if (ns <= 1 || ns > max_splits) return;  // single partition: written directly
     t = cu[s] + qi;
+  } else if constexpr (MODE == kReducePrefill) {
+    t = prow;
+    ns = ns_pre;
   } else {
     t = prow;
     ns = min(num_splits[t], max_splits);
@@ -944,14 +1062,41 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   *reinterpret_cast<bf16x8*>(out + (t * Hq + h) * D + c * 8) = __builtin_bit_cast(bf16x8, r);
 }
 
+// One thread per (row, head, 8-dim chunk); the prefill merge strides over all tokens with a
+// small grid, since most tokens (those of unsplit tiles and of decodes) only read their count.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void reduce_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    const int32_t* __restrict__ num_splits, __bf16* __restrict__ out, int32_t Hq,
+    int32_t max_splits, int64_t nrows, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ kv_lens, int32_t qmaxd, int32_t G, int32_t P,
+    const int32_t* __restrict__ split_flag) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if constexpr (MODE == kReducePrefill) {
+    if (*split_flag == 0) return;  // the plan split no prefill tile
+    const int64_t total = nrows * Hq * (D / 8);
+    for (int64_t x = gid; x < total; x += (int64_t)gridDim.x * 256)
+      merge_one<D, MODE>(x, o_part, lse_part, num_splits, out, Hq, max_splits, nrows, cu, kv_lens,
+                         qmaxd, G, P);
+  } else {
+    merge_one<D, MODE>(gid, o_part, lse_part, num_splits, out, Hq, max_splits, nrows, cu, kv_lens,
+                       qmaxd, G, P);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Host side
 
 struct Plan {
-  int32_t G = 0, P = 0, max_splits = 0, qmaxd = 0, bq = 0;
+  int32_t G = 0, P = 0, max_splits = 0, qmaxd = 0, bq = 0, pre_splits = 1;
   int64_t dec_cap = 0, pre_cap = 0;
-  size_t off_counts = 0, off_dec = 0, off_pre = 0, off_opart = 0, off_lse = 0, total = 0;
+  size_t off_counts = 0, off_dec = 0, off_pre = 0, off_opart = 0, off_lse = 0;
+  size_t off_opre = 0, off_lsepre = 0, off_nsplit = 0, total = 0;
 };
+
+// Prefill partials take num_tokens * Hq * pre_splits * (D + 1) fp32 of workspace; splitting is
+// offered only while that stays within this budget.
+constexpr size_t kPrefillPartialBudget = size_t(256) << 20;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -977,7 +1122,13 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, in
   p.qmaxd = max_q_len < dec_q ? max_q_len : dec_q;
   p.bq = kPrefillRows / p.G;
   p.dec_cap = (int64_t)num_seqs * p.max_splits;
-  p.pre_cap = (max_q_len > dec_q) ? (int64_t)num_tokens / p.bq + num_seqs : 0;
+  if (max_q_len > dec_q) {
+    const size_t per_split = (size_t)num_tokens * Hq * (D + 1) * sizeof(float);
+    const size_t fit = per_split > 0 ? kPrefillPartialBudget / per_split : 0;
+    p.pre_splits = (int32_t)std::min<size_t>(kMaxPreSplits, std::max<size_t>(1, fit));
+    if (p.pre_splits < 2) p.pre_splits = 1;
+  }
+  p.pre_cap = (max_q_len > dec_q) ? ((int64_t)num_tokens / p.bq + num_seqs) * p.pre_splits : 0;
   size_t off = 0;
   p.off_counts = off;
   off = align256(off + 16);
@@ -990,6 +1141,13 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, in
   off = align256(off + sizeof(float) * nrows * D);
   p.off_lse = off;
   off = align256(off + sizeof(float) * nrows);
+  const size_t prows = p.pre_splits > 1 ? (size_t)num_tokens * Hq * p.pre_splits : 0;
+  p.off_opre = off;
+  off = align256(off + sizeof(float) * prows * D);
+  p.off_lsepre = off;
+  off = align256(off + sizeof(float) * prows);
+  p.off_nsplit = off;
+  off = align256(off + (p.pre_splits > 1 ? sizeof(int32_t) * (size_t)num_tokens : 0));
   p.total = off;
   return p;
 }
@@ -1139,6 +1297,11 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
   Work* pre = reinterpret_cast<Work*>(ws + p.off_pre);
   float* o_part = reinterpret_cast<float*>(ws + p.off_opart);
   float* lse_part = reinterpret_cast<float*>(ws + p.off_lse);
+  float* o_pre = reinterpret_cast<float*>(ws + p.off_opre);
+  float* lse_pre = reinterpret_cast<float*>(ws + p.off_lsepre);
+  int32_t* nsplit_tok = reinterpret_cast<int32_t*>(ws + p.off_nsplit);
+  int cus = 0;
+  if (!device_cus(&cus)) return fail(CB_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
   const float scale_log2 = scale * kLog2e;
   const __bf16* qp = static_cast<const __bf16*>(q_packed);
   const __bf16* kc = static_cast<const __bf16*>(k_cache);
@@ -1147,7 +1310,8 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
 
   plan_kernel<<<1, 1024, 0, st>>>(cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd,
                                   p.max_splits, p.bq, block_size, max_blocks_per_seq, max_kv_len, dec,
-                                  p.dec_cap, pre, p.pre_cap, counts);
+                                  p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus, p.pre_splits,
+                                  num_tokens, 4 * head_dim, nsplit_tok);
   // With prefill work, the decode kernel goes to the second stream and overlaps the prefill.
   hipStream_t dst = st;
   AuxStream aux;
@@ -1158,23 +1322,44 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
     dst = aux.stream;
   }
   if (p.pre_cap > 0) {
-    const unsigned grid = (unsigned)(p.pre_cap * num_kv_heads);
+    // one workgroup per (item, KV head); workgroups past the plan's item count exit at once.
+    // Tiles are split only while tiles * Hkv < 2 * CUs, so items * Hkv stays below
+    // 2 * CUs * pre_splits then, which bounds the grid beside the unsplit tile bound.
+    const int64_t unsplit = p.pre_cap / p.pre_splits * num_kv_heads;
+    const int64_t grid64 = std::min<int64_t>(
+        p.pre_cap * num_kv_heads,
+        p.pre_splits > 1 ? std::max<int64_t>(unsplit, 2 * (int64_t)cus * p.pre_splits) : unsplit);
+    const unsigned grid = (unsigned)grid64;
     if (!record_if(tm, CB_KERNEL_PREFILL, true, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
     if (head_dim == 128)
       prefill_kernel<128><<<grid, kPrefillWaves * 64, 0, st>>>(
-          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
-          num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
+          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, o_pre, lse_pre,
+          nsplit_tok, p.pre_splits, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq,
+          p.bq, scale_log2);
     else
       prefill_kernel<64><<<grid, kPrefillWaves * 64, 0, st>>>(
-          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, num_q_heads,
-          num_kv_heads, block_size, max_blocks_per_seq, p.bq, scale_log2);
+          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, o_pre, lse_pre,
+          nsplit_tok, p.pre_splits, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq,
+          p.bq, scale_log2);
     if (!record_if(tm, CB_KERNEL_PREFILL, false, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
+    // merge the parts of split prefill tiles (tokens of other tiles skip); no tile can split
+    // when no sequence is longer than one part
+    if (p.pre_splits > 1 && max_kv_len > kPrefillSplitKeys) {
+      const int64_t threads = (int64_t)num_tokens * num_q_heads * (head_dim / 8);
+      const unsigned mgrid = (unsigned)std::min<int64_t>((threads + 255) / 256, 2 * (int64_t)cus);
+      if (head_dim == 128)
+        reduce_kernel<128, kReducePrefill><<<mgrid, 256, 0, st>>>(
+            o_pre, lse_pre, nsplit_tok, op, num_q_heads, p.pre_splits, num_tokens, nullptr,
+            nullptr, 0, 0, 0, counts + 3);
+      else
+        reduce_kernel<64, kReducePrefill><<<mgrid, 256, 0, st>>>(
+            o_pre, lse_pre, nsplit_tok, op, num_q_heads, p.pre_splits, num_tokens, nullptr,
+            nullptr, 0, 0, 0, counts + 3);
+    }
   }
   {
     // persistent: two 4-wave workgroups per compute unit (2 waves per SIMD), never more
     // workgroups than a quarter of the items
-    int cus = 0;
-    if (!device_cus(&cus)) return fail(CB_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
     const int64_t items = p.dec_cap * num_kv_heads;
     const unsigned grid = (unsigned)std::max<int64_t>(
         1, std::min<int64_t>((items + kDecodeWaves - 1) / kDecodeWaves, 2 * (int64_t)cus));
@@ -1201,13 +1386,13 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
     const int64_t threads = nrows * num_q_heads * (head_dim / 8);
     const unsigned grid = (unsigned)((threads + 255) / 256);
     if (head_dim == 128)
-      reduce_kernel<128, true><<<grid, 256, 0, st>>>(o_part, lse_part, nullptr, op, num_q_heads,
+      reduce_kernel<128, kReduceDecode><<<grid, 256, 0, st>>>(o_part, lse_part, nullptr, op, num_q_heads,
                                                      p.max_splits, nrows, cu_seqlens_q, kv_lens,
-                                                     p.qmaxd, p.G, p.P);
+                                                     p.qmaxd, p.G, p.P, nullptr);
     else
-      reduce_kernel<64, true><<<grid, 256, 0, st>>>(o_part, lse_part, nullptr, op, num_q_heads,
+      reduce_kernel<64, kReduceDecode><<<grid, 256, 0, st>>>(o_part, lse_part, nullptr, op, num_q_heads,
                                                     p.max_splits, nrows, cu_seqlens_q, kv_lens,
-                                                    p.qmaxd, p.G, p.P);
+                                                    p.qmaxd, p.G, p.P, nullptr);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(CB_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
@@ -1233,13 +1418,13 @@ extern "C" int cb_split_kv_reduce(const float* o_part, const float* lse_part,
   const int64_t grid = (threads + 255) / 256;
   if (grid > INT32_MAX) return fail(CB_ERR_UNSUPPORTED, "cb_split_kv_reduce: too many rows");
   if (head_dim == 128)
-    reduce_kernel<128, false><<<(unsigned)grid, 256, 0, st>>>(
+    reduce_kernel<128, kReduceStandalone><<<(unsigned)grid, 256, 0, st>>>(
         o_part, lse_part, num_splits, op, num_q_heads, max_splits, num_tokens, nullptr, nullptr,
-        1, 1, 1);
+        1, 1, 1, nullptr);
   else
-    reduce_kernel<64, false><<<(unsigned)grid, 256, 0, st>>>(
+    reduce_kernel<64, kReduceStandalone><<<(unsigned)grid, 256, 0, st>>>(
         o_part, lse_part, num_splits, op, num_q_heads, max_splits, num_tokens, nullptr, nullptr,
-        1, 1, 1);
+        1, 1, 1, nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(CB_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(e));
   return cb::ok();

@@ -167,6 +167,14 @@ EDGE = {
     "bs64": ([synth.SeqSpec(1, 200), synth.SeqSpec(50, 150)], 32, 8, 128, 64),
     "bs256": ([synth.SeqSpec(1, 700), synth.SeqSpec(100, 600)], 32, 8, 128, 256),
     "long-chunk-offset": ([synth.SeqSpec(200, 1500)], 32, 8, 128, 16),
+    # prefill tiles split along the keys (few tiles, long contexts): 4 parts, uneven rounding,
+    # head_dim 64, 256-row tiles of one head, and next to decodes and a short prompt
+    "prefill-split-4": ([synth.SeqSpec(96, 4096)], 32, 8, 128, 16),
+    "prefill-split-uneven": ([synth.SeqSpec(20, 2049), synth.SeqSpec(40, 3073)], 32, 8, 128, 32),
+    "prefill-split-d64": ([synth.SeqSpec(70, 2500)], 16, 2, 64, 16),
+    "prefill-split-mha": ([synth.SeqSpec(300, 2600)], 4, 4, 128, 16),
+    "prefill-split-mixed": ([synth.SeqSpec(1, 3000), synth.SeqSpec(64, 2100), synth.SeqSpec(33, 33)],
+                            32, 8, 128, 16),
 }
 
 
