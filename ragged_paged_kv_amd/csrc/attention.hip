@@ -608,6 +608,74 @@ void decode_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// 32 x 32 MFMA layout of the prefill kernel (v_mfma_f32_32x32x16_bf16). A operand: lane l holds
+// row l % 32, contraction slots 8h .. 8h + 7 (h = l / 32); B operand: column l % 32, the same
+// slots; C/D: column l % 32, rows 8(i / 4) + 4h + i % 4 for accumulator i = 0..15. The prefill
+// kernel computes S^T = K Q^T (rows = 32 keys, columns = 32 query rows), so each lane holds 16
+// of the 32 scores of its query row, the other 16 sitting in lane l ^ 32.
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ inline f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// max / sum over lanes l and l ^ 32 (the two halves of a query row's scores)
+__device__ inline float pair_max(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Online softmax over one 32-key chunk in the 32 x 32 layout: acc[i] is the score of key
+// k0 + 8(i / 4) + 4h + i % 4 of this lane's row. Same scheme as chunk_max / rescale_lazy /
+// chunk_exp: m is the row's reference max (scaled log2 units, equal in both lanes of the row),
+// l this lane's part of the row sum.
+template <bool MASK>
+__device__ inline float chunk_max32(f32x16& acc, int k0, int kend, int last_key, float c, int h) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (MASK) {
+      const int key = k0 + 8 * (i >> 2) + 4 * h + (i & 3);
+      acc[i] = (key < kend && key <= last_key) ? acc[i] : -INFINITY;
+    }
+    mx = fmaxf(mx, acc[i]);
+  }
+  return mx * c;
+}
+
+template <int NDT>
+__device__ inline void rescale_lazy32(float m_lane, float& m, float& l, f32x16 (&o)[NDT]) {
+  if (__builtin_amdgcn_ballot_w64(m_lane > m + kRescaleSlack) != 0) {  // wave-uniform
+    const float m_new = fmaxf(m, pair_max(m_lane));
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+    m = m_new;
+  }
+}
+
+// P^T operands of the chunk's two 16-key halves: slot e of half ks is key
+// k0 + 16ks + 8(e / 4) + 4h + e % 4, i.e. accumulator 8ks + e.
+__device__ inline void chunk_exp32(const f32x16& acc, float c, float m, float& l, bf16x8 (&pb)[2]) {
+  float rs = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[8 * ks + e], c, -m));
+      rs += p;
+      pb[ks][e] = (__bf16)p;
+    }
+  l += rs;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Prefill kernel: one workgroup of 4 waves per (query tile of 128 rows, KV head). Each wave owns
 // 32 rows (two 16-row MFMA tiles). K/V tiles of 32 keys are gathered through the block table
 // into LDS by all 256 threads and read by every wave. Three LDS tiles are in flight, so a wave
@@ -638,9 +706,8 @@ void prefill_kernel(
     int32_t maxs, int32_t Hq, int32_t Hkv, int32_t bs, int32_t max_blocks_per_seq, int32_t bq,
     float scale_log2) {
   constexpr int KS = kPrefillKeys;
-  constexpr int NT = kPrefillTiles;  // 16-row MFMA tiles per wave
-  constexpr int KSTEPS = D / 32;
-  constexpr int NO = D / 16;
+  constexpr int KK = D / 16;   // 32x32x16 MFMA k-steps over the head dimension
+  constexpr int NDT = D / 32;  // 32-dim output tiles
   constexpr int CPR = D / 8;  // 16-byte chunks per key row
   // threads that load K/V (a whole number of waves) and key rows they cover per pass
   constexpr int LOADERS = kPrefillWaves * 64 < KS * CPR ? kPrefillWaves * 64 : KS * CPR;
@@ -673,33 +740,33 @@ void prefill_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
+  const int n32 = lane & 31, h = lane >> 5;  // this lane's query row of the wave, row half
 
-  // Q^T operands of this wave's two row tiles
-  bf16x8 qf[NT][KSTEPS];
-  int last_key[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int R = wave * (16 * NT) + nt * 16 + n;
+  // Q^T operand (B of S^T = K Q^T): lane l holds dims [16kk + 8h, +8) of query row
+  // R = 32 wave + l % 32, row = (token R / G, head R % G)
+  static_assert(kPrefillTiles == 2, "the 32 x 32 layout gives each wave 32 query rows");
+  bf16x8 qf[KK];
+  int last_key;
+  {
+    const int R = wave * 32 + n32;
     const int qi = tok0 + R / G, hh = R - (R / G) * G;
     if (qi < tok_end) {
-      const bf16x8* p = reinterpret_cast<const bf16x8*>(
-          q + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + g * (D / 4));
+      const __bf16* p = q + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + 8 * h;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qf[nt][kk] = p[kk];
-      last_key[nt] = L - qn + qi;
+      for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(p + 16 * kk);
+      last_key = L - qn + qi;
     } else {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[nt][kk][e] = (__bf16)0.f;
-      last_key[nt] = -1;
+        for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
+      last_key = -1;
     }
   }
 
   // smallest last visible key over this wave's rows (its first row's token); rows past tok_end
   // have zero Q, finite scores and are never written
-  const int wave_first_last_key = L - qn + tok0 + wave * (16 * NT) / G;
+  const int wave_first_last_key = L - qn + tok0 + wave * 32 / G;
 
   // Loader role of this thread: key row lr + pass * RPP of each tile, 16-byte chunk lc. A pass
   // covers whole 16-key groups, each inside one block, so the block id and in-block offset of a
@@ -783,49 +850,39 @@ void prefill_kernel(
     }
   };
 
-  // S^T = K Q^T of LDS tile `buf` for both row tiles (the K fragment is shared):
-  // acc[nt][j][i] is the score of key 16j + 4g + i of the tile for row n of row tile nt.
-  auto qk = [&](int buf, f32x4 (&acc)[NT][2]) {
+  // S^T = K Q^T of LDS tile `buf`: A = K rows (lane l: key l % 32, dims [16kk + 8h, +8))
+  auto qk = [&](int buf, f32x16& acc) {
+    acc = f32x16{};
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * j + n][g * (D / 4) + 8 * kk]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][j] = mfma16x16x32(kf, qf[nt][kk], acc[nt][j]);
-      }
-  };
-  // O^T += V^T P^T of LDS tile `buf`. The V^T operands come from transposing LDS reads: lanes
-  // 4j + a of lane group g read key 16h + 4g + j, dims (D/4)a + 4jt .. +3; lane 4a + b of the
-  // group receives element b of those four reads, i.e. dim (D/4)a + 4jt + b for keys
-  // 16h + 4g + j, j = 0..3, which is the key order of P^T's elements.
-  f32x4 o[NT][NO];
-  auto pv = [&](int buf, const bf16x8 (&pb)[NT]) {
-    const __bf16* vb = &sm.v[buf][4 * g + (n >> 2)][(D / 4) * (n & 3)];
-#pragma unroll
-    for (int jt = 0; jt < NO; ++jt) {
-      const s16x4 lo = lds_read_tr16(vb + 4 * jt);
-      const s16x4 hi = lds_read_tr16(vb + 16 * SmemT::STRIDE + 4 * jt);
-      const bf16x8 vt =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt][jt] = mfma16x16x32(vt, pb[nt], o[nt][jt]);
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sm.k[buf][n32][16 * kk + 8 * h]);
+      acc = mfma32x32x16(kf, qf[kk], acc);
     }
   };
+  // O^T += V^T P^T of LDS tile `buf`, per 32-dim tile dt and 16-key half ks. The V^T operand
+  // (A: lane l holds dim 32dt + l % 32 for the slots of P^T's half ks) comes from transposing
+  // LDS reads: within each 16-lane group, lanes 4j + a read key 16ks + 8e' + 4h + j, dims
+  // 32dt + 16(group % 2) + 4a .. +3, and lane 4a + b receives element b of the four reads: dim
+  // 32dt + l % 32, keys 16ks + 8e' + 4h + j, j = 0..3 (slots 4e' + j).
+  f32x16 o[NDT];
+  auto pv = [&](int buf, const bf16x8 (&pb)[2]) {
+    const int r = lane & 15;
+    const __bf16* vb = &sm.v[buf][4 * h + (r >> 2)][16 * ((lane >> 4) & 1) + 4 * (r & 3)];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const s16x4 lo = lds_read_tr16(vb + (16 * ks) * SmemT::STRIDE + 32 * dt);
+        const s16x4 hi = lds_read_tr16(vb + (16 * ks + 8) * SmemT::STRIDE + 32 * dt);
+        const bf16x8 vt =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = mfma32x32x16(vt, pb[ks], o[dt]);
+      }
+  };
 
-  float m[NT], l[NT];
+  float m = kMaxFloor, l = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m[nt] = kMaxFloor;
-    l[nt] = 0.f;
-#pragma unroll
-    for (int t = 0; t < NO; ++t) o[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < NDT; ++t) o[t] = f32x16{};
 
   // Tiles whose keys are all visible to every row of this wave take no mask; the rest (the
   // causal diagonal and the range end) do. The split differs between waves, but every wave runs
@@ -848,16 +905,12 @@ void prefill_kernel(
   fetch_bases(min(3, last_tile), base_a);
   __syncthreads();
 
-  f32x4 acc[NT][2];
+  f32x16 acc;
   qk(0, acc);
   {
-    float mc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      mc[nt] = n_open > 0 ? chunk_max<false>(acc[nt], kb, kend, last_key[nt], scale_log2, g)
-                          : chunk_max<true>(acc[nt], kb, kend, last_key[nt], scale_log2, g);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) rescale_lazy<NO>(mc[nt], m[nt], l[nt], o[nt]);
+    const float mc = n_open > 0 ? chunk_max32<false>(acc, kb, kend, last_key, scale_log2, h)
+                                : chunk_max32<true>(acc, kb, kend, last_key, scale_log2, h);
+    rescale_lazy32<NDT>(mc, m, l, o);
   }
 
   // step st < nsteps - 1: tile st is in LDS buffer cur with its scores (masked) in acc and its
@@ -869,28 +922,20 @@ void prefill_kernel(
     constexpr int P = decltype(parity_tag)::value;
     fetch(Int<1 - P>{}, min(st + 3, last_tile), base_a);
     fetch_bases(min(st + 4, last_tile), base_b);
-    f32x4 acc_n[NT][2];
+    f32x16 acc_n;
     qk(nxt, acc_n);
-    bf16x8 pb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) pb[nt] = chunk_exp(acc[nt], scale_log2, m[nt], l[nt]);
+    bf16x8 pb[2];
+    chunk_exp32(acc, scale_log2, m, l, pb);
     pv(cur, pb);
-    float mc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      mc[nt] = chunk_max<MASK_NEXT>(acc_n[nt], kb + (st + 1) * KS, kend, last_key[nt], scale_log2, g);
+    const float mc = chunk_max32<MASK_NEXT>(acc_n, kb + (st + 1) * KS, kend, last_key, scale_log2, h);
     stash(Int<P>{}, fil, min(st + 2, last_tile));
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps)
 #pragma unroll
       for (int gi = 0; gi < GPP; ++gi) base_a[ps][gi] = base_b[ps][gi];
     __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      rescale_lazy<NO>(mc[nt], m[nt], l[nt], o[nt]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[nt][j] = acc_n[nt][j];
-    }
+    rescale_lazy32<NDT>(mc, m, l, o);
+    acc = acc_n;
     const int t = cur;
     cur = nxt;
     nxt = fil;
@@ -909,45 +954,48 @@ void prefill_kernel(
   run(Tag<false>{}, n_open - 1);
   run(Tag<true>{}, nsteps - 1);
   {
-    bf16x8 pb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) pb[nt] = chunk_exp(acc[nt], scale_log2, m[nt], l[nt]);
+    bf16x8 pb[2];
+    chunk_exp32(acc, scale_log2, m, l, pb);
     pv(cur, pb);
   }
 
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) l[nt] = group_sum(l[nt]);  // row sums (all lanes take part)
+  l = pair_sum(l);  // the row's sum (all lanes take part)
   if (ns > 1 && part == 0 && kvh == 0)  // the merge finds this tile's tokens by their count
     for (int i = tid; i < tok_end - tok0; i += kPrefillWaves * 64) nsplit_tok[q0 + tok0 + i] = ns;
-  // normalise and store: lane (n, g) holds row n, dims (D/4)g + 4jt + i (D/4 contiguous dims);
-  // a part of a split tile stores fp32 o and its lse
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int R = wave * (16 * NT) + nt * 16 + n;
+  // normalise and store: lane l holds query row R = 32 wave + l % 32, dims
+  // 32dt + 8(i / 4) + 4h + i % 4 of tile dt; a part of a split tile stores fp32 o and its lse
+  {
+    const int R = wave * 32 + n32;
     const int qi = tok0 + R / G, hh = R - (R / G) * G;
-    if (qi >= tok_end) continue;
-    const int64_t row = (int64_t)(q0 + qi) * Hq + kvh * G + hh;
-    if (ns > 1) {
-      const bool empty = !(l[nt] > 0.f);  // no visible key in this part
-      const float inv = empty ? 0.f : 1.f / l[nt];
-      const int64_t pb = row * maxs + part;
-      float* dst = o_pre + pb * D + (D / 4) * g;
+    if (qi < tok_end) {
+      const int64_t row = (int64_t)(q0 + qi) * Hq + kvh * G + hh;
+      if (ns > 1) {
+        const bool empty = !(l > 0.f);  // no visible key in this part
+        const float inv = empty ? 0.f : 1.f / l;
+        const int64_t pb = row * maxs + part;
+        float* dst = o_pre + pb * D + 4 * h;
 #pragma unroll
-      for (int jt = 0; jt < NO; ++jt)
-        *reinterpret_cast<float4*>(dst + 4 * jt) =
-            make_float4(o[nt][jt][0] * inv, o[nt][jt][1] * inv, o[nt][jt][2] * inv, o[nt][jt][3] * inv);
-      if (g == 0) lse_pre[pb] = empty ? -INFINITY : (m[nt] + __log2f(l[nt])) * kLn2;
-      continue;
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<float4*>(dst + 32 * dt + 8 * g4) =
+                make_float4(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv, o[dt][4 * g4 + 2] * inv,
+                            o[dt][4 * g4 + 3] * inv);
+        if (h == 0) lse_pre[pb] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+      } else {
+        const float inv = 1.f / l;
+        __bf16* dst = out + row * D + 4 * h;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            __bf16 r4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r4[i] = (__bf16)(o[dt][4 * g4 + i] * inv);
+            *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * g4) = __builtin_bit_cast(uint2, r4);
+          }
+      }
     }
-    const float inv = 1.f / l[nt];
-    __bf16 r[D / 4];
-#pragma unroll
-    for (int jt = 0; jt < NO; ++jt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[4 * jt + i] = (__bf16)(o[nt][jt][i] * inv);
-    uint4* dst = reinterpret_cast<uint4*>(out + row * D + (D / 4) * g);
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) dst[c] = __builtin_bit_cast(uint4, *reinterpret_cast<const bf16x8*>(&r[8 * c]));
   }
 }
 
