@@ -689,7 +689,12 @@ constexpr int kPrefillBufs = 3;   // LDS tiles: being computed, ready, being fil
 
 template <int D>
 struct PrefillSmem {
-  static constexpr int STRIDE = D + 8;  // bf16 per LDS row (16-byte pad)
+  // bf16 per LDS row. A V^T transposing read takes 8 bytes from each of 4 consecutive rows per
+  // 16-lane group, a K fragment read 16 bytes from each of 16 consecutive rows. Measured on
+  // gfx950, rows 76 words apart (D = 128, 48-byte pad) let the transposing reads run at the rate
+  // of contiguous 8-byte reads, while 68 words (16-byte pad) halve it; the K reads run at the
+  // contiguous 16-byte rate with either. For D = 64, rows 36 words apart keep both apart too.
+  static constexpr int STRIDE = D == 128 ? D + 24 : D + 8;
   __bf16 k[kPrefillBufs][kPrefillKeys][STRIDE];
   __bf16 v[kPrefillBufs][kPrefillKeys][STRIDE];
 };
@@ -787,14 +792,14 @@ void prefill_kernel(
   int w0 = kb / bs;
   int win = w0 + lane < nbt ? bt_row[w0 + lane] : 0;
   asm volatile("" : : "v"(win));
-  auto group_base = [&](int step, int ps, int grp) -> int64_t {
+  auto group_base = [&](int step, int ps, int grp) __attribute__((always_inline)) -> int64_t {
     const int key = kb + step * KS + ps * RPP + 16 * grp;
     if (key >= kend) return -1;
     const int blk = __builtin_amdgcn_readlane(win, key / bs - w0);
     return ((int64_t)blk * bs + key % bs) * Hkv + kvh;
   };
   // keep the blocks of tile `step` inside the window (tiles are visited in increasing order)
-  auto slide_window = [&](int step) {
+  auto slide_window = [&](int step) __attribute__((always_inline)) {
     const int k_last = min(kb + step * KS + KS, kend) - 1;
     if (k_last / bs >= w0 + 64) {  // wave-uniform
       w0 = (kb + step * KS) / bs;
@@ -803,7 +808,7 @@ void prefill_kernel(
       asm volatile("" : : "v"(win));
     }
   };
-  auto fetch_bases = [&](int step, int64_t (&base)[PASSES][GPP]) {
+  auto fetch_bases = [&](int step, int64_t (&base)[PASSES][GPP]) __attribute__((always_inline)) {
     slide_window(step);
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps)
@@ -817,7 +822,7 @@ void prefill_kernel(
   uint4 rk[2][PASSES], rv[2][PASSES];
   // Load tile `step` into register set X. Groups past kend read the tile's first group instead
   // (always valid); those rows are zeroed when stored.
-  auto fetch = [&](auto set_tag, int step, const int64_t (&base)[PASSES][GPP]) {
+  auto fetch = [&](auto set_tag, int step, const int64_t (&base)[PASSES][GPP]) __attribute__((always_inline)) {
     constexpr int X = decltype(set_tag)::value;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
@@ -833,7 +838,7 @@ void prefill_kernel(
   };
   // Store register set X (tile `step`) to LDS buffer buf. In the last tile, rows at or past kend
   // are stored as zero, so that a masked probability (0) never meets an unwritten V value.
-  auto stash = [&](auto set_tag, int buf, int step) {
+  auto stash = [&](auto set_tag, int buf, int step) __attribute__((always_inline)) {
     constexpr int X = decltype(set_tag)::value;
     if (kb + (step + 1) * KS > kend) {  // wave-uniform
 #pragma unroll
@@ -851,7 +856,7 @@ void prefill_kernel(
   };
 
   // S^T = K Q^T of LDS tile `buf`: A = K rows (lane l: key l % 32, dims [16kk + 8h, +8))
-  auto qk = [&](int buf, f32x16& acc) {
+  auto qk = [&](int buf, f32x16& acc) __attribute__((always_inline)) {
     acc = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -865,7 +870,7 @@ void prefill_kernel(
   // 32dt + 16(group % 2) + 4a .. +3, and lane 4a + b receives element b of the four reads: dim
   // 32dt + l % 32, keys 16ks + 8e' + 4h + j, j = 0..3 (slots 4e' + j).
   f32x16 o[NDT];
-  auto pv = [&](int buf, const bf16x8 (&pb)[2]) {
+  auto pv = [&](int buf, const bf16x8 (&pb)[2]) __attribute__((always_inline)) {
     const int r = lane & 15;
     const __bf16* vb = &sm.v[buf][4 * h + (r >> 2)][16 * ((lane >> 4) & 1) + 4 * (r & 3)];
 #pragma unroll
@@ -905,29 +910,88 @@ void prefill_kernel(
   fetch_bases(min(3, last_tile), base_a);
   __syncthreads();
 
-  f32x16 acc;
-  qk(0, acc);
+  // scores of even tiles live in accA, of odd tiles in accB (no copy between steps)
+  f32x16 accA, accB;
+  qk(0, accA);
   {
-    const float mc = n_open > 0 ? chunk_max32<false>(acc, kb, kend, last_key, scale_log2, h)
-                                : chunk_max32<true>(acc, kb, kend, last_key, scale_log2, h);
+    const float mc = n_open > 0 ? chunk_max32<false>(accA, kb, kend, last_key, scale_log2, h)
+                                : chunk_max32<true>(accA, kb, kend, last_key, scale_log2, h);
     rescale_lazy32<NDT>(mc, m, l, o);
   }
 
-  // step st < nsteps - 1: tile st is in LDS buffer cur with its scores (masked) in acc and its
-  // reference max settled; tile st + 1 is in buffer nxt; buffer fil receives tile st + 2 from
-  // register set P = st % 2, and tile st + 3 is loaded into the other set.
+  // step st < nsteps - 1: tile st is in LDS buffer cur with its scores (masked) in accA / accB
+  // by the parity P = st % 2 and its reference max settled; tile st + 1 is in buffer nxt; buffer
+  // fil receives tile st + 2 from register set P, and tile st + 3 is loaded into the other set.
+  // The order of the work is fixed with scheduling barriers: the K fragments of tile st + 1 are
+  // read first; each of the KK score MFMAs of tile st + 1 then follows EPP exponentials and VPP
+  // V^T reads of tile st, so that the VALU work and the LDS reads run under the MFMAs; each of
+  // the 2 NDT output MFMAs of tile st carries part of the max of tile st + 1.
+  constexpr int EPP = 16 / KK;
+  constexpr int VPP = 4 * NDT / KK;
+  constexpr int XPP = 16 / (2 * NDT);
+  static_assert(16 % KK == 0 && (4 * NDT) % KK == 0 && 16 % (2 * NDT) == 0, "step layout");
   int cur = 0, nxt = 1, fil = 2;
-  auto step = [&](auto mask_tag, auto parity_tag, int st) {
+  auto step = [&](auto mask_tag, auto parity_tag, int st) __attribute__((always_inline)) {
     constexpr bool MASK_NEXT = decltype(mask_tag)::value;
     constexpr int P = decltype(parity_tag)::value;
+    const f32x16& acc = P ? accB : accA;
+    f32x16& acc_n = P ? accA : accB;
+    bf16x8 kf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      kf[kk] = *reinterpret_cast<const bf16x8*>(&sm.k[nxt][n32][16 * kk + 8 * h]);
     fetch(Int<1 - P>{}, min(st + 3, last_tile), base_a);
     fetch_bases(min(st + 4, last_tile), base_b);
-    f32x16 acc_n;
-    qk(nxt, acc_n);
+    __builtin_amdgcn_sched_barrier(0);
+    // V^T read j of tile st: key half ks = j / (2 NDT), dim tile dt = (j / 2) % NDT, 8-key half
+    // j % 2 (the operand layout of pv above)
+    const int r = lane & 15;
+    const __bf16* vb = &sm.v[cur][4 * h + (r >> 2)][16 * ((lane >> 4) & 1) + 4 * (r & 3)];
+    s16x4 vr[4 * NDT];
     bf16x8 pb[2];
-    chunk_exp32(acc, scale_log2, m, l, pb);
-    pv(cur, pb);
-    const float mc = chunk_max32<MASK_NEXT>(acc_n, kb + (st + 1) * KS, kend, last_key, scale_log2, h);
+    float rs = 0.f;
+    acc_n = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) {
+        const int i = kk * EPP + e;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m));
+        rs += p;
+        pb[i / 8][i % 8] = (__bf16)p;
+      }
+#pragma unroll
+      for (int v = 0; v < VPP; ++v) {
+        const int j = kk * VPP + v;
+        vr[j] = lds_read_tr16(vb + (16 * (j / (2 * NDT)) + 8 * (j % 2)) * SmemT::STRIDE +
+                              32 * ((j / 2) % NDT));
+      }
+      acc_n = mfma32x32x16(kf[kk], qf[kk], acc_n);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += rs;
+    float mx = -INFINITY;
+    const int k0n = kb + (st + 1) * KS;
+#pragma unroll
+    for (int pc = 0; pc < 2 * NDT; ++pc) {
+      const int ks = pc / NDT, dt = pc % NDT, j = ks * 2 * NDT + 2 * dt;
+      const bf16x8 vt =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(vr[j], vr[j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+      o[dt] = mfma32x32x16(vt, pb[ks], o[dt]);
+#pragma unroll
+      for (int e = 0; e < XPP; ++e) {
+        const int i = pc * XPP + e;
+        if (MASK_NEXT) {
+          const int key = k0n + 8 * (i >> 2) + 4 * h + (i & 3);
+          acc_n[i] = (key < kend && key <= last_key) ? acc_n[i] : -INFINITY;
+        }
+        mx = fmaxf(mx, acc_n[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float mc = mx * scale_log2;
+    // settle the max and the sum here rather than past the branch in stash
+    asm volatile("" : : "v"(mc), "v"(l));
     stash(Int<P>{}, fil, min(st + 2, last_tile));
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps)
@@ -935,7 +999,6 @@ void prefill_kernel(
       for (int gi = 0; gi < GPP; ++gi) base_a[ps][gi] = base_b[ps][gi];
     __syncthreads();
     rescale_lazy32<NDT>(mc, m, l, o);
-    acc = acc_n;
     const int t = cur;
     cur = nxt;
     nxt = fil;
@@ -943,7 +1006,7 @@ void prefill_kernel(
   };
   // steps [st, end) with the register-set parity known at compile time
   int st = 0;
-  auto run = [&](auto mask_tag, int end) {
+  auto run = [&](auto mask_tag, int end) __attribute__((always_inline)) {
     if ((st & 1) && st < end) step(mask_tag, Int<1>{}, st++);
     for (; st + 1 < end; st += 2) {
       step(mask_tag, Int<0>{}, st);
@@ -954,8 +1017,9 @@ void prefill_kernel(
   run(Tag<false>{}, n_open - 1);
   run(Tag<true>{}, nsteps - 1);
   {
+    const f32x16 acc_last = (nsteps - 1) & 1 ? accB : accA;
     bf16x8 pb[2];
-    chunk_exp32(acc, scale_log2, m, l, pb);
+    chunk_exp32(acc_last, scale_log2, m, l, pb);
     pv(cur, pb);
   }
 
