@@ -815,10 +815,11 @@ void prefill_kernel(
 #pragma unroll
       for (int gi = 0; gi < GPP; ++gi) base[ps][gi] = group_base(step, ps, gi);
   };
-  // Two register sets stage tile loads: tile t goes through set t % 2, so the loads of a tile
-  // have two steps to arrive before they are stored to LDS. Every step loads and stores a tile
-  // (past the last tile, the last one again, into a buffer nobody reads), so the number of
-  // loads in flight is the same on every path.
+  // Two register sets stage tile loads: tile t goes through set t % 2. A step first stores its
+  // set to LDS and then reloads that set with the tile two steps on, so the loads of a tile have
+  // two whole steps to arrive. Every step loads and stores a tile (past the last tile, the last
+  // one again, into a buffer nobody reads), so the number of loads in flight is the same on
+  // every path.
   uint4 rk[2][PASSES], rv[2][PASSES];
   // Load tile `step` into register set X. Groups past kend read the tile's first group instead
   // (always valid); those rows are zeroed when stored.
@@ -895,19 +896,21 @@ void prefill_kernel(
   const int nsteps = (kend - kb + KS - 1) / KS;  // >= 1
   const int n_open = min(nsteps, max(0, min(kend, wave_first_last_key + 1) - kb) / KS);
 
-  // prologue: tiles 0 and 1 into LDS, tile 2 into register set 0, bases of tile 3 (tile
-  // indices past the last tile stand for the last tile)
+  // prologue: tiles 0 and 1 into LDS, tiles 2 and 3 into register sets 0 and 1, bases of tile
+  // 4 (tile indices past the last tile stand for the last tile)
   const int last_tile = nsteps - 1;
-  int64_t base_a[PASSES][GPP], base_b[PASSES][GPP];
-  fetch_bases(0, base_a);
-  fetch(Int<0>{}, 0, base_a);
-  fetch_bases(min(1, last_tile), base_b);
-  fetch(Int<1>{}, min(1, last_tile), base_b);
+  int64_t base[PASSES][GPP];
+  fetch_bases(0, base);
+  fetch(Int<0>{}, 0, base);
+  fetch_bases(min(1, last_tile), base);
+  fetch(Int<1>{}, min(1, last_tile), base);
   stash(Int<0>{}, 0, 0);
   stash(Int<1>{}, 1, min(1, last_tile));
-  fetch_bases(min(2, last_tile), base_a);
-  fetch(Int<0>{}, min(2, last_tile), base_a);
-  fetch_bases(min(3, last_tile), base_a);
+  fetch_bases(min(2, last_tile), base);
+  fetch(Int<0>{}, min(2, last_tile), base);
+  fetch_bases(min(3, last_tile), base);
+  fetch(Int<1>{}, min(3, last_tile), base);
+  fetch_bases(min(4, last_tile), base);
   __syncthreads();
 
   // scores of even tiles live in accA, of odd tiles in accB (no copy between steps)
@@ -921,7 +924,7 @@ void prefill_kernel(
 
   // step st < nsteps - 1: tile st is in LDS buffer cur with its scores (masked) in accA / accB
   // by the parity P = st % 2 and its reference max settled; tile st + 1 is in buffer nxt; buffer
-  // fil receives tile st + 2 from register set P, and tile st + 3 is loaded into the other set.
+  // fil receives tile st + 2 from register set P, which then receives tile st + 4.
   // The order of the work is fixed with scheduling barriers: the K fragments of tile st + 1 are
   // read first; each of the KK score MFMAs of tile st + 1 then follows EPP exponentials and VPP
   // V^T reads of tile st, so that the VALU work and the LDS reads run under the MFMAs; each of
@@ -940,8 +943,9 @@ void prefill_kernel(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       kf[kk] = *reinterpret_cast<const bf16x8*>(&sm.k[nxt][n32][16 * kk + 8 * h]);
-    fetch(Int<1 - P>{}, min(st + 3, last_tile), base_a);
-    fetch_bases(min(st + 4, last_tile), base_b);
+    stash(Int<P>{}, fil, min(st + 2, last_tile));
+    fetch(Int<P>{}, min(st + 4, last_tile), base);
+    fetch_bases(min(st + 5, last_tile), base);
     __builtin_amdgcn_sched_barrier(0);
     // V^T read j of tile st: key half ks = j / (2 NDT), dim tile dt = (j / 2) % NDT, 8-key half
     // j % 2 (the operand layout of pv above)
@@ -990,13 +994,8 @@ void prefill_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     const float mc = mx * scale_log2;
-    // settle the max and the sum here rather than past the branch in stash
+    // settle the max and the sum under the MFMAs rather than after the barrier
     asm volatile("" : : "v"(mc), "v"(l));
-    stash(Int<P>{}, fil, min(st + 2, last_tile));
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps)
-#pragma unroll
-      for (int gi = 0; gi < GPP; ++gi) base_a[ps][gi] = base_b[ps][gi];
     __syncthreads();
     rescale_lazy32<NDT>(mc, m, l, o);
     const int t = cur;
