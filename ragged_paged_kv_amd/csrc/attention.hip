@@ -687,6 +687,24 @@ __device__ inline void chunk_exp32(const f32x16& acc, float c, float m, float& l
 constexpr int kPrefillKeys = 32;  // keys per LDS tile (one barrier per tile)
 constexpr int kPrefillBufs = 3;   // LDS tiles: being computed, ready, being filled
 
+// Division of keys (0 <= key < 2^31) by the block size with a multiply and a shift. With
+// l = ceil(log2 bs) and magic = ceil(2^(31 + l) / bs), which is below 2^32, key / bs equals
+// floor(key * magic / 2^(31 + l)) exactly (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994: the error of the scaled reciprocal stays below 1 / bs).
+// The kernel takes the high 32 bits of the product and shifts them right by l - 1.
+struct BlockDiv {
+  int32_t bs;
+  uint32_t magic;
+  int32_t shift;
+  __device__ int div(int key) const { return (int)(__umulhi((uint32_t)key, magic) >> shift); }
+};
+inline BlockDiv block_div(int32_t bs) {
+  int l = 0;
+  while ((1 << l) < bs) ++l;
+  const uint64_t num = uint64_t{1} << (31 + l);
+  return BlockDiv{bs, (uint32_t)((num + (uint64_t)bs - 1) / (uint64_t)bs), l - 1};
+}
+
 template <int D>
 struct PrefillSmem {
   // bf16 per LDS row. A V^T transposing read takes 8 bytes from each of 4 consecutive rows per
@@ -708,9 +726,10 @@ void prefill_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     __bf16* __restrict__ out, const Work* __restrict__ items, const int32_t* __restrict__ counts,
     float* __restrict__ o_pre, float* __restrict__ lse_pre, int32_t* __restrict__ nsplit_tok,
-    int32_t maxs, int32_t Hq, int32_t Hkv, int32_t bs, int32_t max_blocks_per_seq, int32_t bq,
+    int32_t maxs, int32_t Hq, int32_t Hkv, BlockDiv bdiv, int32_t max_blocks_per_seq, int32_t bq,
     float scale_log2) {
   constexpr int KS = kPrefillKeys;
+  const int bs = bdiv.bs;
   constexpr int KK = D / 16;   // 32x32x16 MFMA k-steps over the head dimension
   constexpr int NDT = D / 32;  // 32-dim output tiles
   constexpr int CPR = D / 8;  // 16-byte chunks per key row
@@ -781,39 +800,32 @@ void prefill_kernel(
   const int ltid = LOADERS < kPrefillWaves * 64 ? tid % LOADERS : tid;
   const int lr = ltid / CPR, lc = ltid - (ltid / CPR) * CPR;
   const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
-  const int64_t lane_off = (int64_t)(lr & 15) * Hkv * D + lc * 8;  // row within group, chunk
-  const int lane_grp = lr >> 4;                                       // group within the pass
-  // cache row (units of D elements) of the first key of 16-key group grp of pass ps of a tile;
-  // groups at or past kend are not read (-1)
+  // The group of a pass that a lane loads is lr / 16 = ltid / (16 CPR): whole waves share it, so
+  // a group's cache address is a scalar and each lane adds a fixed byte offset (row within the
+  // group, chunk).
+  static_assert((16 * CPR) % 64 == 0 && LOADERS % (16 * CPR) == 0, "load groups are wave-uniform");
+  const int lane_grp = __builtin_amdgcn_readfirstlane(lr >> 4);
+  const uint32_t lane_off = ((lr & 15) * Hkv * D + lc * 8) * (uint32_t)sizeof(__bf16);
+  const int64_t row_elems = (int64_t)Hkv * D;  // elements per cache row (token slot)
+  const __bf16* k_head = k_cache + (int64_t)kvh * D;
+  const __bf16* v_head = v_cache + (int64_t)kvh * D;
+  auto blk_of = [&](int key) __attribute__((always_inline)) { return bdiv.div(key); };
   // Block ids come from a window of the sequence's block-table row held in one register: lane i
   // has the entry of block w0 + i. A group's id is read with readlane (no memory wait in the
   // steps); the window moves (one vector load, waited on) once per 64 blocks.
-  const int nbt = (kend + bs - 1) / bs;  // table entries the part reads
-  int w0 = kb / bs;
+  const int nbt = bdiv.div(kend + bs - 1);  // table entries the part reads
+  int w0 = bdiv.div(kb);
   int win = w0 + lane < nbt ? bt_row[w0 + lane] : 0;
   asm volatile("" : : "v"(win));
-  auto group_base = [&](int step, int ps, int grp) __attribute__((always_inline)) -> int64_t {
-    const int key = kb + step * KS + ps * RPP + 16 * grp;
-    if (key >= kend) return -1;
-    const int blk = __builtin_amdgcn_readlane(win, key / bs - w0);
-    return ((int64_t)blk * bs + key % bs) * Hkv + kvh;
-  };
   // keep the blocks of tile `step` inside the window (tiles are visited in increasing order)
   auto slide_window = [&](int step) __attribute__((always_inline)) {
     const int k_last = min(kb + step * KS + KS, kend) - 1;
-    if (k_last / bs >= w0 + 64) {  // wave-uniform
-      w0 = (kb + step * KS) / bs;
+    if (blk_of(k_last) >= w0 + 64) {  // wave-uniform
+      w0 = blk_of(kb + step * KS);
       win = w0 + lane < nbt ? bt_row[w0 + lane] : 0;
       // consume the load here, so that no wait for it is left to the reads in every step
       asm volatile("" : : "v"(win));
     }
-  };
-  auto fetch_bases = [&](int step, int64_t (&base)[PASSES][GPP]) __attribute__((always_inline)) {
-    slide_window(step);
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps)
-#pragma unroll
-      for (int gi = 0; gi < GPP; ++gi) base[ps][gi] = group_base(step, ps, gi);
   };
   // Two register sets stage tile loads: tile t goes through set t % 2. A step first stores its
   // set to LDS and then reloads that set with the tile two steps on, so the loads of a tile have
@@ -821,20 +833,21 @@ void prefill_kernel(
   // one again, into a buffer nobody reads), so the number of loads in flight is the same on
   // every path.
   uint4 rk[2][PASSES], rv[2][PASSES];
-  // Load tile `step` into register set X. Groups past kend read the tile's first group instead
-  // (always valid); those rows are zeroed when stored.
-  auto fetch = [&](auto set_tag, int step, const int64_t (&base)[PASSES][GPP]) __attribute__((always_inline)) {
+  // Load tile `step` into register set X. A group at or past kend reads the tile's first group
+  // instead (always valid); those rows are zeroed when stored.
+  auto fetch = [&](auto set_tag, int step) __attribute__((always_inline)) {
     constexpr int X = decltype(set_tag)::value;
+    slide_window(step);
+    const int t0 = kb + step * KS;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
-      int64_t b = base[ps][0];
-#pragma unroll
-      for (int gi = 1; gi < GPP; ++gi)
-        if (lane_grp == gi) b = base[ps][gi];
-      if (b < 0) b = base[0][0];
-      const int64_t off = b * D + lane_off;
-      rk[X][ps] = *reinterpret_cast<const uint4*>(k_cache + off);
-      rv[X][ps] = *reinterpret_cast<const uint4*>(v_cache + off);
+      int key = t0 + ps * RPP + 16 * lane_grp;
+      if (key >= kend) key = t0;
+      const int bi = blk_of(key);
+      const int blk = __builtin_amdgcn_readlane(win, bi - w0);
+      const int64_t row = (int64_t)(uint32_t)(blk * bs + (key - bi * bs)) * row_elems;
+      rk[X][ps] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(k_head + row) + lane_off);
+      rv[X][ps] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(v_head + row) + lane_off);
     }
   };
   // Store register set X (tile `step`) to LDS buffer buf. In the last tile, rows at or past kend
@@ -896,21 +909,15 @@ void prefill_kernel(
   const int nsteps = (kend - kb + KS - 1) / KS;  // >= 1
   const int n_open = min(nsteps, max(0, min(kend, wave_first_last_key + 1) - kb) / KS);
 
-  // prologue: tiles 0 and 1 into LDS, tiles 2 and 3 into register sets 0 and 1, bases of tile
-  // 4 (tile indices past the last tile stand for the last tile)
+  // prologue: tiles 0 and 1 into LDS, tiles 2 and 3 into register sets 0 and 1 (tile indices
+  // past the last tile stand for the last tile)
   const int last_tile = nsteps - 1;
-  int64_t base[PASSES][GPP];
-  fetch_bases(0, base);
-  fetch(Int<0>{}, 0, base);
-  fetch_bases(min(1, last_tile), base);
-  fetch(Int<1>{}, min(1, last_tile), base);
+  fetch(Int<0>{}, 0);
+  fetch(Int<1>{}, min(1, last_tile));
   stash(Int<0>{}, 0, 0);
   stash(Int<1>{}, 1, min(1, last_tile));
-  fetch_bases(min(2, last_tile), base);
-  fetch(Int<0>{}, min(2, last_tile), base);
-  fetch_bases(min(3, last_tile), base);
-  fetch(Int<1>{}, min(3, last_tile), base);
-  fetch_bases(min(4, last_tile), base);
+  fetch(Int<0>{}, min(2, last_tile));
+  fetch(Int<1>{}, min(3, last_tile));
   __syncthreads();
 
   // scores of even tiles live in accA, of odd tiles in accB (no copy between steps)
@@ -944,8 +951,7 @@ void prefill_kernel(
     for (int kk = 0; kk < KK; ++kk)
       kf[kk] = *reinterpret_cast<const bf16x8*>(&sm.k[nxt][n32][16 * kk + 8 * h]);
     stash(Int<P>{}, fil, min(st + 2, last_tile));
-    fetch(Int<P>{}, min(st + 4, last_tile), base);
-    fetch_bases(min(st + 5, last_tile), base);
+    fetch(Int<P>{}, min(st + 4, last_tile));
     __builtin_amdgcn_sched_barrier(0);
     // V^T read j of tile st: key half ks = j / (2 NDT), dim tile dt = (j / 2) % NDT, 8-key half
     // j % 2 (the operand layout of pv above)
@@ -1445,13 +1451,13 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
     if (head_dim == 128)
       prefill_kernel<128><<<grid, kPrefillWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, o_pre, lse_pre,
-          nsplit_tok, p.pre_splits, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq,
-          p.bq, scale_log2);
+          nsplit_tok, p.pre_splits, num_q_heads, num_kv_heads, block_div(block_size),
+          max_blocks_per_seq, p.bq, scale_log2);
     else
       prefill_kernel<64><<<grid, kPrefillWaves * 64, 0, st>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, pre, counts, o_pre, lse_pre,
-          nsplit_tok, p.pre_splits, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq,
-          p.bq, scale_log2);
+          nsplit_tok, p.pre_splits, num_q_heads, num_kv_heads, block_div(block_size),
+          max_blocks_per_seq, p.bq, scale_log2);
     if (!record_if(tm, CB_KERNEL_PREFILL, false, st)) return fail(CB_ERR_HIP, "hipEventRecord failed");
     // merge the parts of split prefill tiles (tokens of other tiles skip); no tile can split
     // when no sequence is longer than one part

@@ -166,6 +166,10 @@ EDGE = {
     "prefill-only": ([synth.SeqSpec(130, 130), synth.SeqSpec(77, 300)], 32, 8, 128, 16),
     "bs64": ([synth.SeqSpec(1, 200), synth.SeqSpec(50, 150)], 32, 8, 128, 64),
     "bs256": ([synth.SeqSpec(1, 700), synth.SeqSpec(100, 600)], 32, 8, 128, 256),
+    # block sizes that are not powers of two (keys divided by multiply and shift), with more
+    # than 64 blocks per sequence so that the prefill block-id window moves
+    "bs48-long": ([synth.SeqSpec(1, 3500), synth.SeqSpec(150, 4000)], 32, 8, 128, 48),
+    "bs80-d64": ([synth.SeqSpec(1, 900), synth.SeqSpec(90, 5300)], 16, 2, 64, 80),
     "long-chunk-offset": ([synth.SeqSpec(200, 1500)], 32, 8, 128, 16),
     # prefill tiles split along the keys (few tiles, long contexts): 4 parts, uneven rounding,
     # head_dim 64, 256-row tiles of one head, and next to decodes and a short prompt
