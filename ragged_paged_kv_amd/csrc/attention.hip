@@ -389,6 +389,24 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Division of keys (0 <= key < 2^31) by the block size with a multiply and a shift. With
+// l = ceil(log2 bs) and magic = ceil(2^(31 + l) / bs), which is below 2^32, key / bs equals
+// floor(key * magic / 2^(31 + l)) exactly (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994: the error of the scaled reciprocal stays below 1 / bs).
+// The kernel takes the high 32 bits of the product and shifts them right by l - 1.
+struct BlockDiv {
+  int32_t bs;
+  uint32_t magic;
+  int32_t shift;
+  __device__ int div(int key) const { return (int)(__umulhi((uint32_t)key, magic) >> shift); }
+};
+inline BlockDiv block_div(int32_t bs) {
+  int l = 0;
+  while ((1 << l) < bs) ++l;
+  const uint64_t num = uint64_t{1} << (31 + l);
+  return BlockDiv{bs, (uint32_t)((num + (uint64_t)bs - 1) / (uint64_t)bs), l - 1};
+}
+
 // ---------------------------------------------------------------------------------------------
 // Decode / split-KV kernel. Persistent waves, each working alone: a wave takes one
 // (KV partition, KV head) item at a time from a queue and streams its keys 32 at a time. K/V
@@ -408,23 +426,23 @@ __device__ inline u32x2 ld_stream8(const void* p) {
 // of key 16 j + n, so one instruction covers 64 contiguous bytes of each of 16 key rows and the
 // next one completes each 128-byte line: ordinary cached loads. V: lane (c = n, g) reads chunk n
 // of key 16 (e / 4) + 4 g + e % 4, whole 256-byte rows per instruction: streaming loads.
-// row_j = (block_j * bs + offset_j) * Hkv + kvh is the cache row of the first key of group j.
+// base_j (wave-uniform) is the cache address of the first key of group j at this KV head; a
+// lane adds its fixed byte offsets: koff for K (key n, dims 8 g) and voff[i] for V (key 4 g + i,
+// chunk n).
 template <int D>
 __device__ inline void load_step(KVFrag<D>& f, const __bf16* __restrict__ kc,
-                                 const __bf16* __restrict__ vc, int64_t row0, int64_t row1,
-                                 int Hkv, int n, int g) {
+                                 const __bf16* __restrict__ vc, int64_t base0, int64_t base1,
+                                 uint32_t koff, const uint32_t (&voff)[4]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int64_t r = (j ? row1 : row0) + (int64_t)n * Hkv;
-    const __bf16* p = kc + r * D + 8 * g;
+    const char* p = reinterpret_cast<const char*>(kc + (j ? base1 : base0)) + koff;
 #pragma unroll
     for (int kk = 0; kk < KVFrag<D>::KSTEPS; ++kk)
-      f.k[j][kk] = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
+      f.k[j][kk] = *reinterpret_cast<const bf16x8*>(p + 64 * kk);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int64_t r = ((e >> 2) ? row1 : row0) + (int64_t)(4 * g + (e & 3)) * Hkv;
-    const __bf16* p = vc + r * D + n * (D / 16);
+    const char* p = reinterpret_cast<const char*>(vc + ((e >> 2) ? base1 : base0)) + voff[e & 3];
     if constexpr (D == 128) {
       const u32x4 x = ld_stream16(p);
       f.v[e][0] = x.x; f.v[e][1] = x.y; f.v[e][2] = x.z; f.v[e][3] = x.w;
@@ -482,7 +500,7 @@ void decode_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     __bf16* __restrict__ out, float* __restrict__ o_part, float* __restrict__ lse_part,
     const Work* __restrict__ items, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ queue, int32_t Hq, int32_t Hkv, int32_t bs,
+    int32_t* __restrict__ queue, int32_t Hq, int32_t Hkv, BlockDiv bdiv,
     int32_t max_blocks_per_seq, int32_t P, int32_t max_splits, int32_t qmaxd,
     float scale_log2) {
   constexpr int KSTEPS = D / 32;
@@ -491,6 +509,13 @@ void decode_kernel(
   const int n = lane & 15, g = lane >> 4;
   const int G = Hq / Hkv;
   const int total = counts[0] * Hkv;
+  const int bs = bdiv.bs;
+  // per-lane byte offsets from a group's first cache row (see load_step)
+  const uint32_t row_bytes = (uint32_t)Hkv * D * (uint32_t)sizeof(__bf16);
+  const uint32_t koff = n * row_bytes + 16 * g;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (4 * g + i) * row_bytes + n * (D / 16) * (uint32_t)sizeof(__bf16);
 
   // Each wave pulls (partition, KV head) items until the queue is exhausted; every wave leaves
   // the loop once the shared counter passes `total`.
@@ -513,8 +538,8 @@ void decode_kernel(
 
     // block-table entries of this partition, one per lane
     const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
-    const int jb0 = kb / bs;
-    const int nbt = (ke + bs - 1) / bs - jb0;
+    const int jb0 = bdiv.div(kb);
+    const int nbt = bdiv.div(ke + bs - 1) - jb0;
     int bt[3];
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
@@ -544,24 +569,25 @@ void decode_kernel(
     for (int t = 0; t < NO; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int first_last_key = L - qn;  // last visible key of the item's first token
 
-    // cache row (units of D elements) of the first key of the 16-key group starting at key k;
+    // element offset of the first key of the 16-key group starting at key k, at this KV head;
     // groups wholly past the range end alias the first group (loaded, then masked)
     auto group_row = [&](int k) -> int64_t {
       const int kk = k < ke ? k : kb;
-      const int blk = block_of(bt, kk / bs - jb0);
-      return ((int64_t)blk * bs + (kk % bs)) * Hkv + kvh;
+      const int bi = bdiv.div(kk);
+      const int blk = block_of(bt, bi - jb0);
+      return ((int64_t)(uint32_t)(blk * bs + (kk - bi * bs)) * Hkv + kvh) * D;
     };
 
     int k0 = kb;
     KVFrag<D> fa, fb;
-    load_step<D>(fa, k_cache, v_cache, group_row(k0), group_row(k0 + 16), Hkv, n, g);
+    load_step<D>(fa, k_cache, v_cache, group_row(k0), group_row(k0 + 16), koff, voff);
     while (true) {
       const int k1 = k0 + 32;
-      if (k1 < ke) load_step<D>(fb, k_cache, v_cache, group_row(k1), group_row(k1 + 16), Hkv, n, g);
+      if (k1 < ke) load_step<D>(fb, k_cache, v_cache, group_row(k1), group_row(k1 + 16), koff, voff);
       compute_step<D>(fa, qf, k0, ke, last_key, first_last_key, scale_log2, g, m, l, o);
       if (k1 >= ke) break;
       const int k2 = k1 + 32;
-      if (k2 < ke) load_step<D>(fa, k_cache, v_cache, group_row(k2), group_row(k2 + 16), Hkv, n, g);
+      if (k2 < ke) load_step<D>(fa, k_cache, v_cache, group_row(k2), group_row(k2 + 16), koff, voff);
       compute_step<D>(fb, qf, k1, ke, last_key, first_last_key, scale_log2, g, m, l, o);
       if (k2 >= ke) break;
       k0 = k2;
@@ -686,24 +712,6 @@ __device__ inline void chunk_exp32(const f32x16& acc, float c, float m, float& l
 
 constexpr int kPrefillKeys = 32;  // keys per LDS tile (one barrier per tile)
 constexpr int kPrefillBufs = 3;   // LDS tiles: being computed, ready, being filled
-
-// Division of keys (0 <= key < 2^31) by the block size with a multiply and a shift. With
-// l = ceil(log2 bs) and magic = ceil(2^(31 + l) / bs), which is below 2^32, key / bs equals
-// floor(key * magic / 2^(31 + l)) exactly (Granlund and Montgomery, "Division by invariant
-// integers using multiplication", 1994: the error of the scaled reciprocal stays below 1 / bs).
-// The kernel takes the high 32 bits of the product and shifts them right by l - 1.
-struct BlockDiv {
-  int32_t bs;
-  uint32_t magic;
-  int32_t shift;
-  __device__ int div(int key) const { return (int)(__umulhi((uint32_t)key, magic) >> shift); }
-};
-inline BlockDiv block_div(int32_t bs) {
-  int l = 0;
-  while ((1 << l) < bs) ++l;
-  const uint64_t num = uint64_t{1} << (31 + l);
-  return BlockDiv{bs, (uint32_t)((num + (uint64_t)bs - 1) / (uint64_t)bs), l - 1};
-}
 
 template <int D>
 struct PrefillSmem {
@@ -1485,12 +1493,12 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
     if (head_dim == 128)
       decode_kernel<128><<<grid, kDecodeWaves * 64, 0, dst>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
-          queue, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits,
+          queue, num_q_heads, num_kv_heads, block_div(block_size), max_blocks_per_seq, p.P, p.max_splits,
           p.qmaxd, scale_log2);
     else
       decode_kernel<64><<<grid, kDecodeWaves * 64, 0, dst>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
-          queue, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, p.P, p.max_splits,
+          queue, num_q_heads, num_kv_heads, block_div(block_size), max_blocks_per_seq, p.P, p.max_splits,
           p.qmaxd, scale_log2);
     if (!record_if(tm, CB_KERNEL_DECODE, false, dst)) return fail(CB_ERR_HIP, "hipEventRecord failed");
   }
