@@ -66,10 +66,14 @@ def work_of(b):
     # decode kernel alone: the decode rows' K/V, q and output rows, block-table entries
     dec_bytes = int((L[decode] * kv_tok).sum() + 2 * q[decode].sum() * Hq * D * 2
                     + 4 * blocks[decode].sum())
+    # prefill kernel alone: each prefill row's K/V once, its q and output rows, table entries
+    pre_bytes = int((L[~decode] * kv_tok).sum() + 2 * q[~decode].sum() * Hq * D * 2
+                    + 4 * blocks[~decode].sum())
     return {
         "T": T, "S": S,
         "kv_bytes": kv_bytes,
         "decode_kernel_bytes": dec_bytes,
+        "prefill_kernel_bytes": pre_bytes,
         "attn_bytes": int(attn),
         "step_bytes": int(attn + write + slots),
         "attn_flops": int((4 * D * Hq * pairs).sum()),
@@ -280,7 +284,10 @@ def copy_calibration():
     log(f"[bench] copied {COPY_BYTES} bytes 5 times")
 
 
-def _pmc_means(d, counter, name_part):
+def _pmc_means(d, counter, name_part, last_group=False):
+    """Mean of a counter per dispatch of the kernel named like name_part. last_group: only the
+    final run of dispatches with the grid size of the last one (the prefill chunks alone, which
+    the bench launches after the full steps and times for the MFMA roofline)."""
     import csv
     import collections
     vals = collections.defaultdict(list)
@@ -290,10 +297,19 @@ def _pmc_means(d, counter, name_part):
     for f in files:
         for row in csv.DictReader(open(f)):
             if row["Counter_Name"] == counter and name_part in row["Kernel_Name"]:
-                vals[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+                vals[row["Kernel_Name"]].append(
+                    (int(row["Dispatch_Id"]), row["Grid_Size"], float(row["Counter_Value"])))
     if not vals:
         raise SystemExit(f"no {counter} rows for a kernel named like {name_part!r} under {d}")
-    name, v = max(vals.items(), key=lambda kv: sum(kv[1]) / len(kv[1]))
+    name, rows = max(vals.items(), key=lambda kv: sum(r[2] for r in kv[1]) / len(kv[1]))
+    rows.sort()
+    if last_group:
+        grid = rows[-1][1]
+        i = len(rows)
+        while i > 0 and rows[i - 1][1] == grid:
+            i -= 1
+        rows = rows[i:]
+    v = [r[2] for r in rows]
     return name, sum(v) / len(v), len(v)
 
 
@@ -302,8 +318,9 @@ def traffic_summary(args):
     import synth
     b = synth.make_config(args.config)
     kname = "decode_kernel" if args.config in DECODE_CONFIGS else "prefill_kernel"
-    kn, fetch_kib, nf = _pmc_means(fetch_dir, "FETCH_SIZE", kname)
-    _, write_kib, nw = _pmc_means(write_dir, "WRITE_SIZE", kname)
+    alone = kname == "prefill_kernel"
+    kn, fetch_kib, nf = _pmc_means(fetch_dir, "FETCH_SIZE", kname, last_group=alone)
+    _, write_kib, nw = _pmc_means(write_dir, "WRITE_SIZE", kname, last_group=alone)
     cn, cfetch_kib, _ = _pmc_means(cfetch_dir, "FETCH_SIZE", "")
     _, cwrite_kib, _ = _pmc_means(cwrite_dir, "WRITE_SIZE", cn[:40])
     f_fetch = COPY_BYTES / 1024 / cfetch_kib
@@ -311,11 +328,13 @@ def traffic_summary(args):
     fetch_b = fetch_kib * 1024 * f_fetch
     write_b = write_kib * 1024 * f_write
     w = work_of(b)
-    alg = w["decode_kernel_bytes"] if kname == "decode_kernel" else None
+    alg = w["decode_kernel_bytes"] if kname == "decode_kernel" else w["prefill_kernel_bytes"]
     rec = {
         "workload": b.name, "kernel": kn, "attention_hip_sha256": attention_source_sha256(),
         "fetch_kib_per_launch": round(fetch_kib, 1), "write_kib_per_launch": round(write_kib, 1),
         "launches": [nf, nw],
+        "launches_measured": "the prefill chunks alone (the launches the MFMA roofline times)"
+        if alone else "every launch of the decode kernel",
         "copy_kernel": cn, "copy_bytes": COPY_BYTES,
         "copy_fetch_kib": round(cfetch_kib, 1), "copy_write_kib": round(cwrite_kib, 1),
         "fetch_scale": round(f_fetch, 5), "write_scale": round(f_write, 5),
