@@ -917,6 +917,16 @@ void prefill_kernel(
   const int nsteps = (kend - kb + KS - 1) / KS;  // >= 1
   const int n_open = min(nsteps, max(0, min(kend, wave_first_last_key + 1) - kb) / KS);
 
+  // The two waves of a SIMD run half a step apart: a step is an issue-bound half (score MFMAs
+  // with the exponentials) and an MFMA-bound half (output MFMAs with the max), and group A runs
+  // them in that order before the step's barrier while group B passes the barrier between them,
+  // so that one wave's first half meets the other's second half. The group is the wave's rank
+  // among the waves of its SIMD (hardware id register), exchanged through LDS.
+  __shared__ int wave_simd[kPrefillWaves];
+  const int my_simd = __builtin_amdgcn_readfirstlane(
+      (int)__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4));  // HW_ID bits 5:4 (SIMD)
+  if (lane == 0) wave_simd[wave] = my_simd;
+
   // prologue: tiles 0 and 1 into LDS, tiles 2 and 3 into register sets 0 and 1 (tile indices
   // past the last tile stand for the last tile)
   const int last_tile = nsteps - 1;
@@ -927,6 +937,9 @@ void prefill_kernel(
   fetch(Int<0>{}, min(2, last_tile));
   fetch(Int<1>{}, min(3, last_tile));
   __syncthreads();
+  int grp = 0;
+  for (int w = 0; w < wave; ++w) grp |= wave_simd[w] == my_simd;
+  grp = __builtin_amdgcn_readfirstlane(grp);
 
   // scores of even tiles live in accA, of odd tiles in accB (no copy between steps)
   f32x16 accA, accB;
@@ -949,8 +962,11 @@ void prefill_kernel(
   constexpr int XPP = 16 / (2 * NDT);
   static_assert(16 % KK == 0 && (4 * NDT) % KK == 0 && 16 % (2 * NDT) == 0, "step layout");
   int cur = 0, nxt = 1, fil = 2;
-  auto step = [&](auto mask_tag, auto parity_tag, int st) __attribute__((always_inline)) {
-    constexpr bool MASK_NEXT = decltype(mask_tag)::value;
+  // carried from the first half of a step to the second: V^T fragments and probabilities of
+  // tile st (the second half's operands)
+  s16x4 vr[4 * NDT];
+  bf16x8 pb[2];
+  auto half1 = [&](auto parity_tag, int st) __attribute__((always_inline)) {
     constexpr int P = decltype(parity_tag)::value;
     const f32x16& acc = P ? accB : accA;
     f32x16& acc_n = P ? accA : accB;
@@ -965,8 +981,6 @@ void prefill_kernel(
     // j % 2 (the operand layout of pv above)
     const int r = lane & 15;
     const __bf16* vb = &sm.v[cur][4 * h + (r >> 2)][16 * ((lane >> 4) & 1) + 4 * (r & 3)];
-    s16x4 vr[4 * NDT];
-    bf16x8 pb[2];
     float rs = 0.f;
     acc_n = f32x16{};
 #pragma unroll
@@ -988,6 +1002,11 @@ void prefill_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     l += rs;
+  };
+  auto half2 = [&](auto mask_tag, auto parity_tag, int st) __attribute__((always_inline)) {
+    constexpr bool MASK_NEXT = decltype(mask_tag)::value;
+    constexpr int P = decltype(parity_tag)::value;
+    f32x16& acc_n = P ? accA : accB;
     float mx = -INFINITY;
     const int k0n = kb + (st + 1) * KS;
 #pragma unroll
@@ -1008,14 +1027,18 @@ void prefill_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     const float mc = mx * scale_log2;
-    // settle the max and the sum under the MFMAs rather than after the barrier
-    asm volatile("" : : "v"(mc), "v"(l));
-    __syncthreads();
     rescale_lazy32<NDT>(mc, m, l, o);
     const int t = cur;
     cur = nxt;
     nxt = fil;
     fil = t;
+  };
+  // one barrier per step for every wave: group B's between the halves, group A's after them
+  auto step = [&](auto mask_tag, auto parity_tag, int st) __attribute__((always_inline)) {
+    half1(parity_tag, st);
+    if (grp) __syncthreads();
+    half2(mask_tag, parity_tag, st);
+    if (!grp) __syncthreads();
   };
   // steps [st, end) with the register-set parity known at compile time
   int st = 0;
