@@ -688,15 +688,22 @@ __device__ inline void rescale_lazy32(float m_lane, float& m, float& l, f32x16 (
 
 // P^T operands of the chunk's two 16-key halves: slot e of half ks is key
 // k0 + 16ks + 8(e / 4) + 4h + e % 4, i.e. accumulator 8ks + e.
+// Adds a pair of bf16 probabilities to a row sum (one dot-product instruction against (1, 1)).
+// The sum is taken over the bf16 values that the P V MFMAs multiply, so that the output's
+// weights add up to one.
+__device__ inline float add_pair(float s, __bf16 a, __bf16 b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 pr = {a, b}, one = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
+}
 __device__ inline void chunk_exp32(const f32x16& acc, float c, float m, float& l, bf16x8 (&pb)[2]) {
   float rs = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[8 * ks + e], c, -m));
-      rs += p;
-      pb[ks][e] = (__bf16)p;
+      pb[ks][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(acc[8 * ks + e], c, -m));
+      if (e & 1) rs = add_pair(rs, pb[ks][e - 1], pb[ks][e]);
     }
   l += rs;
 }
@@ -988,9 +995,8 @@ void prefill_kernel(
 #pragma unroll
       for (int e = 0; e < EPP; ++e) {
         const int i = kk * EPP + e;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m));
-        rs += p;
-        pb[i / 8][i % 8] = (__bf16)p;
+        pb[i / 8][i % 8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m));
+        if (e & 1) rs = add_pair(rs, pb[i / 8][i % 8 - 1], pb[i / 8][i % 8]);
       }
 #pragma unroll
       for (int v = 0; v < VPP; ++v) {
