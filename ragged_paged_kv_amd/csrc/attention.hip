@@ -65,11 +65,16 @@ constexpr int kPrefillTiles = CB_PREFILL_TILES;  // 16-row MFMA tiles per prefil
 constexpr int kPrefillRows = kPrefillWaves * 16 * kPrefillTiles;  // query rows (token x head) per tile
 // two waves per SIMD at two row tiles per wave; with more, the wave needs the whole register file
 constexpr int kPrefillWavesPerSimd = kPrefillTiles > 2 ? 1 : 2;
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWaves = 8;  // waves per decode workgroup beside prefill work (4 otherwise)
 
 struct Work {
   int32_t seq;
-  int32_t idx;  // KV partition (decode) or query tile (prefill)
+  int32_t idx;  // query tile (prefill)
+};
+// A decode item carries what its wave needs to start (one 32-byte scalar load): sequence, KV
+// partition, first query row, query rows, KV length.
+struct alignas(32) DecWork {
+  int32_t seq, split, q0, qn, L, pad0, pad1, pad2;
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -223,8 +228,8 @@ constexpr int kPrefillSplitKeys = 1024;
 // Splitting pays only when the longest prefill tile would outlast the batch's decode work, which
 // otherwise fills the compute units that the long tiles leave idle (the two kernels run side by
 // side). Estimated from measured rates on this GPU: one 32-key step of a prefill workgroup takes
-// about 1.4 us, and the decode kernel streams about 5.5 GB/ms.
-constexpr float kPrefillStepUs = 1.4f;
+// about 1.0 us, and the decode kernel streams about 5.5 GB/ms.
+constexpr float kPrefillStepUs = 1.0f;
 constexpr float kDecodeBytesPerUs = 5.5e6f;
 
 __device__ inline void prefill_split(int kend, int emax, int& ns, int& chunk) {
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int32_t num_seqs, int32_t G, int32_t P,
                                                     int32_t qmaxd, int32_t max_splits,
                                                     int32_t bq, int32_t bs, int32_t max_blocks,
-                                                    int32_t max_kv, Work* __restrict__ dec,
+                                                    int32_t max_kv, DecWork* __restrict__ dec,
                                                     int64_t dec_cap, Work* __restrict__ pre,
                                                     int64_t pre_cap, int32_t* __restrict__ counts,
                                                     int32_t Hkv, int32_t cus, int32_t maxs,
@@ -271,6 +276,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   __shared__ int32_t base[2];
   __shared__ int32_t split_on;
   __shared__ unsigned long long dec_keys;  // sum of decode sequences' lengths
+  __shared__ unsigned long long pre_steps; // 32-key steps of all prefill tiles (one KV head)
   __shared__ int32_t max_pre_len;          // longest prefill sequence (its last tile's keys)
   __shared__ int32_t tail_count[kTailBuckets];
   __shared__ int32_t tail_next[kTailBuckets];
@@ -278,6 +284,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (tid == 0) {
     base[0] = base[1] = 0;
     dec_keys = 0;
+    pre_steps = 0;
     max_pre_len = 0;
   }
   if (tid < kTailBuckets) tail_count[tid] = tail_next[tid] = 0;
@@ -292,7 +299,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
               rem, np);
     if (rem > 0) atomicAdd(&tail_count[(P - rem) * kTailBuckets / P], 1);
     if (nfull + rem > 0) atomicAdd(&dec_keys, (unsigned long long)(nfull * P + rem));
-    if (np > 0) atomicMax(&max_pre_len, kv_lens[s]);
+    if (np > 0) {
+      atomicMax(&max_pre_len, kv_lens[s]);
+      const int qn = cu[s + 1] - cu[s], L = kv_lens[s];
+      unsigned long long stp = 0;
+      for (int t = 0; t < np; ++t) stp += (L - qn + min(qn, (t + 1) * bq) + 31) / 32;
+      atomicAdd(&pre_steps, stp);
+    }
     sd[tid] = nfull;
     sp[tid] = np;
     __syncthreads();
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     }
     const int64_t ed = (int64_t)base[0] + sd[tid] - nfull;
     for (int k = 0; k < nfull; ++k)
-      if (ed + k < dec_cap) dec[ed + k] = Work{s, k};
+      if (ed + k < dec_cap) dec[ed + k] = DecWork{s, k, cu[s], cu[s + 1] - cu[s], kv_lens[s], 0, 0, 0};
     __syncthreads();
     if (tid == 1023) {
       base[0] += sd[1023];
@@ -328,6 +341,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     split_on = (maxs > 1 && (int64_t)base[1] * Hkv < 2 * (int64_t)cus && t_longest > t_decode)
                    ? 1 : 0;  // split prefill tiles
     counts[3] = split_on;
+    // Compute units for the decode kernel when it runs beside the prefill kernel (one workgroup
+    // each): its share of the estimated work, at least half of them (below that its streaming
+    // rate drops). Without prefill work every workgroup of the decode grid works.
+    const float t_prefill = (float)pre_steps * Hkv * kPrefillStepUs / cus;
+    int n_dec = 1 << 30;
+    if (t_prefill > 0.f && t_decode > 0.f)
+      n_dec = max(cus / 2, min(cus, (int)(cus * t_decode / (t_decode + t_prefill) + 0.5f)));
+    counts[4] = n_dec;
   }
   __syncthreads();
   const int emax = split_on ? maxs : 1;
@@ -384,7 +405,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
               rem, np);
     if (rem > 0) {
       const int64_t pos = atomicAdd(&tail_next[(P - rem) * kTailBuckets / P], 1);
-      if (pos < dec_cap) dec[pos] = Work{s, nfull};
+      if (pos < dec_cap) dec[pos] = DecWork{s, nfull, cu[s], cu[s + 1] - cu[s], kv_lens[s], 0, 0, 0};
     }
   }
 }
@@ -499,7 +520,7 @@ void decode_kernel(
     const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables,
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     __bf16* __restrict__ out, float* __restrict__ o_part, float* __restrict__ lse_part,
-    const Work* __restrict__ items, const int32_t* __restrict__ counts,
+    const DecWork* __restrict__ items, const int32_t* __restrict__ counts,
     int32_t* __restrict__ queue, int32_t Hq, int32_t Hkv, BlockDiv bdiv,
     int32_t max_blocks_per_seq, int32_t P, int32_t max_splits, int32_t qmaxd,
     float scale_log2) {
@@ -510,6 +531,8 @@ void decode_kernel(
   const int G = Hq / Hkv;
   const int total = counts[0] * Hkv;
   const int bs = bdiv.bs;
+  // beside prefill work, only the first counts[4] workgroups (one per compute unit) take items
+  if ((int)blockIdx.x >= counts[4]) return;
   // per-lane byte offsets from a group's first cache row (see load_step)
   const uint32_t row_bytes = (uint32_t)Hkv * D * (uint32_t)sizeof(__bf16);
   const uint32_t koff = n * row_bytes + 16 * g;
@@ -518,7 +541,9 @@ void decode_kernel(
   for (int i = 0; i < 4; ++i) voff[i] = (4 * g + i) * row_bytes + n * (D / 16) * (uint32_t)sizeof(__bf16);
 
   // Each wave pulls (partition, KV head) items until the queue is exhausted; every wave leaves
-  // the loop once the shared counter passes `total`.
+  // the loop once the shared counter passes `total`. (Taking the next index while the current
+  // item still streams was measured slower: near the end of the queue it binds short items to
+  // waves that are still busy.)
   while (true) {
     int idx = 0;
     if (lane == 0) idx = atomicAdd(queue, 1);
@@ -526,11 +551,11 @@ void decode_kernel(
     if (idx >= total) break;
     const int e = idx / Hkv;
     const int kvh = idx - e * Hkv;
-    const Work w = items[e];
-    const int s = w.seq, split = w.idx;
-    const int q0 = cu[s];
-    const int qn = cu[s + 1] - q0;
-    const int L = kv_lens[s];
+    const DecWork w = items[e];
+    const int s = w.seq, split = w.split;
+    const int q0 = w.q0;
+    const int qn = w.qn;
+    const int L = w.L;
     const int kb = split * P;
     const int ke = min(L, kb + P);
     const int nsplit = (L + P - 1) / P;
@@ -1285,9 +1310,9 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, in
   p.pre_cap = (max_q_len > dec_q) ? ((int64_t)num_tokens / p.bq + num_seqs) * p.pre_splits : 0;
   size_t off = 0;
   p.off_counts = off;
-  off = align256(off + 16);
+  off = align256(off + 32);
   p.off_dec = off;
-  off = align256(off + sizeof(Work) * (size_t)p.dec_cap);
+  off = align256(off + sizeof(DecWork) * (size_t)p.dec_cap);
   p.off_pre = off;
   off = align256(off + sizeof(Work) * (size_t)p.pre_cap);
   const size_t nrows = p.max_splits > 1 ? (size_t)num_seqs * p.qmaxd * Hq * p.max_splits : 0;
@@ -1447,7 +1472,7 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
   hipStream_t st = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
-  Work* dec = reinterpret_cast<Work*>(ws + p.off_dec);
+  DecWork* dec = reinterpret_cast<DecWork*>(ws + p.off_dec);
   Work* pre = reinterpret_cast<Work*>(ws + p.off_pre);
   float* o_part = reinterpret_cast<float*>(ws + p.off_opart);
   float* lse_part = reinterpret_cast<float*>(ws + p.off_lse);
@@ -1512,20 +1537,24 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
     }
   }
   {
-    // persistent: two 4-wave workgroups per compute unit (2 waves per SIMD), never more
-    // workgroups than a quarter of the items
+    // Persistent, 2 waves per SIMD. Beside prefill work: one 8-wave workgroup per compute unit
+    // (the whole register file, so a compute unit holds either decode or prefill work and none is
+    // left over), of which the plan lets counts[4] work. Otherwise two 4-wave workgroups per
+    // compute unit, which spreads small batches over more units. Never more waves than items.
     const int64_t items = p.dec_cap * num_kv_heads;
+    const int waves = dst != st ? kDecodeWaves : kDecodeWaves / 2;
+    const int64_t per_cu = dst != st ? 1 : 2;
     const unsigned grid = (unsigned)std::max<int64_t>(
-        1, std::min<int64_t>((items + kDecodeWaves - 1) / kDecodeWaves, 2 * (int64_t)cus));
+        1, std::min<int64_t>((items + waves - 1) / waves, per_cu * (int64_t)cus));
     int32_t* queue = counts + 2;
     if (!record_if(tm, CB_KERNEL_DECODE, true, dst)) return fail(CB_ERR_HIP, "hipEventRecord failed");
     if (head_dim == 128)
-      decode_kernel<128><<<grid, kDecodeWaves * 64, 0, dst>>>(
+      decode_kernel<128><<<grid, waves * 64, 0, dst>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
           queue, num_q_heads, num_kv_heads, block_div(block_size), max_blocks_per_seq, p.P, p.max_splits,
           p.qmaxd, scale_log2);
     else
-      decode_kernel<64><<<grid, kDecodeWaves * 64, 0, dst>>>(
+      decode_kernel<64><<<grid, waves * 64, 0, dst>>>(
           qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
           queue, num_q_heads, num_kv_heads, block_div(block_size), max_blocks_per_seq, p.P, p.max_splits,
           p.qmaxd, scale_log2);
