@@ -224,7 +224,7 @@ constexpr int kTailBuckets = 32;
 // fp32 (o, lse) partials that the log-sum-exp merge combines. Plan and kernel use this same
 // function, so they agree on the parts.
 constexpr int kMaxPreSplits = 4;
-constexpr int kPrefillSplitKeys = 1024;
+constexpr int kPrefillSplitKeys = 1536;
 // Splitting pays only when the longest prefill tile would outlast the batch's decode work, which
 // otherwise fills the compute units that the long tiles leave idle (the two kernels run side by
 // side). Estimated from measured rates on this GPU: one 32-key step of a prefill workgroup takes

@@ -173,7 +173,7 @@ EDGE = {
     "long-chunk-offset": ([synth.SeqSpec(200, 1500)], 32, 8, 128, 16),
     # prefill tiles split along the keys (few tiles, long contexts): 4 parts, uneven rounding,
     # head_dim 64, 256-row tiles of one head, and next to decodes and a short prompt
-    "prefill-split-4": ([synth.SeqSpec(96, 4096)], 32, 8, 128, 16),
+    "prefill-split-4": ([synth.SeqSpec(96, 6200)], 32, 8, 128, 16),
     "prefill-split-uneven": ([synth.SeqSpec(20, 2049), synth.SeqSpec(40, 3073)], 32, 8, 128, 32),
     "prefill-split-d64": ([synth.SeqSpec(70, 2500)], 16, 2, 64, 16),
     "prefill-split-mha": ([synth.SeqSpec(300, 2600)], 4, 4, 128, 16),
