@@ -58,7 +58,8 @@ typedef enum {
   CB_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad shape relation, misalignment */
   CB_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, block_size or head ratio */
   CB_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required */
-  CB_ERR_HIP = -4          /* a HIP launch failed; see cb_last_error() */
+  CB_ERR_HIP = -4,         /* a HIP launch failed; see cb_last_error() */
+  CB_ERR_OUT_OF_BLOCKS = -5 /* the block manager's pool cannot supply the blocks (cbblocks.h) */
 } cb_status;
 
 /* Static text naming a status code. Never NULL. */

@@ -1,0 +1,330 @@
+"""Oracle of the host block manager of the paged KV cache (test infrastructure only).
+
+Plain Python, one step at a time, written from these passages:
+  * "3.3 Batching & Memory Management", section "PagedAttention: block tables": the pool is
+    split into physical blocks of bs tokens; a sequence's table maps its logical block j to the
+    physical block holding positions [j*bs, (j+1)*bs); a new block is taken only when the last
+    one is full.
+  * same page, section "Sharing and copy-on-write": every block carries a reference count; a
+    forked sequence shares all of its parent's blocks; before a sequence writes into a block
+    whose count is above 1 it copies the block, points its table at the copy and decrements the
+    original's count.
+  * same page, section "Prefix caching and RadixAttention" (hash-based blocks): a full block is
+    identified by its tokens together with everything before it; a new request reuses every
+    leading block found; free cached blocks are evicted least recently used first.
+  * "Continuous batching architecture", sections "Prefix caching" and "Eviction": freed blocks
+    keep their content and key and count as free; cached blocks are given up only when the
+    never-used blocks run out.
+
+Where the pages leave a choice open, the reading taken (the library follows the same one):
+  * never-used blocks go out lowest id first; the cached pool is evicted least recently freed
+    first (the chapter's LRU, not the transformers docs' most-recent-first demotion); a sequence
+    frees its blocks last block first;
+  * the block holding a prompt's last token is never reused (its KV is computed so that the
+    step yields that token's output);
+  * a block's key here is the exact token prefix it completes (the library hashes it and checks
+    the hit), every block that completes a prefix is keyed, and a lookup takes the lowest id;
+  * the step protocol of the library header: KV is written by the GPU after the step closes,
+    so keys become findable, copy sources leave the pools, and written blocks may be copied
+    only after that; a copy whose source was written in the open step is refused; a sequence
+    in the open step's batch cannot be freed; a fork needs a parent with no pending tokens.
+
+``apply_step`` plays the GPU's part of a step on a simulated cache in which a slot holds the
+tuple of tokens its KV depends on (the whole prefix through its position), so that
+``check_views`` can verify by brute force that every sequence reads its own prefix back.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+OK = 0
+INVALID = -1
+OUT_OF_BLOCKS = -5
+
+FRESH, CACHED, USED, HELD = range(4)
+
+
+class BlockError(Exception):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class BlockManagerOracle:
+    def __init__(self, num_blocks: int, block_size: int):
+        if block_size < 1 or num_blocks < 1:
+            raise BlockError(INVALID, "sizes")
+        self.nb, self.bs = num_blocks, block_size
+        self.ref = [0] * num_blocks
+        self.pending = [0] * num_blocks
+        self.state = [FRESH] * num_blocks
+        self.cached: list[int] = []            # least recently freed first
+        self.key: list[tuple | None] = [None] * num_blocks
+        self.visible = [False] * num_blocks
+        self.dirty = [False] * num_blocks
+        self.seqs: dict[int, dict] = {}
+        self.copies: list[tuple[int, int]] = []
+        self.step_blocks: list[int] = []
+        self.step_seqs: list[int] = []
+        self.kv = [[None] * block_size for _ in range(num_blocks)]  # simulated cache
+
+    # -- pools ------------------------------------------------------------------------------
+    def _available(self) -> int:
+        return self.state.count(FRESH) + len(self.cached)
+
+    def _take(self) -> int:
+        fresh = [b for b in range(self.nb) if self.state[b] == FRESH]
+        if fresh:
+            b = min(fresh)
+        else:
+            b = self.cached.pop(0)
+            self.key[b] = None
+            self.visible[b] = False
+        self.state[b] = USED
+        self.ref[b] = 1
+        return b
+
+    def _add_ref(self, b: int):
+        if self.state[b] == CACHED:
+            self.cached.remove(b)
+            self.state[b] = USED
+        self.ref[b] += 1
+
+    def _to_pool(self, b: int):
+        if self.pending[b] > 0:
+            self.state[b] = HELD
+        elif self.key[b] is not None:
+            self.state[b] = CACHED
+            self.cached.append(b)
+        else:
+            self.state[b] = FRESH
+
+    def _release(self, b: int):
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self._to_pool(b)
+
+    def _lookup(self, prefix: tuple) -> int | None:
+        hits = [b for b in range(self.nb) if self.visible[b] and self.key[b] == prefix]
+        return min(hits) if hits else None
+
+    def _seq(self, sid) -> dict:
+        if sid not in self.seqs:
+            raise BlockError(INVALID, "unknown sequence id")
+        return self.seqs[sid]
+
+    # -- operations -------------------------------------------------------------------------
+    def add_sequence(self, sid: int, tokens) -> int:
+        tokens = [int(t) for t in tokens]
+        n, bs = len(tokens), self.bs
+        if n < 1:
+            raise BlockError(INVALID, "empty prompt")
+        if sid in self.seqs:
+            raise BlockError(INVALID, "id in use")
+        hits = []
+        for j in range((n - 1) // bs):
+            b = self._lookup(tuple(tokens[:(j + 1) * bs]))
+            if b is None:
+                break
+            hits.append(b)
+        nblocks = -(-n // bs)
+        cached_hits = sum(1 for b in hits if self.state[b] == CACHED)
+        if nblocks - len(hits) > self._available() - cached_hits:
+            raise BlockError(OUT_OF_BLOCKS, "pool exhausted")
+        table = []
+        for b in hits:
+            self._add_ref(b)
+            table.append(b)
+        while len(table) < nblocks:
+            table.append(self._take())
+        self.seqs[sid] = dict(tokens=tokens, table=table, computed=len(hits) * bs,
+                              nkeys=len(hits), in_batch=False)
+        return len(hits) * bs
+
+    def append_tokens(self, sid: int, tokens):
+        s = self._seq(sid)
+        tokens = [int(t) for t in tokens]
+        if not tokens:
+            return
+        bs, n = self.bs, len(s["tokens"])
+        last = s["table"][-1]
+        cow = n % bs != 0 and self.ref[last] > 1
+        if cow and self.dirty[last]:
+            raise BlockError(INVALID, "copy of a block written in the open step")
+        nblocks = -(-(n + len(tokens)) // bs)
+        if nblocks - len(s["table"]) + int(cow) > self._available():
+            raise BlockError(OUT_OF_BLOCKS, "pool exhausted")
+        if cow:
+            dst = self._take()
+            self.pending[last] += 1
+            self.ref[last] -= 1
+            self.copies.append((last, dst))
+            s["table"][-1] = dst
+        s["tokens"].extend(tokens)
+        while len(s["table"]) < nblocks:
+            s["table"].append(self._take())
+
+    def fork(self, parent: int, child: int):
+        p = self._seq(parent)
+        if child in self.seqs:
+            raise BlockError(INVALID, "child id in use")
+        if p["computed"] != len(p["tokens"]):
+            raise BlockError(INVALID, "parent has tokens not yet computed")
+        c = dict(tokens=list(p["tokens"]), table=list(p["table"]), computed=p["computed"],
+                 nkeys=p["nkeys"], in_batch=False)
+        for b in c["table"]:
+            self._add_ref(b)
+        self.seqs[child] = c
+
+    def free_sequence(self, sid: int):
+        s = self._seq(sid)
+        if s["in_batch"]:
+            raise BlockError(INVALID, "sequence in the open step's batch")
+        for b in reversed(s["table"]):
+            self._release(b)
+        del self.seqs[sid]
+
+    def build_batch(self, seq_ids, q_lens, max_blocks_per_seq: int, token_capacity: int):
+        """Returns (cu_seqlens_q, kv_lens, block_tables, slot_mapping, token_ids) as int32 arrays.
+        The i-th batch row computes positions [computed, computed + q) of its sequence; position p
+        is stored at slot table[p // bs] * bs + p % bs."""
+        bs = self.bs
+        seq_ids, q_lens = [int(x) for x in seq_ids], [int(x) for x in q_lens]
+        seen = set()
+        for sid, q in zip(seq_ids, q_lens):
+            s = self._seq(sid)
+            if sid in seen:
+                raise BlockError(INVALID, "sequence twice in one batch")
+            seen.add(sid)
+            if not 1 <= q <= len(s["tokens"]) - s["computed"]:
+                raise BlockError(INVALID, "bad q_len")
+            if len(s["table"]) > max_blocks_per_seq:
+                raise BlockError(INVALID, "table longer than max_blocks_per_seq")
+            for j in range(s["computed"] // bs, (s["computed"] + q - 1) // bs + 1):
+                if self.ref[s["table"][j]] != 1:
+                    raise BlockError(INVALID, "a written block is shared")
+        if sum(q_lens) > token_capacity:
+            raise BlockError(INVALID, "token_capacity too small")
+        S = len(seq_ids)
+        cu = np.zeros(S + 1, np.int32)
+        kv_lens = np.zeros(S, np.int32)
+        tables = np.full((S, max_blocks_per_seq), -1, np.int32)
+        slots, toks = [], []
+        for i, (sid, q) in enumerate(zip(seq_ids, q_lens)):
+            s = self.seqs[sid]
+            p0 = s["computed"]
+            for p in range(p0, p0 + q):
+                b = s["table"][p // bs]
+                slots.append(b * bs + p % bs)
+                toks.append(s["tokens"][p])
+                if not self.dirty[b]:
+                    self.dirty[b] = True
+                    self.step_blocks.append(b)
+            cu[i + 1] = len(slots)
+            kv_lens[i] = p0 + q
+            tables[i, :len(s["table"])] = s["table"]
+            s["computed"] = p0 + q
+            for j in range(s["nkeys"], s["computed"] // bs):   # key the newly completed blocks
+                b = s["table"][j]
+                if self.key[b] is None:
+                    self.key[b] = tuple(s["tokens"][:(j + 1) * bs])
+                    self.visible[b] = False
+                    self.step_blocks.append(b)
+            s["nkeys"] = max(s["nkeys"], s["computed"] // bs)
+            if not s["in_batch"]:
+                s["in_batch"] = True
+                self.step_seqs.append(sid)
+        return cu, kv_lens, tables, np.array(slots, np.int32), np.array(toks, np.int32)
+
+    def take_copies(self, capacity: int | None = None):
+        """Closes the step; returns the pending (src, dst) copies in the order they were made."""
+        if capacity is not None and len(self.copies) > capacity:
+            raise BlockError(INVALID, "capacity too small")
+        out = list(self.copies)
+        for src, _ in out:
+            self.pending[src] -= 1
+            if self.pending[src] == 0 and self.state[src] == HELD:
+                self._to_pool(src)
+        for b in self.step_blocks:
+            self.dirty[b] = False
+            if self.key[b] is not None:
+                self.visible[b] = True
+        for sid in self.step_seqs:
+            if sid in self.seqs:
+                self.seqs[sid]["in_batch"] = False
+        self.copies, self.step_blocks, self.step_seqs = [], [], []
+        return out
+
+    # -- views ------------------------------------------------------------------------------
+    def stats(self):
+        held = sum(1 for b in range(self.nb) if self.state[b] == HELD)
+        return self.state.count(FRESH), len(self.cached), held, len(self.seqs)
+
+    def block_table(self, sid) -> list[int]:
+        return list(self._seq(sid)["table"])
+
+    def sequence_info(self, sid):
+        s = self._seq(sid)
+        return len(s["tokens"]), s["computed"], len(s["table"])
+
+    # -- the GPU's part of a step, simulated -------------------------------------------------
+    def apply_step(self, copies, batch):
+        """Copies first (whole blocks), then the batch's new KV at its slots: the KV of the
+        token at position p of a sequence is the tuple of that sequence's tokens 0..p."""
+        for src, dst in copies:
+            self.kv[dst] = list(self.kv[src])
+        seq_ids, cu, slots = batch
+        bs = self.bs
+        for i, sid in enumerate(seq_ids):
+            s = self.seqs[sid]
+            q = int(cu[i + 1] - cu[i])
+            p0 = s["computed"] - q
+            for k in range(q):
+                p = p0 + k
+                sl = int(slots[cu[i] + k])
+                self.kv[sl // bs][sl % bs] = tuple(s["tokens"][:p + 1])
+
+    def check_views(self):
+        """Brute force: every computed position of every live sequence reads its own prefix."""
+        bs = self.bs
+        for sid, s in self.seqs.items():
+            for p in range(s["computed"]):
+                b = s["table"][p // bs]
+                if self.kv[b][p % bs] != tuple(s["tokens"][:p + 1]):
+                    return f"sequence {sid} position {p} reads the wrong KV (block {b})"
+        return None
+
+    def check_counts(self):
+        """Reference counts equal the table entries that name each block; pool states agree."""
+        count = [0] * self.nb
+        for s in self.seqs.values():
+            for b in s["table"]:
+                count[b] += 1
+        if count != self.ref:
+            return "reference counts differ from table entries"
+        for b in range(self.nb):
+            st = self.state[b]
+            if (st == USED) != (self.ref[b] > 0):
+                return f"block {b}: state {st} with ref {self.ref[b]}"
+            if st == HELD and self.pending[b] == 0:
+                return f"block {b} held without a pending copy"
+            if st == CACHED and (self.key[b] is None or b not in self.cached):
+                return f"block {b} cached without a key"
+        if len(set(self.cached)) != len(self.cached):
+            return "a block is cached twice"
+        return None
+
+
+def copy_blocks(k_cache, v_cache, src, dst):
+    """Copies of the caches after the copy-on-write copies: block dst[i] of K and of V becomes
+    block src[i] ("Sharing and copy-on-write": the engine copies the shared block before the
+    write). Arrays [..., num_blocks, bs, Hkv, D] (a leading layer axis is allowed); pairs with an
+    id outside [0, num_blocks) or src == dst are skipped, as the library does. Pairs are applied
+    from the originals, so the result does not depend on their order when no dst is a src."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    nb = kc.shape[-4]
+    for s, d in zip(np.asarray(src).tolist(), np.asarray(dst).tolist()):
+        if 0 <= s < nb and 0 <= d < nb and s != d:
+            kc[..., d, :, :, :] = k_cache[..., s, :, :, :]
+            vc[..., d, :, :, :] = v_cache[..., s, :, :, :]
+    return kc, vc

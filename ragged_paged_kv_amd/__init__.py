@@ -26,12 +26,17 @@ __all__ = [
     "cb_cache_write", "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens",
     "cb_paged_attention", "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
     "alloc_workspace", "EXPORTED_SYMBOLS", "CB_KERNEL_DECODE", "CB_KERNEL_PREFILL",
+    "cb_copy_blocks", "BlockManager", "CB_ERR_OUT_OF_BLOCKS",
 ]
 
 EXPORTED_SYMBOLS = (
     "cb_status_string", "cb_last_error", "cb_slot_mapping", "cb_cache_write",
     "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens", "cb_paged_attention",
     "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
+    # include/cbblocks.h
+    "cb_bm_create", "cb_bm_destroy", "cb_bm_add_sequence", "cb_bm_append_tokens", "cb_bm_fork",
+    "cb_bm_free_sequence", "cb_bm_build_batch", "cb_bm_take_copies", "cb_bm_sequence_info",
+    "cb_bm_block_table", "cb_bm_stats", "cb_bm_ref_counts", "cb_copy_blocks",
 )
 
 
@@ -69,10 +74,24 @@ _sig = {
     "cb_split_kv_reduce": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "cb_validate_batch": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _i32]),
     "cb_time_next_kernel": (ctypes.c_int, [_i32, _p, _p]),
+    "cb_bm_create": (ctypes.c_int, [_i64, _i32, _p]),
+    "cb_bm_destroy": (None, [_p]),
+    "cb_bm_add_sequence": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
+    "cb_bm_append_tokens": (ctypes.c_int, [_p, _i64, _p, _i32]),
+    "cb_bm_fork": (ctypes.c_int, [_p, _i64, _i64]),
+    "cb_bm_free_sequence": (ctypes.c_int, [_p, _i64]),
+    "cb_bm_build_batch": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
+    "cb_bm_take_copies": (ctypes.c_int, [_p, _p, _p, _i32, _p]),
+    "cb_bm_sequence_info": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
+    "cb_bm_block_table": (ctypes.c_int, [_p, _i64, _p, _i32]),
+    "cb_bm_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
+    "cb_bm_ref_counts": (ctypes.c_int, [_p, _p, _i64]),
+    "cb_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i64, _i64, _i32, _i64, _p]),
 }
 
 CB_KERNEL_DECODE = 1
 CB_KERNEL_PREFILL = 2
+CB_ERR_OUT_OF_BLOCKS = -5
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(lib, _name)
     _fn.restype = _res
@@ -253,3 +272,119 @@ def cb_validate_batch(cu_seqlens_q, kv_lens, block_tables, slot_mapping, block_s
     if raise_on_error:
         _check(st, "cb_validate_batch")
     return int(st)
+
+
+# ---------------------------------------------------------------------------------------------
+# block manager (include/cbblocks.h): host arrays are numpy int32 / int64
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class BlockManager:
+    """Owner of one cb_block_manager handle. Each method calls the C function of the same name
+    (cb_bm_<method>) and raises CBError on a non-zero status."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = ctypes.c_void_p()
+        _check(lib.cb_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)), "cb_bm_create")
+        self._h = h
+        self._destroy = lib.cb_bm_destroy  # kept: module globals may be gone at interpreter exit
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def add_sequence(self, seq_id: int, tokens) -> int:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib.cb_bm_add_sequence(self._h, int(seq_id), _ptr(t), t.size, ctypes.byref(n)),
+               "cb_bm_add_sequence")
+        return n.value
+
+    def append_tokens(self, seq_id: int, tokens):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(lib.cb_bm_append_tokens(self._h, int(seq_id), _ptr(t), t.size), "cb_bm_append_tokens")
+
+    def fork(self, parent: int, child: int):
+        _check(lib.cb_bm_fork(self._h, int(parent), int(child)), "cb_bm_fork")
+
+    def free_sequence(self, seq_id: int):
+        _check(lib.cb_bm_free_sequence(self._h, int(seq_id)), "cb_bm_free_sequence")
+
+    def build_batch(self, seq_ids, q_lens, max_blocks_per_seq: int, token_capacity: int | None = None):
+        """Returns (cu_seqlens_q, kv_lens, block_tables, slot_mapping, token_ids), int32 numpy."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        q = np.ascontiguousarray(q_lens, dtype=np.int32)
+        S = ids.size
+        cap = int(q.sum()) if token_capacity is None else int(token_capacity)
+        cu = np.zeros(S + 1, np.int32)
+        kv = np.zeros(max(S, 1), np.int32)
+        bt = np.zeros((max(S, 1), int(max_blocks_per_seq)), np.int32)
+        sl = np.zeros(max(cap, 1), np.int32)
+        tk = np.zeros(max(cap, 1), np.int32)
+        _check(lib.cb_bm_build_batch(self._h, _ptr(ids), _ptr(q), S, int(max_blocks_per_seq), cap,
+                                     _ptr(cu), _ptr(kv), _ptr(bt), _ptr(sl), _ptr(tk)),
+               "cb_bm_build_batch")
+        T = int(cu[-1])
+        return cu, kv[:S], bt[:S], sl[:T], tk[:T]
+
+    def take_copies(self, capacity: int | None = None):
+        """Closes the step; returns (src, dst) int32 arrays of the pending copies."""
+        n = ctypes.c_int32()
+        if capacity is None:
+            lib.cb_bm_take_copies(self._h, None, None, 0, ctypes.byref(n))  # count only
+            capacity = n.value
+        src = np.zeros(max(capacity, 1), np.int32)
+        dst = np.zeros(max(capacity, 1), np.int32)
+        _check(lib.cb_bm_take_copies(self._h, _ptr(src), _ptr(dst), int(capacity), ctypes.byref(n)),
+               "cb_bm_take_copies")
+        return src[:n.value], dst[:n.value]
+
+    def sequence_info(self, seq_id: int):
+        n, c, b = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check(lib.cb_bm_sequence_info(self._h, int(seq_id), ctypes.byref(n), ctypes.byref(c),
+                                       ctypes.byref(b)), "cb_bm_sequence_info")
+        return n.value, c.value, b.value
+
+    def block_table(self, seq_id: int):
+        nb = self.sequence_info(seq_id)[2]
+        out = np.zeros(max(nb, 1), np.int32)
+        _check(lib.cb_bm_block_table(self._h, int(seq_id), _ptr(out), out.size), "cb_bm_block_table")
+        return out[:nb]
+
+    def stats(self):
+        """(never-used free blocks, cached blocks, held blocks, live sequences)."""
+        v = [ctypes.c_int64() for _ in range(4)]
+        _check(lib.cb_bm_stats(self._h, *[ctypes.byref(x) for x in v]), "cb_bm_stats")
+        return tuple(x.value for x in v)
+
+    def ref_counts(self):
+        out = np.zeros(self.num_blocks, np.int32)
+        _check(lib.cb_bm_ref_counts(self._h, _ptr(out), out.size), "cb_bm_ref_counts")
+        return out
+
+
+def cb_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, num_layers: int = 1, stream=None):
+    """Copy blocks src_blocks[i] -> dst_blocks[i] (int32 device tensors) of K and V. The caches are
+    [NB, bs, Hkv, D] bf16, or [L, NB, bs, Hkv, D] with num_layers = L."""
+    torch = _torch()
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or src_blocks.shape != dst_blocks.shape:
+        raise ValueError("cb_copy_blocks: inconsistent shapes")
+    nd = 5 if num_layers > 1 else 4
+    if k_cache.dim() != nd or (nd == 5 and k_cache.shape[0] != num_layers):
+        raise ValueError("cb_copy_blocks: caches must be [NB, bs, Hkv, D] or [L, NB, bs, Hkv, D]")
+    NB = k_cache.shape[-4]
+    block_bytes = int(np.prod(k_cache.shape[-3:])) * k_cache.element_size()
+    layer_stride = NB * block_bytes
+    _check(lib.cb_copy_blocks(_dev(k_cache, "k_cache", torch.bfloat16, nd),
+                              _dev(v_cache, "v_cache", torch.bfloat16, nd),
+                              _dev(src_blocks, "src_blocks", torch.int32, 1),
+                              _dev(dst_blocks, "dst_blocks", torch.int32, 1), src_blocks.numel(),
+                              block_bytes, NB, int(num_layers), layer_stride, _stream(stream)),
+           "cb_copy_blocks")

@@ -30,6 +30,7 @@ extern "C" const char* cb_status_string(int status) {
     case CB_ERR_UNSUPPORTED: return "CB_ERR_UNSUPPORTED";
     case CB_ERR_WORKSPACE: return "CB_ERR_WORKSPACE";
     case CB_ERR_HIP: return "CB_ERR_HIP";
+    case CB_ERR_OUT_OF_BLOCKS: return "CB_ERR_OUT_OF_BLOCKS";
     default: return "CB_ERR_UNKNOWN";
   }
 }

@@ -2,6 +2,7 @@
 rejects host-checkable bad arguments with the documented status codes before touching a GPU,
 and its host-only validator enforces the documented preconditions."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -15,11 +16,11 @@ from conftest import ROOT
 
 cb = pytest.importorskip("ragged_paged_kv_amd")
 
-HEADER = os.path.join(ROOT, "include", "cbattn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(cb_[a-z0-9_]+)\s*\(", text)))
 
@@ -50,6 +51,7 @@ def test_status_strings():
     assert cb.cb_status_string(-2) == "CB_ERR_UNSUPPORTED"
     assert cb.cb_status_string(-3) == "CB_ERR_WORKSPACE"
     assert cb.cb_status_string(-4) == "CB_ERR_HIP"
+    assert cb.cb_status_string(-5) == "CB_ERR_OUT_OF_BLOCKS"
     assert cb.cb_status_string(7) == "CB_ERR_UNKNOWN"
 
 

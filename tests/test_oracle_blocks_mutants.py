@@ -1,0 +1,85 @@
+"""Plant plausible mistakes in copies of the block-manager oracle (on the CPU) and require that
+some pin catches each one."""
+import os
+import types
+
+import pytest
+
+from conftest import ROOT, read_golden
+from pins_blocks import (pin_block_table_example, pin_eviction_order, pin_fork_cow_example,
+                         pin_last_token_block_not_reused, pin_prefix_worked_example,
+                         pin_protocol_rules, pin_random_bruteforce)
+
+SRC = open(os.path.join(ROOT, "oracle", "blocks.py")).read()
+
+MUTANTS = {
+    # a write into a shared partial block goes in place
+    "no-cow": [("cow = n % bs != 0 and self.ref[last] > 1", "cow = False", 1)],
+    # the original's count is not decremented on a copy
+    "cow-keeps-ref": [("            self.ref[last] -= 1\n", "", 1)],
+    # the block holding the last prompt token is reused too
+    "hit-last-block": [("for j in range((n - 1) // bs):", "for j in range(n // bs):", 1)],
+    # most recently freed cached block evicted first
+    "mru-eviction": [("b = self.cached.pop(0)", "b = self.cached.pop()", 1)],
+    # a sequence's blocks freed first block first
+    "free-forward": [('for b in reversed(s["table"]):', 'for b in s["table"]:', 1)],
+    # an evicted block keeps its key
+    "evict-keeps-key": [("            self.key[b] = None\n            self.visible[b] = False\n",
+                         "", 1)],
+    # a copy's source goes straight back to the pool
+    "no-hold": [("        if self.pending[b] > 0:\n            self.state[b] = HELD\n        elif",
+                 "        if", 1)],
+    # blocks computed in the open step are found at once
+    "visible-at-once": [("                    self.visible[b] = False\n",
+                         "                    self.visible[b] = True\n", 1)],
+    # a copy of a block written in the open step is allowed
+    "cow-of-dirty": [("if cow and self.dirty[last]:", "if False:", 1)],
+    # a block keyed by its own tokens only, not by the whole prefix
+    "key-own-tokens": [('self.key[b] = tuple(s["tokens"][:(j + 1) * bs])',
+                        'self.key[b] = tuple(s["tokens"][j * bs:(j + 1) * bs])', 1),
+                       ("b = self._lookup(tuple(tokens[:(j + 1) * bs]))",
+                        "b = self._lookup(tuple(tokens[j * bs:(j + 1) * bs]))", 1)],
+    # the slot offset taken from the batch row instead of the position
+    "slot-offset": [("slots.append(b * bs + p % bs)", "slots.append(b * bs + (p - p0) % bs)", 1)],
+    # fork does not take references
+    "fork-no-ref": [('        for b in c["table"]:\n            self._add_ref(b)\n', "", 1)],
+}
+
+
+def mutant(name):
+    src = SRC
+    for old, new, count in MUTANTS[name]:
+        assert src.count(old) == count, f"mutation site for {name} not found exactly {count} time(s)"
+        src = src.replace(old, new)
+    mod = types.ModuleType(f"blocks_mutant_{name}")
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def caught(mod):
+    pins = [
+        lambda: pin_fork_cow_example(mod, read_golden("p3_fork_cow_example.txt")),
+        lambda: pin_block_table_example(mod, read_golden("p3_block_table_example.txt")),
+        lambda: pin_prefix_worked_example(mod, read_golden("p3_prefix_examples.txt")),
+        lambda: pin_last_token_block_not_reused(mod),
+        lambda: pin_eviction_order(mod),
+        lambda: pin_protocol_rules(mod),
+        lambda: pin_random_bruteforce(mod, seeds=range(6), n_ops=120),
+    ]
+    for pin in pins:
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 -- any failure of a pin counts as caught
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    assert caught(mutant(name)), f"no pin notices the planted mistake {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    mod = types.ModuleType("blocks_unmutated")
+    exec(compile(SRC, "<unmutated>", "exec"), mod.__dict__)
+    assert not caught(mod)
