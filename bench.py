@@ -16,6 +16,12 @@ the mixed ones. The roofline object covers the dominant kernel (the decode kerne
 the prefill-chunk kernel, MFMA-bound), timed with HIP events that the library records around
 that kernel on the stream it runs on (cb_time_next_kernel).
 
+Block manager data path (its own JSON line, not the default run):
+    python bench.py --blocks [--steps K] [--warmup W]
+        cb_copy_blocks on a Llama-3-8B-shaped pool (32 layers, block 16, 8 KV heads, head_dim 128)
+        copying one shared partial block per sequence of a 256-sequence batch, against the HBM
+        roofline; plus the host block manager's cost per decode step and per prompt admission.
+
 Measurement helpers (not part of the timed run):
     python bench.py --copy-calibration            # plain device copy of known size, for counters
     python bench.py --traffic-summary FETCH WRITE CFETCH CWRITE [--config N]
@@ -81,23 +87,23 @@ def work_of(b):
     }
 
 
-def traffic_record_path(workload):
-    return os.path.join(ROOT, "profiles", f"paged_attention_{workload}_hbm_traffic.json")
+def traffic_record_path(workload, op="paged_attention"):
+    return os.path.join(ROOT, "profiles", f"{op}_{workload}_hbm_traffic.json")
 
 
-def attention_source_sha256():
-    src = open(os.path.join(ROOT, "ragged_paged_kv_amd", "csrc", "attention.hip"), "rb").read()
+def source_sha256(name="attention.hip"):
+    src = open(os.path.join(ROOT, "ragged_paged_kv_amd", "csrc", name), "rb").read()
     return hashlib.sha256(src).hexdigest()
 
 
-def traffic_from_profile(workload):
+def traffic_from_profile(workload, op="paged_attention", source="attention.hip"):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
-    path = traffic_record_path(workload)
+    path = traffic_record_path(workload, op)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("attention_hip_sha256") != attention_source_sha256():
+    if rec.get("source_sha256", rec.get("attention_hip_sha256")) != source_sha256(source):
         return None
     return rec.get("bytes_per_launch")
 
@@ -315,10 +321,22 @@ def _pmc_means(d, counter, name_part, last_group=False):
 
 def traffic_summary(args):
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_summary
-    import synth
-    b = synth.make_config(args.config)
-    kname = "decode_kernel" if args.config in DECODE_CONFIGS else "prefill_kernel"
-    alone = kname == "prefill_kernel"
+    if args.blocks:
+        workload, op, source = BLOCKS_WORKLOAD, "copy_blocks", "block_copy.hip"
+        kname, alone, alg = "copy_blocks_kernel", False, blocks_launch_bytes()
+        bench_flags = "--blocks --steps 5 --warmup 1 --no-cpu-baseline"
+        measured = "every launch of the copy kernel"
+    else:
+        import synth
+        b = synth.make_config(args.config)
+        workload, op, source = b.name, "paged_attention", "attention.hip"
+        kname = "decode_kernel" if args.config in DECODE_CONFIGS else "prefill_kernel"
+        alone = kname == "prefill_kernel"
+        w = work_of(b)
+        alg = w["decode_kernel_bytes"] if kname == "decode_kernel" else w["prefill_kernel_bytes"]
+        bench_flags = f"--config {args.config} --steps 5 --warmup 2 --no-cpu-baseline --no-mixed"
+        measured = ("the prefill chunks alone (the launches the MFMA roofline times)" if alone
+                    else "every launch of the decode kernel")
     kn, fetch_kib, nf = _pmc_means(fetch_dir, "FETCH_SIZE", kname, last_group=alone)
     _, write_kib, nw = _pmc_means(write_dir, "WRITE_SIZE", kname, last_group=alone)
     cn, cfetch_kib, _ = _pmc_means(cfetch_dir, "FETCH_SIZE", "")
@@ -327,34 +345,144 @@ def traffic_summary(args):
     f_write = COPY_BYTES / 1024 / cwrite_kib
     fetch_b = fetch_kib * 1024 * f_fetch
     write_b = write_kib * 1024 * f_write
-    w = work_of(b)
-    alg = w["decode_kernel_bytes"] if kname == "decode_kernel" else w["prefill_kernel_bytes"]
     rec = {
-        "workload": b.name, "kernel": kn, "attention_hip_sha256": attention_source_sha256(),
+        "workload": workload, "kernel": kn, "source": source, "source_sha256": source_sha256(source),
         "fetch_kib_per_launch": round(fetch_kib, 1), "write_kib_per_launch": round(write_kib, 1),
-        "launches": [nf, nw],
-        "launches_measured": "the prefill chunks alone (the launches the MFMA roofline times)"
-        if alone else "every launch of the decode kernel",
+        "launches": [nf, nw], "launches_measured": measured,
         "copy_kernel": cn, "copy_bytes": COPY_BYTES,
         "copy_fetch_kib": round(cfetch_kib, 1), "copy_write_kib": round(cwrite_kib, 1),
         "fetch_scale": round(f_fetch, 5), "write_scale": round(f_write, 5),
         "bytes_per_launch": int(fetch_b + write_b),
         "algorithmic_bytes_per_launch": alg,
         "commands": [
-            f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o p --output-format csv -- python3 bench.py "
-            f"--config {args.config} --steps 5 --warmup 2 --no-cpu-baseline --no-mixed",
-            f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o p --output-format csv -- python3 bench.py "
-            f"--config {args.config} --steps 5 --warmup 2 --no-cpu-baseline --no-mixed",
+            f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o p --output-format csv -- python3 bench.py {bench_flags}",
+            f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o p --output-format csv -- python3 bench.py {bench_flags}",
             f"rocprofv3 --pmc FETCH_SIZE -d {cfetch_dir} -o p --output-format csv -- python3 bench.py --copy-calibration",
             f"rocprofv3 --pmc WRITE_SIZE -d {cwrite_dir} -o p --output-format csv -- python3 bench.py --copy-calibration",
-            "python3 bench.py --traffic-summary " + " ".join(args.traffic_summary) + f" --config {args.config}",
+            "python3 bench.py --traffic-summary " + " ".join(args.traffic_summary)
+            + (" --blocks" if args.blocks else f" --config {args.config}"),
         ],
     }
-    path = traffic_record_path(b.name)
+    path = traffic_record_path(workload, op)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+
+
+BLOCKS_SHAPE = dict(layers=32, num_blocks=4096, block_size=16, kv_heads=8, head_dim=128, pairs=256)
+BLOCKS_WORKLOAD = "cow-copy-llama3-8b-shape"
+
+
+def blocks_launch_bytes():
+    """Algorithmic bytes of one copy launch: every pair reads and writes one block of K and one of
+    V in every layer."""
+    sh = BLOCKS_SHAPE
+    block_bytes = sh["block_size"] * sh["kv_heads"] * sh["head_dim"] * 2
+    return 2 * sh["pairs"] * sh["layers"] * 2 * block_bytes
+
+
+def bench_blocks(args):
+    """cb_copy_blocks throughput and host manager cost; prints one JSON line."""
+    import numpy as np
+    import torch
+    import ragged_paged_kv_amd as cb
+    sh = BLOCKS_SHAPE
+    L, NB, bs, hkv, d, n = (sh[k] for k in ("layers", "num_blocks", "block_size", "kv_heads",
+                                            "head_dim", "pairs"))
+    block_bytes = bs * hkv * d * 2
+    shape = (L, NB, bs, hkv, d)
+    kc = torch.randn(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.randn(shape, dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(5)
+    ids = rng.permutation(NB)
+    src = torch.from_numpy(ids[:n].astype(np.int32)).cuda()
+    dst = torch.from_numpy(ids[n:2 * n].astype(np.int32)).cuda()
+    launch_bytes = blocks_launch_bytes()
+    for _ in range(args.warmup):
+        cb.cb_copy_blocks(kc, vc, src, dst, num_layers=L)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        cb.cb_copy_blocks(kc, vc, src, dst, num_layers=L)
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ok = torch.equal(kc[:, dst.long()], kc[:, src.long()]) and torch.equal(vc[:, dst.long()],
+                                                                           vc[:, src.long()])
+    gbs = launch_bytes / (ms / 1e3) / 1e9
+    log(f"[bench] copy_blocks: {ms * 1e3:.1f} us per launch, {gbs:.0f} GB/s, copies intact: {ok}")
+
+    # host manager: a 256-sequence decode step (append one token each, build the batch, take the
+    # copies) and the admission of a 2048-token prompt whose first 1536 tokens are cached
+    m = cb.BlockManager(1 << 16, bs)
+    S = 256
+    for s_ in range(S):
+        m.add_sequence(s_, rng.integers(0, 32000, int(rng.integers(128, 4096))).tolist())
+    pend = [m.sequence_info(s_)[0] for s_ in range(S)]
+    m.build_batch(list(range(S)), pend, 512)
+    m.take_copies()
+    reps = 200
+    t0 = time.perf_counter()
+    ids, ones = np.arange(S, dtype=np.int64), np.ones(S, np.int32)
+    bufs = (np.zeros(S + 1, np.int32), np.zeros(S, np.int32), np.full((S, 512), -1, np.int32),
+            np.zeros(S, np.int32), np.zeros(S, np.int32))
+    for r in range(reps):
+        m.append_batch(ids, ones, np.full(S, r, np.int32))
+        m.build_batch(ids, ones, 512, out=bufs)
+        m.take_copies()
+    step_us = (time.perf_counter() - t0) / reps * 1e6
+    system = rng.integers(0, 32000, 1536).tolist()
+    m.add_sequence(10_000, system + [1] * 512)
+    m.build_batch([10_000], [2048], 512)
+    m.take_copies()
+    t0 = time.perf_counter()
+    for r in range(reps):
+        hit = m.add_sequence(20_000 + r, system + rng.integers(0, 32000, 512).tolist())
+    admit_us = (time.perf_counter() - t0) / reps * 1e6
+    log(f"[bench] manager: decode step of {S} sequences {step_us:.0f} us, admission {admit_us:.0f} us "
+        f"(cached {hit} of 2048)")
+
+    cpu = None
+    if not args.no_cpu_baseline:   # the oracle's copy on the host cores, on a sample of the pairs
+        import oracle.blocks as ob
+        kh = kc[:, :64].view(torch.int16).cpu().numpy()
+        vh = vc[:, :64].view(torch.int16).cpu().numpy()
+        sp = np.arange(16, dtype=np.int32)
+        dp = np.arange(16, 32, dtype=np.int32)
+        t0 = time.perf_counter()
+        it = 0
+        while time.perf_counter() - t0 < 10.0:
+            ob.copy_blocks(kh, vh, sp, dp)
+            it += 1
+        cpu_s = (time.perf_counter() - t0) / it
+        cpu = {"value": round(2 * 16 * L * 2 * block_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"oracle copy_blocks, 16 pairs x {L} layers, {it} runs"}
+    res = {
+        "metric": "copy-on-write block copy GB/s (% HBM peak)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": BLOCKS_WORKLOAD, "layers": L, "num_blocks": NB,
+                   "block_size": bs, "kv_heads": hkv, "head_dim": d, "pairs": n,
+                   "block_bytes_per_layer_tensor": block_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(BLOCKS_WORKLOAD, "copy_blocks", "block_copy.hip"),
+                     "kernel": "copy_blocks_kernel", "kernel_ms": round(ms, 5),
+                     "bytes_per_launch": launch_bytes},
+        "wall_ms_per_launch": round(wall * 1e3, 5),
+        "copies_verified": bool(ok),
+        "host_manager": {"decode_step_us_256_seqs": round(step_us, 1),
+                         "admission_us_2048_tokens_1536_cached": round(admit_us, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -368,6 +496,7 @@ def main():
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-batch measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR")
+    ap.add_argument("--blocks", action="store_true", help="block copy and host manager measurement")
     args = ap.parse_args()
 
     if args.traffic_summary:
@@ -388,6 +517,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.blocks:
+        bench_blocks(args)
         return
 
     r = measure(args, args.config, args.steps, args.warmup)

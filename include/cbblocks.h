@@ -78,6 +78,13 @@ int cb_bm_add_sequence(cb_block_manager* m, int64_t seq_id, const int32_t* token
 int cb_bm_append_tokens(cb_block_manager* m, int64_t seq_id, const int32_t* tokens,
                         int32_t num_tokens);
 
+/* cb_bm_append_tokens for seq_ids[i] with counts[i] tokens taken in order from the packed host
+ * array tokens (sum of counts entries), for i = 0, 1, ... until one fails: that failure's status is
+ * returned, earlier appends stay done and *num_done receives how many succeeded (a decode step's
+ * appends in one call; the scheduler preempts from the first refused sequence on). */
+int cb_bm_append_batch(cb_block_manager* m, const int64_t* seq_ids, const int32_t* counts,
+                       const int32_t* tokens, int32_t num_seqs, int32_t* num_done);
+
 /* New sequence `child` sharing every block of `parent` (parallel sampling, beam search). */
 int cb_bm_fork(cb_block_manager* m, int64_t parent, int64_t child);
 
@@ -90,7 +97,8 @@ int cb_bm_free_sequence(cb_block_manager* m, int64_t seq_id);
  * (1 <= q_lens[i] <= tokens not yet computed; no sequence twice). Outputs (host arrays the caller
  * allocates), in the layouts cb_paged_attention reads (include/cbattn.h):
  *   cu_seqlens_q [num_seqs + 1], kv_lens [num_seqs] (positions computed after this step),
- *   block_tables [num_seqs, max_blocks_per_seq] (entries past the table hold -1),
+ *   block_tables [num_seqs, max_blocks_per_seq] (row i gets sequence i's table; entries past it
+ *   are left as they are: cb_paged_attention never reads them),
  *   slot_mapping [T] and token_ids [T] (may be NULL) with T = sum q_lens <= token_capacity.
  * Those positions count as computed from here on.
  */

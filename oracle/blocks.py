@@ -164,6 +164,19 @@ class BlockManagerOracle:
         while len(s["table"]) < nblocks:
             s["table"].append(self._take())
 
+    def append_batch(self, seq_ids, counts, tokens):
+        """append_tokens for each sequence in order until one is refused; returns how many were
+        appended, or raises with .num_done set."""
+        off = 0
+        for i, (sid, n) in enumerate(zip(seq_ids, counts)):
+            try:
+                self.append_tokens(int(sid), list(tokens[off:off + int(n)]))
+            except BlockError as e:
+                e.num_done = i
+                raise
+            off += int(n)
+        return len(seq_ids)
+
     def fork(self, parent: int, child: int):
         p = self._seq(parent)
         if child in self.seqs:

@@ -34,7 +34,8 @@ EXPORTED_SYMBOLS = (
     "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens", "cb_paged_attention",
     "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
     # include/cbblocks.h
-    "cb_bm_create", "cb_bm_destroy", "cb_bm_add_sequence", "cb_bm_append_tokens", "cb_bm_fork",
+    "cb_bm_create", "cb_bm_destroy", "cb_bm_add_sequence", "cb_bm_append_tokens",
+    "cb_bm_append_batch", "cb_bm_fork",
     "cb_bm_free_sequence", "cb_bm_build_batch", "cb_bm_take_copies", "cb_bm_sequence_info",
     "cb_bm_block_table", "cb_bm_stats", "cb_bm_ref_counts", "cb_copy_blocks",
 )
@@ -78,6 +79,7 @@ _sig = {
     "cb_bm_destroy": (None, [_p]),
     "cb_bm_add_sequence": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
     "cb_bm_append_tokens": (ctypes.c_int, [_p, _i64, _p, _i32]),
+    "cb_bm_append_batch": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p]),
     "cb_bm_fork": (ctypes.c_int, [_p, _i64, _i64]),
     "cb_bm_free_sequence": (ctypes.c_int, [_p, _i64]),
     "cb_bm_build_batch": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
@@ -253,7 +255,7 @@ def _host_i32(a, name):
     if a is None:
         return None, None
     arr = np.ascontiguousarray(np.asarray(a), dtype=np.int32)
-    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+    return arr, ctypes.c_void_p(arr.ctypes.data)
 
 
 def cb_validate_batch(cu_seqlens_q, kv_lens, block_tables, slot_mapping, block_size: int,
@@ -279,7 +281,8 @@ def cb_validate_batch(cu_seqlens_q, kv_lens, block_tables, slot_mapping, block_s
 
 
 def _ptr(a):
-    return a.ctypes.data_as(ctypes.c_void_p)
+    # the raw address: numpy's data_as goes through ctypes.cast, which is slow here (~70 us)
+    return ctypes.c_void_p(a.ctypes.data)
 
 
 class BlockManager:
@@ -311,28 +314,57 @@ class BlockManager:
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         _check(lib.cb_bm_append_tokens(self._h, int(seq_id), _ptr(t), t.size), "cb_bm_append_tokens")
 
+    def append_batch(self, seq_ids, counts, tokens) -> int:
+        """Appends counts[i] tokens (packed in order in `tokens`) to seq_ids[i] until one is refused;
+        returns how many sequences were appended (all of them, or raises CBError with the count
+        in .num_done)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        c = np.ascontiguousarray(counts, dtype=np.int32)
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        done = ctypes.c_int32()
+        st = lib.cb_bm_append_batch(self._h, _ptr(ids), _ptr(c), _ptr(t), ids.size, ctypes.byref(done))
+        if st != 0:
+            e = CBError(st, "cb_bm_append_batch", cb_last_error())
+            e.num_done = done.value
+            raise e
+        return done.value
+
     def fork(self, parent: int, child: int):
         _check(lib.cb_bm_fork(self._h, int(parent), int(child)), "cb_bm_fork")
 
     def free_sequence(self, seq_id: int):
         _check(lib.cb_bm_free_sequence(self._h, int(seq_id)), "cb_bm_free_sequence")
 
-    def build_batch(self, seq_ids, q_lens, max_blocks_per_seq: int, token_capacity: int | None = None):
-        """Returns (cu_seqlens_q, kv_lens, block_tables, slot_mapping, token_ids), int32 numpy."""
+    def build_batch(self, seq_ids, q_lens, max_blocks_per_seq: int, token_capacity: int | None = None,
+                    out=None):
+        """Returns (cu_seqlens_q, kv_lens, block_tables, slot_mapping, token_ids), int32 numpy.
+        Without `out`, fresh arrays whose table entries past a sequence's table hold -1. With
+        out = (cu, kv_lens, tables, slots, token_ids), caller-owned int32 arrays (a serving loop
+        keeps them across steps) are filled; table entries past a sequence's table keep their
+        contents, and the returned arrays are views of them."""
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         q = np.ascontiguousarray(q_lens, dtype=np.int32)
         S = ids.size
-        cap = int(q.sum()) if token_capacity is None else int(token_capacity)
-        cu = np.zeros(S + 1, np.int32)
-        kv = np.zeros(max(S, 1), np.int32)
-        bt = np.zeros((max(S, 1), int(max_blocks_per_seq)), np.int32)
-        sl = np.zeros(max(cap, 1), np.int32)
-        tk = np.zeros(max(cap, 1), np.int32)
+        if out is None:
+            cap = int(q.sum()) if token_capacity is None else int(token_capacity)
+            cu = np.zeros(S + 1, np.int32)
+            kv = np.zeros(max(S, 1), np.int32)
+            bt = np.full((max(S, 1), int(max_blocks_per_seq)), -1, np.int32)
+            sl = np.zeros(max(cap, 1), np.int32)
+            tk = np.zeros(max(cap, 1), np.int32)
+        else:
+            cu, kv, bt, sl, tk = out
+            for a in out:
+                if a.dtype != np.int32 or not a.flags.c_contiguous:
+                    raise ValueError("build_batch: out arrays must be C-contiguous int32")
+            if cu.size < S + 1 or kv.size < S or bt.shape[0] < S or bt.shape[1] != max_blocks_per_seq:
+                raise ValueError("build_batch: out arrays are too small")
+            cap = min(sl.size, tk.size)
         _check(lib.cb_bm_build_batch(self._h, _ptr(ids), _ptr(q), S, int(max_blocks_per_seq), cap,
                                      _ptr(cu), _ptr(kv), _ptr(bt), _ptr(sl), _ptr(tk)),
                "cb_bm_build_batch")
-        T = int(cu[-1])
-        return cu, kv[:S], bt[:S], sl[:T], tk[:T]
+        T = int(cu[S])
+        return cu[:S + 1], kv[:S], bt[:S], sl[:T], tk[:T]
 
     def take_copies(self, capacity: int | None = None):
         """Closes the step; returns (src, dst) int32 arrays of the pending copies."""

@@ -24,7 +24,6 @@
 #include <new>
 #include <set>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 #include "cb_internal.h"
@@ -37,6 +36,7 @@ struct cb_block_manager {
     std::vector<uint64_t> keys;  // chained key of each leading full block whose KV is computed
     int64_t computed = 0;        // leading positions whose KV is computed or in a built batch
     bool in_batch = false;       // part of a batch built since the step last closed
+    uint64_t stamp = 0;          // the last cb_bm_build_batch call that named this sequence
   };
 
   int64_t num_blocks = 0;
@@ -56,6 +56,8 @@ struct cb_block_manager {
   std::vector<int32_t> step_blocks;         // blocks keyed or written in the open step
   std::vector<int64_t> step_seqs;           // sequences in batches of the open step
   int64_t held = 0;                         // blocks in state kHeld
+  uint64_t build_calls = 0;                 // cb_bm_build_batch calls so far
+  std::vector<Seq*> batch;                  // scratch of cb_bm_build_batch
 };
 
 namespace {
@@ -286,6 +288,24 @@ extern "C" int cb_bm_append_tokens(cb_block_manager* m, int64_t seq_id, const in
   return cb::ok();
 }
 
+extern "C" int cb_bm_append_batch(cb_block_manager* m, const int64_t* seq_ids,
+                                  const int32_t* counts, const int32_t* tokens, int32_t num_seqs,
+                                  int32_t* num_done) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  if (!num_done) return cb::fail(E, "num_done is NULL");
+  *num_done = 0;
+  if (num_seqs < 0) return cb::fail(E, "num_seqs must be >= 0");
+  if (num_seqs > 0 && (!seq_ids || !counts)) return cb::fail(E, "NULL array");
+  int64_t off = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int st = cb_bm_append_tokens(m, seq_ids[i], tokens ? tokens + off : nullptr, counts[i]);
+    if (st != CB_OK) return st;
+    off += counts[i];
+    *num_done = i + 1;
+  }
+  return cb::ok();
+}
+
 extern "C" int cb_bm_fork(cb_block_manager* m, int64_t parent, int64_t child) {
   if (!m) return cb::fail(E, "manager is NULL");
   Mgr::Seq* p = find_seq(m, parent);
@@ -322,13 +342,15 @@ extern "C" int cb_bm_build_batch(cb_block_manager* m, const int64_t* seq_ids, co
   if (!cu_seqlens_q) return cb::fail(E, "cu_seqlens_q is NULL");
   if (num_seqs > 0 && (!seq_ids || !q_lens || !kv_lens || !block_tables || !slot_mapping))
     return cb::fail(E, "NULL array");
-  std::vector<Mgr::Seq*> ss(num_seqs);
-  std::unordered_set<int64_t> seen;
+  auto& ss = m->batch;
+  ss.resize(num_seqs);
+  const uint64_t stamp = ++m->build_calls;
   int64_t total = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
     Mgr::Seq* s = ss[i] = find_seq(m, seq_ids[i]);
     if (!s) return cb::fail(E, "unknown sequence id");
-    if (!seen.insert(seq_ids[i]).second) return cb::fail(E, "a sequence appears twice in the batch");
+    if (s->stamp == stamp) return cb::fail(E, "a sequence appears twice in the batch");
+    s->stamp = stamp;
     const int64_t left = (int64_t)s->tokens.size() - s->computed;
     if (q_lens[i] < 1 || q_lens[i] > left)
       return cb::fail(E, "q_len must be in [1, tokens not yet computed]");
@@ -356,7 +378,7 @@ extern "C" int cb_bm_build_batch(cb_block_manager* m, const int64_t* seq_ids, co
     cu_seqlens_q[i + 1] = (int32_t)t;
     kv_lens[i] = (int32_t)p1;
     int32_t* row = block_tables + (int64_t)i * max_blocks_per_seq;
-    for (int32_t j = 0; j < max_blocks_per_seq; ++j) row[j] = j < (int32_t)s.table.size() ? s.table[j] : -1;
+    std::memcpy(row, s.table.data(), sizeof(int32_t) * s.table.size());  // the rest is not read
     s.computed = p1;
     key_computed_blocks(m, s);
     if (!s.in_batch) {

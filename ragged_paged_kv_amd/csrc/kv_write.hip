@@ -97,7 +97,8 @@ extern "C" int cb_cache_write(const void* k, const void* v, const int32_t* slot_
   const int32_t chunks = (int32_t)((int64_t)num_kv_heads * head_dim * 2 / 16);
   const int64_t total = 2 * (int64_t)num_tokens * chunks;
   const int64_t grid = (total + 255) / 256;
-  if (grid > INT32_MAX) return fail(CB_ERR_UNSUPPORTED, "cb_cache_write: batch too large");
+  // a dispatch holds fewer than 2^32 work-items
+  if (grid * 256 > (int64_t)UINT32_MAX) return fail(CB_ERR_UNSUPPORTED, "cb_cache_write: batch too large");
   cache_write_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(
       (const uint4*)k, (const uint4*)v, slot_mapping, (uint4*)k_cache, (uint4*)v_cache,
       num_tokens, chunks);

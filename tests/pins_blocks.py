@@ -296,8 +296,10 @@ def random_ops(rng, n_ops, vocab=3, bs=4, shared=(), max_prompt=14):
             base = list(shared[rng.integers(len(shared))]) if shared and rng.random() < 0.7 else []
             extra = rng.integers(1, max_prompt)
             ops.append(("add", base + [int(x) for x in rng.integers(0, vocab, extra)]))
-        elif r < 0.45:
+        elif r < 0.4:
             ops.append(("append", [int(x) for x in rng.integers(0, vocab, rng.integers(1, 4))]))
+        elif r < 0.45:
+            ops.append(("append_batch", int(rng.integers(1, 1 << 30))))
         elif r < 0.55:
             ops.append(("fork", None))
         elif r < 0.7:
@@ -321,6 +323,12 @@ def drive(sim_like, ops, rng_seed):
             elif kind == "append" and live:
                 sid = live[rng.integers(len(live))]
                 out = sim_like.append(sid, arg)
+            elif kind == "append_batch" and live:
+                r2 = np.random.default_rng(arg)
+                ids = [s for s in live if r2.random() < 0.5]
+                counts = [int(r2.integers(0, 3)) for _ in ids]
+                toks = [int(x) for x in r2.integers(0, 3, sum(counts))]
+                out = sim_like.append_batch(ids, counts, toks)
             elif kind == "fork" and live:
                 sid = live[rng.integers(len(live))]
                 out = sim_like.fork(sid, next_id)
@@ -342,7 +350,7 @@ def drive(sim_like, ops, rng_seed):
         except Exception as e:  # noqa: BLE001 -- refusals are part of the compared behaviour
             if not hasattr(e, "status"):
                 raise
-            log.append((kind, e.status, None))
+            log.append((kind, e.status, getattr(e, "num_done", None)))
             if kind == "add":
                 next_id += 1
             if kind == "fork":
@@ -361,6 +369,9 @@ class OracleDriver:
 
     def append(self, sid, toks):
         return self.sim.m.append_tokens(sid, toks)
+
+    def append_batch(self, ids, counts, toks):
+        return self.sim.m.append_batch(ids, counts, toks)
 
     def fork(self, p, c):
         return self.sim.fork(p, c)

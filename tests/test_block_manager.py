@@ -25,6 +25,9 @@ class LibDriver:
     def append(self, sid, toks):
         return self.m.append_tokens(sid, toks)
 
+    def append_batch(self, ids, counts, toks):
+        return self.m.append_batch(ids, counts, toks)
+
     def fork(self, p, c):
         return self.m.fork(p, c)
 
@@ -176,3 +179,40 @@ def test_serving_steps_cpu_data_path(hq, hkv, d, bs, nb, seed):
     stats = serving_run(cb, CpuBackend, hq, hkv, d, bs, nb, n_steps=24, seed=seed,
                         log=lambda *a: None)
     assert stats["hits"] > 0 and stats["copies"] > 0 and stats["forks"] > 0
+
+
+def test_copy_blocks_rejects_oversized_dispatch():
+    fake = ctypes.c_void_p(0x10000)
+    # 2^21 copies x 32 layers x 2 tensors x 16 workgroups of 128 lanes > 2^32 work-items
+    assert cb.lib.cb_copy_blocks(fake, fake, fake, fake, 1 << 21, 32768, 1 << 22, 32,
+                                 32768 << 22, None) == -2
+
+
+def test_build_batch_into_caller_buffers():
+    m = cb.BlockManager(64, 4)
+    for s in range(3):
+        m.add_sequence(s, list(range(10 * s, 10 * s + 5 + s)))
+    a = m.build_batch([0, 1, 2], [5, 6, 7], 8)
+    m2 = cb.BlockManager(64, 4)
+    for s in range(3):
+        m2.add_sequence(s, list(range(10 * s, 10 * s + 5 + s)))
+    bufs = (np.zeros(4, np.int32), np.zeros(3, np.int32), np.full((3, 8), -1, np.int32),
+            np.zeros(18, np.int32), np.zeros(18, np.int32))
+    b = m2.build_batch([0, 1, 2], [5, 6, 7], 8, out=bufs)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    with pytest.raises(ValueError):
+        m2.build_batch([0], [1], 8, out=(bufs[0].astype(np.int64),) + bufs[1:])
+
+
+def test_append_batch_stops_at_first_refusal():
+    m = cb.BlockManager(4, 4)
+    m.add_sequence(0, [1, 2, 3, 4])
+    m.add_sequence(1, [5, 6, 7, 8])
+    m.build_batch([0, 1], [4, 4], 4)
+    m.take_copies()
+    # seq 0 takes a block, seq 1 takes the last, the third append (seq 0 again) needs one more
+    with pytest.raises(cb.CBError) as e:
+        m.append_batch([0, 1, 0], [1, 1, 4], list(range(6)))
+    assert e.value.status == cb.CB_ERR_OUT_OF_BLOCKS and e.value.num_done == 2
+    assert m.sequence_info(0)[0] == 5 and m.sequence_info(1)[0] == 5
