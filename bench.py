@@ -22,6 +22,13 @@ Block manager data path (its own JSON line, not the default run):
         copying one shared partial block per sequence of a 256-sequence batch, against the HBM
         roofline; plus the host block manager's cost per decode step and per prompt admission.
 
+Step graphs (its own JSON line, not the default run):
+    python bench.py --graphs [--steps K] [--warmup W]
+        a small Llama-3-8B-shaped decode batch (16 sequences, KV length uniform in [256, 2048]),
+        one step = metadata upload + slot mapping + cache write + paged attention, run eagerly
+        through the Python binding and through the step-graph executor (one upload + one graph
+        launch); wall time per step of back-to-back steps, and the GPU time per step.
+
 Measurement helpers (not part of the timed run):
     python bench.py --copy-calibration            # plain device copy of known size, for counters
     python bench.py --traffic-summary FETCH WRITE CFETCH CWRITE [--config N]
@@ -485,6 +492,145 @@ def bench_blocks(args):
     print(json.dumps(res), flush=True)
 
 
+GRAPHS_SHAPE = dict(seqs=16, q_heads=32, kv_heads=8, head_dim=128, block_size=16, kv_lo=256,
+                    kv_hi=2048)
+
+
+def bench_graphs(args):
+    """Eager vs recorded steps on a launch-bound decode batch; prints one JSON line."""
+    import numpy as np
+    import torch
+    import ragged_paged_kv_amd as cb
+    sh = GRAPHS_SHAPE
+    S, Hq, Hkv, D, bs = (sh[k] for k in ("seqs", "q_heads", "kv_heads", "head_dim", "block_size"))
+    rng = np.random.default_rng(7)
+    kv = rng.integers(sh["kv_lo"], sh["kv_hi"] + 1, S).astype(np.int32)
+    MB = -(-sh["kv_hi"] // bs)
+    nblk = -(-kv // bs)
+    NB = int(nblk.sum()) + 64
+    perm = rng.permutation(NB)
+    tables = np.full((S, MB), -1, np.int32)
+    o = 0
+    for i in range(S):
+        tables[i, :nblk[i]] = perm[o:o + nblk[i]]
+        o += nblk[i]
+    cu = np.arange(S + 1, dtype=np.int32)
+    T, scale = S, 1.0 / np.sqrt(D)
+    dev = "cuda"
+    kc = torch.randn((NB, bs, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.randn_like(kc)
+    maxT = 64
+    q = torch.randn((maxT, Hq, D), dtype=torch.bfloat16, device=dev)
+    k = torch.randn((maxT, Hkv, D), dtype=torch.bfloat16, device=dev)
+    v = torch.randn_like(k)
+    out = torch.empty_like(q)
+    stream = torch.cuda.Stream()
+    pin = [torch.from_numpy(a).pin_memory() for a in (cu, kv, tables)]
+    dmeta = [torch.empty_like(t, device=dev) for t in pin]
+    slots = torch.empty(T, dtype=torch.int32, device=dev)
+    ws = cb.alloc_workspace(S, T, Hq, Hkv, D, bs, 1, int(kv.max()))
+
+    def eager():
+        for h, d in zip(pin, dmeta):
+            d.copy_(h, non_blocking=True)
+        cb.cb_slot_mapping(dmeta[0], dmeta[1], dmeta[2], slots, bs)
+        cb.cb_cache_write(k[:T], v[:T], slots, kc, vc)
+        cb.cb_paged_attention(q[:T], dmeta[0], dmeta[1], dmeta[2], kc, vc, out[:T], scale, 1,
+                              int(kv.max()), ws)
+
+    g = cb.StepGraphs(q, k, v, out, kc, vc, scale, max_seqs=S + 8, max_kv_len=MB * bs,
+                      max_blocks_per_seq=MB, use_graphs=True)
+    gd = cb.StepGraphs(q, k, v, out, kc, vc, scale, max_seqs=S + 8, max_kv_len=MB * bs,
+                       max_blocks_per_seq=MB, use_graphs=False)
+
+    def graph():
+        g.run(cu, kv, tables, stream=stream)
+
+    def direct():
+        gd.run(cu, kv, tables, stream=stream)
+
+    # the graph's padded shape, run eagerly: separates the cost of padding from that of replay
+    shape = g.run(cu, kv, tables, stream=stream)
+    stream.synchronize()
+    Sb, Tb, mqb, mkvb = shape
+    pcu = np.concatenate([cu, np.full(Sb - S, Tb)]).astype(np.int32)
+    pkv = np.concatenate([kv, np.zeros(Sb - S)]).astype(np.int32)
+    ptab = np.concatenate([tables, np.full((Sb - S, MB), -1)]).astype(np.int32)
+    ppin = [torch.from_numpy(a).pin_memory() for a in (pcu, pkv, ptab)]
+    pdev = [torch.empty_like(t, device=dev) for t in ppin]
+    pslots = torch.empty(Tb, dtype=torch.int32, device=dev)
+    pws = cb.alloc_workspace(Sb, Tb, Hq, Hkv, D, bs, mqb, mkvb)
+
+    def eager_padded():
+        for h, d in zip(ppin, pdev):
+            d.copy_(h, non_blocking=True)
+        cb.cb_slot_mapping(pdev[0], pdev[1], pdev[2], pslots, bs)
+        cb.cb_cache_write(k[:Tb], v[:Tb], pslots, kc, vc)
+        cb.cb_paged_attention(q[:Tb], pdev[0], pdev[1], pdev[2], kc, vc, out[:Tb], scale, mqb, mkvb,
+                              pws)
+
+    def timed(fn):
+        """(synchronous: wall ms per step when every step is waited for, as an engine that needs
+        the step's output before it can build the next; back-to-back: wall ms per step with no
+        wait between steps, and the stream's span per step)"""
+        for _ in range(max(args.warmup, 3)):
+            fn()
+        stream.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+            stream.synchronize()
+        sync_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        stream.synchronize()
+        b2b_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        return {"sync_ms_per_step": round(sync_ms, 5), "back_to_back_ms_per_step": round(b2b_ms, 5),
+                "stream_ms_per_step": round(a.elapsed_time(b) / args.steps, 5)}
+
+    with torch.cuda.stream(stream):
+        e = timed(eager)
+        ref = out[:T].clone()
+        ep = timed(eager_padded)
+        gr = timed(graph)
+        diff = float((out[:T].float() - ref.float()).abs().max())
+        di = timed(direct)
+        diff = max(diff, float((out[:T].float() - ref.float()).abs().max()))
+    captures, replays, eager_runs, cached = g.stats()
+    log(f"[bench] steps (synchronous / back to back, us): python calls {e['sync_ms_per_step'] * 1e3:.1f} / "
+        f"{e['back_to_back_ms_per_step'] * 1e3:.1f}, python calls padded {ep['sync_ms_per_step'] * 1e3:.1f} / "
+        f"{ep['back_to_back_ms_per_step'] * 1e3:.1f}, executor direct {di['sync_ms_per_step'] * 1e3:.1f} / "
+        f"{di['back_to_back_ms_per_step'] * 1e3:.1f}, executor graphs {gr['sync_ms_per_step'] * 1e3:.1f} / "
+        f"{gr['back_to_back_ms_per_step'] * 1e3:.1f}; max |executor - python| {diff:.3g}; "
+        f"captures {captures} replays {replays}")
+    g.close()
+    gd.close()
+    g_wall = min(gr["sync_ms_per_step"], di["sync_ms_per_step"])
+    res = {
+        "metric": "synchronous decode steps/s through the native step executor (small batch)",
+        "value": round(1e3 / g_wall, 1), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(g_wall, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3-8b-decode-16seq-graphs", "num_seqs": S, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "block_size": bs,
+                   "kv_tokens": int(kv.sum()),
+                   "step": "metadata upload + slot_mapping + cache_write + paged_attention"},
+        "timing": "synchronous steps (each waited for); value = the faster executor mode's steps/s",
+        "python_calls": e, "python_calls_padded": ep, "executor_direct": di,
+        "executor_graphs": dict(gr, captures=captures, replays=replays),
+        "speedup_sync": round(e["sync_ms_per_step"] / g_wall, 3),
+        "max_abs_diff_vs_eager": diff,
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -497,6 +643,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR")
     ap.add_argument("--blocks", action="store_true", help="block copy and host manager measurement")
+    ap.add_argument("--graphs", action="store_true", help="eager vs recorded steps, small decode batch")
     args = ap.parse_args()
 
     if args.traffic_summary:
@@ -520,6 +667,9 @@ def main():
         return
     if args.blocks:
         bench_blocks(args)
+        return
+    if args.graphs:
+        bench_graphs(args)
         return
 
     r = measure(args, args.config, args.steps, args.warmup)

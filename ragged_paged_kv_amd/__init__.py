@@ -26,7 +26,7 @@ __all__ = [
     "cb_cache_write", "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens",
     "cb_paged_attention", "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
     "alloc_workspace", "EXPORTED_SYMBOLS", "CB_KERNEL_DECODE", "CB_KERNEL_PREFILL",
-    "cb_copy_blocks", "BlockManager", "CB_ERR_OUT_OF_BLOCKS",
+    "cb_copy_blocks", "BlockManager", "CB_ERR_OUT_OF_BLOCKS", "StepGraphs",
 ]
 
 EXPORTED_SYMBOLS = (
@@ -38,6 +38,8 @@ EXPORTED_SYMBOLS = (
     "cb_bm_append_batch", "cb_bm_fork",
     "cb_bm_free_sequence", "cb_bm_build_batch", "cb_bm_take_copies", "cb_bm_sequence_info",
     "cb_bm_block_table", "cb_bm_stats", "cb_bm_ref_counts", "cb_copy_blocks",
+    # include/cbgraphs.h
+    "cb_graphs_create", "cb_graphs_destroy", "cb_graphs_run", "cb_graphs_stats",
 )
 
 
@@ -89,6 +91,10 @@ _sig = {
     "cb_bm_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
     "cb_bm_ref_counts": (ctypes.c_int, [_p, _p, _i64]),
     "cb_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i64, _i64, _i32, _i64, _p]),
+    "cb_graphs_create": (ctypes.c_int, [_p, _p]),
+    "cb_graphs_destroy": (None, [_p]),
+    "cb_graphs_run": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _p]),
+    "cb_graphs_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
 }
 
 CB_KERNEL_DECODE = 1
@@ -420,3 +426,81 @@ def cb_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, num_layers: int = 1
                               _dev(dst_blocks, "dst_blocks", torch.int32, 1), src_blocks.numel(),
                               block_bytes, NB, int(num_layers), layer_stride, _stream(stream)),
            "cb_copy_blocks")
+
+
+# ---------------------------------------------------------------------------------------------
+# step graphs (include/cbgraphs.h)
+
+
+class GraphsConfig(ctypes.Structure):
+    """cb_step_graphs_config, field for field."""
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64), ("max_blocks_per_seq", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
+                ("max_kv_len", ctypes.c_int32), ("token_interval", ctypes.c_int32),
+                ("kv_interval", ctypes.c_int32), ("seq_interval", ctypes.c_int32),
+                ("max_graphs", ctypes.c_int32), ("use_graphs", ctypes.c_int32),
+                ("scale", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
+
+
+class StepGraphs:
+    """Owner of one cb_step_graphs executor over fixed torch buffers (kept referenced here):
+    q [max_tokens, Hq, D], k, v [max_tokens, Hkv, D], out [max_tokens, Hq, D], caches
+    [num_blocks, bs, Hkv, D], all bf16 on the GPU. use_graphs records and replays HIP graphs;
+    the default launches the step's kernels directly (less GPU time per step on MI355X)."""
+
+    def __init__(self, q, k, v, out, k_cache, v_cache, scale: float, max_seqs: int,
+                 max_kv_len: int, max_blocks_per_seq: int, token_interval: int = 16,
+                 kv_interval: int = 256, seq_interval: int = 8, max_graphs: int = 32,
+                 use_graphs: bool = False):
+        torch = _torch()
+        T, Hq, D = q.shape
+        NB, bs, Hkv, _ = k_cache.shape
+        if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D) \
+                or tuple(out.shape) != (T, Hq, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+            raise ValueError("StepGraphs: inconsistent shapes")
+        self._bufs = (q, k, v, out, k_cache, v_cache)
+        cfg = GraphsConfig(Hq, Hkv, D, bs, NB, int(max_blocks_per_seq), T, int(max_seqs),
+                           int(max_kv_len), int(token_interval), int(kv_interval),
+                           int(seq_interval), int(max_graphs), int(bool(use_graphs)), float(scale),
+                           _dev(q, "q", torch.bfloat16, 3), _dev(k, "k", torch.bfloat16, 3),
+                           _dev(v, "v", torch.bfloat16, 3), _dev(out, "out", torch.bfloat16, 3),
+                           _dev(k_cache, "k_cache", torch.bfloat16, 4),
+                           _dev(v_cache, "v_cache", torch.bfloat16, 4))
+        h = ctypes.c_void_p()
+        _check(lib.cb_graphs_create(ctypes.byref(cfg), ctypes.byref(h)), "cb_graphs_create")
+        self._h = h
+        self._destroy = lib.cb_graphs_destroy
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def run(self, cu_seqlens_q, kv_lens, block_tables, stream=None):
+        """One step from host metadata (numpy int32); returns the padded shape (Sb, Tb, max q,
+        max kv). The stream must not be torch's default (NULL) stream."""
+        cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+        kv = np.ascontiguousarray(kv_lens, dtype=np.int32)
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        S = kv.size
+        if cu.size != S + 1 or (S and bt.shape != (S, self.max_blocks_per_seq)):
+            raise ValueError("StepGraphs.run: inconsistent metadata shapes")
+        shape = (ctypes.c_int32 * 4)()
+        _check(lib.cb_graphs_run(self._h, _ptr(cu), _ptr(kv), _ptr(bt), S, _stream(stream), shape),
+               "cb_graphs_run")
+        return tuple(shape)
+
+    def stats(self):
+        """(graphs recorded, replays, eager first runs, graphs cached)."""
+        c, r, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        n = ctypes.c_int32()
+        _check(lib.cb_graphs_stats(self._h, ctypes.byref(c), ctypes.byref(r), ctypes.byref(e),
+                                   ctypes.byref(n)), "cb_graphs_stats")
+        return c.value, r.value, e.value, n.value

@@ -189,3 +189,20 @@ def test_validator_rejections():
     assert _v(b, bs=3) == -1
     cu2 = cu.copy(); cu2[0] = 1
     assert _v(b, cu=cu2) == -1
+
+
+def test_graphs_host_checks():
+    fake = ctypes.c_void_p(0x10000)
+    cfg = cb.GraphsConfig(8, 2, 128, 16, 64, 16, 32, 4, 256, 16, 256, 8, 4, 1, 0.1,
+                          fake, fake, fake, fake, fake, fake)
+    h = ctypes.c_void_p()
+    for field, bad in [("max_seqs", 1), ("block_size", 3), ("token_interval", 0),
+                       ("max_kv_len", 257), ("max_graphs", 0), ("scale", float("nan")), ("q", None)]:
+        c = cb.GraphsConfig.from_buffer_copy(cfg)
+        setattr(c, field, bad)
+        assert cb.lib.cb_graphs_create(ctypes.byref(c), ctypes.byref(h)) == -1, field
+        assert not h.value
+    assert cb.lib.cb_graphs_create(None, ctypes.byref(h)) == -1
+    assert cb.lib.cb_graphs_run(None, None, None, None, 0, None, None) == -1
+    assert cb.lib.cb_graphs_stats(None, None, None, None, None) == -1
+    cb.lib.cb_graphs_destroy(None)
