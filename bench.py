@@ -20,7 +20,9 @@ Block manager data path (its own JSON line, not the default run):
     python bench.py --blocks [--steps K] [--warmup W]
         cb_copy_blocks on a Llama-3-8B-shaped pool (32 layers, block 16, 8 KV heads, head_dim 128)
         copying one shared partial block per sequence of a 256-sequence batch, against the HBM
-        roofline; plus the host block manager's cost per decode step and per prompt admission.
+        roofline; the swap tier moving the same 256 blocks to a pinned host pool and back, against
+        PCIe 5.0 x16 (64 GB/s a direction); the host block manager's cost per decode step and per
+        prompt admission.
 
 Step graphs (its own JSON line, not the default run):
     python bench.py --graphs [--steps K] [--warmup W]
@@ -49,6 +51,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ragged paged-attn decode KV GB/s (% HBM peak) + mixed-batch tokens/s"
 HBM_PEAK_GBS = 8000.0
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
 BF16_PEAK_TFLOPS = 2500.0
 DECODE_CONFIGS = (1, 2, 4)
 COPY_BYTES = 2 << 30  # copy calibration: bytes read and bytes written
@@ -424,6 +427,35 @@ def bench_blocks(args):
     gbs = launch_bytes / (ms / 1e3) / 1e9
     log(f"[bench] copy_blocks: {ms * 1e3:.1f} us per launch, {gbs:.0f} GB/s, copies intact: {ok}")
 
+    # swap tier: the same 256 blocks (all layers, K and V: 512 MiB) to a pinned host pool and back
+    pool = torch.empty((n, 2, L, bs, hkv, d), dtype=torch.bfloat16, pin_memory=True)
+    slots = torch.arange(n, dtype=torch.int32, device="cuda")
+    swap_bytes = n * L * 2 * block_bytes
+
+    def time_launch(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out_ms = time_launch(lambda: cb.cb_swap_out_blocks(kc, vc, src, slots, pool, num_layers=L))
+    in_ms = time_launch(lambda: cb.cb_swap_in_blocks(pool, slots, dst, kc, vc, num_layers=L))
+    swap_ok = torch.equal(kc[:, dst.long()].cpu(), pool[:, 0].transpose(0, 1)) and \
+        torch.equal(vc[:, dst.long()].cpu(), pool[:, 1].transpose(0, 1))
+    flat = torch.empty(swap_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    flat_host = pool.view(-1)
+    dma_d2h = time_launch(lambda: flat_host.copy_(flat, non_blocking=True))
+    dma_h2d = time_launch(lambda: flat.copy_(flat_host, non_blocking=True))
+    out_gbs, in_gbs = swap_bytes / out_ms / 1e6, swap_bytes / in_ms / 1e6
+    log(f"[bench] swap: out {out_ms:.2f} ms {out_gbs:.1f} GB/s, in {in_ms:.2f} ms {in_gbs:.1f} GB/s "
+        f"({swap_bytes} bytes each, blocks intact: {swap_ok}); a contiguous DMA copy of the same "
+        f"size: to host {swap_bytes / dma_d2h / 1e6:.1f} GB/s, to device {swap_bytes / dma_h2d / 1e6:.1f} GB/s")
+
     # host manager: a 256-sequence decode step (append one token each, build the batch, take the
     # copies) and the admission of a 2048-token prompt whose first 1536 tokens are cached
     m = cb.BlockManager(1 << 16, bs)
@@ -485,6 +517,17 @@ def bench_blocks(args):
                      "bytes_per_launch": launch_bytes},
         "wall_ms_per_launch": round(wall * 1e3, 5),
         "copies_verified": bool(ok),
+        "swap": {
+            "bytes_per_transfer": swap_bytes, "blocks_intact": bool(swap_ok),
+            "out": {"bound": "pcie", "achieved": round(out_gbs, 2), "peak": PCIE_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(out_gbs / PCIE_PEAK_GBS, 4),
+                    "kernel": "swap_blocks_kernel<true>", "kernel_ms": round(out_ms, 4)},
+            "in": {"bound": "pcie", "achieved": round(in_gbs, 2), "peak": PCIE_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(in_gbs / PCIE_PEAK_GBS, 4),
+                   "kernel": "swap_blocks_kernel<false>", "kernel_ms": round(in_ms, 4)},
+            "dma_contiguous_gbs": {"to_host": round(swap_bytes / dma_d2h / 1e6, 2),
+                                   "to_device": round(swap_bytes / dma_h2d / 1e6, 2)},
+        },
         "host_manager": {"decode_step_us_256_seqs": round(step_us, 1),
                          "admission_us_2048_tokens_1536_cached": round(admit_us, 1)},
         "cpu_baseline": cpu,

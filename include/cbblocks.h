@@ -36,7 +36,18 @@
  *  - a copy's source block stays out of the free pools until cb_bm_take_copies returns it, so no
  *    copy of one launch overwrites another copy's source; no copy's destination is a source;
  *  - a sequence in a batch of the open step cannot be freed;
- *  - a fork needs a parent whose every token is computed or in a built batch.
+ *  - a fork needs a parent whose every token is computed or in a built batch;
+ *  - swap (below): a sequence with blocks written in the open step cannot be swapped out; blocks
+ *    released by a swap-out and slots released by a swap-in or a free are held until the step
+ *    closes; swapped-in blocks count as written in the open step; a swapped sequence cannot be
+ *    appended to, forked or batched.
+ *
+ * The swap tier ("Continuous batching architecture", section "Offloading": an offloaded
+ * request's KV blocks are copied to a pre-allocated pinned host pool, every request that fits
+ * in one batched transfer, and copied back when device blocks free up, so the request resumes
+ * without recomputing its tokens; one that does not fit is soft-reset by the caller). A step's
+ * GPU work runs in this order: cb_copy_blocks, cb_swap_out_blocks (the step's swap-out pairs),
+ * cb_swap_in_blocks (its swap-in pairs), cb_cache_write, cb_paged_attention.
  *
  * Return values: CB_OK, CB_ERR_INVALID_ARG (null pointer, unknown or duplicate id, a rule above
  * broken, an output array too small) or CB_ERR_OUT_OF_BLOCKS (the pool cannot supply the blocks;
@@ -116,7 +127,28 @@ int cb_bm_build_batch(cb_block_manager* m, const int64_t* seq_ids, const int32_t
 int cb_bm_take_copies(cb_block_manager* m, int32_t* src, int32_t* dst, int32_t capacity,
                       int32_t* num_copies);
 
-/* Tokens, computed positions and table length of a sequence (each output may be NULL). */
+/* Sets the swap pool to num_slots host slots of one block each (K and V, every layer), all free.
+ * Refused while any slot holds data. */
+int cb_bm_set_swap_slots(cb_block_manager* m, int64_t num_slots);
+
+/* Swaps a sequence out: every block of its table, in order, goes to a free slot (lowest id
+ * first): blocks[i] -> slots[i] (host arrays of `capacity` entries), *num_pairs of them; its
+ * blocks are released. CB_ERR_OUT_OF_BLOCKS when the pool lacks free slots. */
+int cb_bm_swap_out(cb_block_manager* m, int64_t seq_id, int32_t* blocks, int32_t* slots,
+                   int32_t capacity, int32_t* num_pairs);
+
+/* Swaps a sequence back in: new blocks for its slots, slots[i] -> blocks[i] (host arrays of
+ * `capacity` entries) in table order; its computed positions stay computed. CB_ERR_OUT_OF_BLOCKS
+ * when the device pool cannot supply the blocks. */
+int cb_bm_swap_in(cb_block_manager* m, int64_t seq_id, int32_t* slots, int32_t* blocks,
+                  int32_t capacity, int32_t* num_pairs);
+
+/* Swap pool occupancy: free, used and held slots (each output may be NULL). */
+int cb_bm_swap_stats(const cb_block_manager* m, int64_t* free_slots, int64_t* used_slots,
+                     int64_t* held_slots);
+
+/* Tokens, computed positions and table length of a sequence (each output may be NULL; a swapped
+ * sequence has table length 0). */
 int cb_bm_sequence_info(const cb_block_manager* m, int64_t seq_id, int64_t* num_tokens,
                         int64_t* num_computed, int32_t* num_blocks);
 
@@ -148,6 +180,27 @@ int cb_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
                    const int32_t* dst_blocks, int32_t num_copies, int64_t block_bytes,
                    int64_t num_blocks, int32_t num_layers, int64_t layer_stride_bytes,
                    void* stream);
+
+/*
+ * cb_swap_out_blocks / cb_swap_in_blocks — the swap tier's transfers ("Continuous batching
+ * architecture", Offloading: a batched copy of offloaded requests' blocks to a pinned host pool,
+ * and back). host_pool: pinned host memory the GPU can address (hipHostMalloc; checked: anything
+ * else returns CB_ERR_INVALID_ARG), 16-byte aligned, laid out [num_slots][2 (K, V)][num_layers]
+ * [block_bytes]. Caches and layers as in cb_copy_blocks. blocks, slots: device int32
+ * [num_pairs]. Swap-out: for every pair and layer, slot slots[i] receives a bit copy of block
+ * blocks[i] of K and of V; swap-in: block blocks[i] receives slot slots[i]. Pairs with an id
+ * out of range are skipped; no slot (swap-out) or block (swap-in) may appear twice. The data
+ * crosses PCIe inside the kernel (device stores to, or loads from, host memory). Enqueued on
+ * `stream`; no allocation, no synchronization.
+ */
+int cb_swap_out_blocks(const void* k_cache, const void* v_cache, const int32_t* blocks,
+                       const int32_t* slots, int32_t num_pairs, void* host_pool, int64_t num_slots,
+                       int64_t block_bytes, int64_t num_blocks, int32_t num_layers,
+                       int64_t layer_stride_bytes, void* stream);
+int cb_swap_in_blocks(const void* host_pool, const int32_t* slots, const int32_t* blocks,
+                      int32_t num_pairs, void* k_cache, void* v_cache, int64_t num_slots,
+                      int64_t block_bytes, int64_t num_blocks, int32_t num_layers,
+                      int64_t layer_stride_bytes, void* stream);
 
 #ifdef __cplusplus
 }

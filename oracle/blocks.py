@@ -15,6 +15,10 @@ Plain Python, one step at a time, written from these passages:
   * "Continuous batching architecture", sections "Prefix caching" and "Eviction": freed blocks
     keep their content and key and count as free; cached blocks are given up only when the
     never-used blocks run out.
+  * same page, section "Offloading" (and "Continuous batching in transformers", the offload
+    paragraph): an offloaded request's KV blocks are copied to a pre-allocated pinned host pool,
+    all requests that fit in one batched transfer, and copied back when space frees up, so the
+    request resumes without recomputing its tokens; a request that does not fit is soft-reset.
 
 Where the pages leave a choice open, the reading taken (the library follows the same one):
   * never-used blocks go out lowest id first; the cached pool is evicted least recently freed
@@ -24,6 +28,11 @@ Where the pages leave a choice open, the reading taken (the library follows the 
     step yields that token's output);
   * a block's key here is the exact token prefix it completes (the library hashes it and checks
     the hit), every block that completes a prefix is keyed, and a lookup takes the lowest id;
+  * swap: every block of the victim is copied (shared ones too) into pool slots taken lowest id
+    first; its blocks are released (held, like copy sources, until the step closes, since the
+    step's gather reads them); swap-in takes new blocks, releases the slots (held until the step
+    closes), keys the full computed blocks again and counts them as written in the open step; a
+    swapped sequence cannot be appended to, forked or batched until it is swapped in;
   * the step protocol of the library header: KV is written by the GPU after the step closes,
     so keys become findable, copy sources leave the pools, and written blocks may be copied
     only after that; a copy whose source was written in the open step is refused; a sequence
@@ -67,6 +76,10 @@ class BlockManagerOracle:
         self.step_blocks: list[int] = []
         self.step_seqs: list[int] = []
         self.kv = [[None] * block_size for _ in range(num_blocks)]  # simulated cache
+        self.num_slots = 0
+        self.slot_state: list[int] = []        # 0 free, 1 used, 2 held until the step closes
+        self.swap_src: list[int] = []          # blocks the open step's gathers read
+        self.pool: list[list] = []             # simulated host pool
 
     # -- pools ------------------------------------------------------------------------------
     def _available(self) -> int:
@@ -87,7 +100,7 @@ class BlockManagerOracle:
     def _add_ref(self, b: int):
         if self.state[b] == CACHED:
             self.cached.remove(b)
-            self.state[b] = USED
+        self.state[b] = USED          # a held block found by a lookup is in use again
         self.ref[b] += 1
 
     def _to_pool(self, b: int):
@@ -108,9 +121,11 @@ class BlockManagerOracle:
         hits = [b for b in range(self.nb) if self.visible[b] and self.key[b] == prefix]
         return min(hits) if hits else None
 
-    def _seq(self, sid) -> dict:
+    def _seq(self, sid, swapped_ok: bool = False) -> dict:
         if sid not in self.seqs:
             raise BlockError(INVALID, "unknown sequence id")
+        if self.seqs[sid].get("swapped") and not swapped_ok:
+            raise BlockError(INVALID, "sequence is swapped out")
         return self.seqs[sid]
 
     # -- operations -------------------------------------------------------------------------
@@ -190,12 +205,68 @@ class BlockManagerOracle:
         self.seqs[child] = c
 
     def free_sequence(self, sid: int):
-        s = self._seq(sid)
+        s = self._seq(sid, swapped_ok=True)
         if s["in_batch"]:
             raise BlockError(INVALID, "sequence in the open step's batch")
         for b in reversed(s["table"]):
             self._release(b)
+        for slot in s.get("slots", []):
+            self.slot_state[slot] = 2
         del self.seqs[sid]
+
+    # -- swap tier ----------------------------------------------------------------------------
+    def set_swap_slots(self, n: int):
+        if any(s.get("swapped") for s in self.seqs.values()) or n < 0:
+            raise BlockError(INVALID, "cannot resize the pool now")
+        self.num_slots = n
+        self.slot_state = [0] * n
+        self.pool = [[None] * self.bs for _ in range(n)]
+
+    def swap_out(self, sid: int):
+        """Copies every block of the sequence to pool slots; returns [(block, slot)]."""
+        s = self._seq(sid)
+        if s["in_batch"] or any(self.dirty[b] for b in s["table"]):
+            raise BlockError(INVALID, "sequence has blocks written in the open step")
+        free = [i for i in range(self.num_slots) if self.slot_state[i] == 0]
+        if len(free) < len(s["table"]):
+            raise BlockError(OUT_OF_BLOCKS, "swap pool full")
+        pairs = list(zip(s["table"], free[:len(s["table"])]))
+        for b, slot in pairs:
+            self.slot_state[slot] = 1
+            self.pending[b] += 1
+            self.swap_src.append(b)
+        for b in reversed(s["table"]):
+            self._release(b)
+        s["slots"] = [slot for _, slot in pairs]
+        s["table"] = []
+        s["swapped"] = True
+        return pairs
+
+    def swap_in(self, sid: int):
+        """New blocks for a swapped sequence; returns [(slot, block)]."""
+        s = self._seq(sid, swapped_ok=True)
+        if not s.get("swapped"):
+            raise BlockError(INVALID, "sequence is not swapped out")
+        if len(s["slots"]) > self._available():
+            raise BlockError(OUT_OF_BLOCKS, "pool exhausted")
+        table = [self._take() for _ in s["slots"]]
+        pairs = list(zip(s["slots"], table))
+        for slot in s["slots"]:
+            self.slot_state[slot] = 2
+        for b in table:
+            self.dirty[b] = True
+            self.step_blocks.append(b)
+        s["table"], s["slots"], s["swapped"] = table, [], False
+        s["nkeys"] = 0
+        for j in range(s["computed"] // self.bs):   # key the computed full blocks again
+            b = table[j]
+            self.key[b] = tuple(s["tokens"][:(j + 1) * self.bs])
+            self.visible[b] = False
+        s["nkeys"] = s["computed"] // self.bs
+        return pairs
+
+    def swap_stats(self):
+        return (self.slot_state.count(0), self.slot_state.count(1), self.slot_state.count(2))
 
     def build_batch(self, seq_ids, q_lens, max_blocks_per_seq: int, token_capacity: int):
         """Returns (cu_seqlens_q, kv_lens, block_tables, slot_mapping, token_ids) as int32 arrays.
@@ -254,10 +325,12 @@ class BlockManagerOracle:
         if capacity is not None and len(self.copies) > capacity:
             raise BlockError(INVALID, "capacity too small")
         out = list(self.copies)
-        for src, _ in out:
+        for src in [s_ for s_, _ in out] + self.swap_src:
             self.pending[src] -= 1
             if self.pending[src] == 0 and self.state[src] == HELD:
                 self._to_pool(src)
+        self.swap_src = []
+        self.slot_state = [0 if st == 2 else st for st in self.slot_state]
         for b in self.step_blocks:
             self.dirty[b] = False
             if self.key[b] is not None:
@@ -274,18 +347,23 @@ class BlockManagerOracle:
         return self.state.count(FRESH), len(self.cached), held, len(self.seqs)
 
     def block_table(self, sid) -> list[int]:
-        return list(self._seq(sid)["table"])
+        return list(self._seq(sid, swapped_ok=True)["table"])
 
     def sequence_info(self, sid):
-        s = self._seq(sid)
+        s = self._seq(sid, swapped_ok=True)
         return len(s["tokens"]), s["computed"], len(s["table"])
 
     # -- the GPU's part of a step, simulated -------------------------------------------------
-    def apply_step(self, copies, batch):
-        """Copies first (whole blocks), then the batch's new KV at its slots: the KV of the
-        token at position p of a sequence is the tuple of that sequence's tokens 0..p."""
+    def apply_step(self, copies, batch, swap_outs=(), swap_ins=()):
+        """Copies first (whole blocks), then the swap gathers (block -> pool slot) and scatters
+        (pool slot -> block), then the batch's new KV at its slots: the KV of the token at
+        position p of a sequence is the tuple of that sequence's tokens 0..p."""
         for src, dst in copies:
             self.kv[dst] = list(self.kv[src])
+        for b, slot in swap_outs:
+            self.pool[slot] = list(self.kv[b])
+        for slot, b in swap_ins:
+            self.kv[b] = list(self.pool[slot])
         seq_ids, cu, slots = batch
         bs = self.bs
         for i, sid in enumerate(seq_ids):
@@ -301,6 +379,8 @@ class BlockManagerOracle:
         """Brute force: every computed position of every live sequence reads its own prefix."""
         bs = self.bs
         for sid, s in self.seqs.items():
+            if s.get("swapped"):
+                continue
             for p in range(s["computed"]):
                 b = s["table"][p // bs]
                 if self.kv[b][p % bs] != tuple(s["tokens"][:p + 1]):
@@ -340,4 +420,35 @@ def copy_blocks(k_cache, v_cache, src, dst):
         if 0 <= s < nb and 0 <= d < nb and s != d:
             kc[..., d, :, :, :] = k_cache[..., s, :, :, :]
             vc[..., d, :, :, :] = v_cache[..., s, :, :, :]
+    return kc, vc
+
+
+def swap_out_blocks(k_cache, v_cache, blocks, slots, pool):
+    """Pool after the swap-out gather ("Continuous batching architecture", Offloading: the
+    request's blocks are copied to the pinned host pool): slot slots[i] takes block blocks[i] of
+    K and of V in every layer. Caches [..., num_blocks, bs, Hkv, D] (leading layer axis allowed),
+    pool [num_slots, 2, layers, bs, Hkv, D]; pairs with an id out of range are skipped."""
+    out = np.array(pool, copy=True)
+    kc, vc = np.asarray(k_cache), np.asarray(v_cache)
+    if kc.ndim == 4:
+        kc, vc = kc[None], vc[None]
+    nb, ns = kc.shape[1], out.shape[0]
+    for b, sl in zip(np.asarray(blocks).tolist(), np.asarray(slots).tolist()):
+        if 0 <= b < nb and 0 <= sl < ns:
+            out[sl, 0] = kc[:, b]
+            out[sl, 1] = vc[:, b]
+    return out
+
+
+def swap_in_blocks(pool, slots, blocks, k_cache, v_cache):
+    """Caches after the swap-in scatter (the blocks are copied back to the GPU): block blocks[i]
+    takes slot slots[i] of K and of V in every layer; out-of-range pairs are skipped."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    kv, vv = (kc[None], vc[None]) if kc.ndim == 4 else (kc, vc)
+    p = np.asarray(pool)
+    nb, ns = kv.shape[1], p.shape[0]
+    for sl, b in zip(np.asarray(slots).tolist(), np.asarray(blocks).tolist()):
+        if 0 <= b < nb and 0 <= sl < ns:
+            kv[:, b] = p[sl, 0]
+            vv[:, b] = p[sl, 1]
     return kc, vc

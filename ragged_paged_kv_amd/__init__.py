@@ -27,6 +27,7 @@ __all__ = [
     "cb_paged_attention", "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
     "alloc_workspace", "EXPORTED_SYMBOLS", "CB_KERNEL_DECODE", "CB_KERNEL_PREFILL",
     "cb_copy_blocks", "BlockManager", "CB_ERR_OUT_OF_BLOCKS", "StepGraphs",
+    "cb_swap_out_blocks", "cb_swap_in_blocks",
 ]
 
 EXPORTED_SYMBOLS = (
@@ -38,6 +39,8 @@ EXPORTED_SYMBOLS = (
     "cb_bm_append_batch", "cb_bm_fork",
     "cb_bm_free_sequence", "cb_bm_build_batch", "cb_bm_take_copies", "cb_bm_sequence_info",
     "cb_bm_block_table", "cb_bm_stats", "cb_bm_ref_counts", "cb_copy_blocks",
+    "cb_bm_set_swap_slots", "cb_bm_swap_out", "cb_bm_swap_in", "cb_bm_swap_stats",
+    "cb_swap_out_blocks", "cb_swap_in_blocks",
     # include/cbgraphs.h
     "cb_graphs_create", "cb_graphs_destroy", "cb_graphs_run", "cb_graphs_stats",
 )
@@ -91,6 +94,12 @@ _sig = {
     "cb_bm_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
     "cb_bm_ref_counts": (ctypes.c_int, [_p, _p, _i64]),
     "cb_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i64, _i64, _i32, _i64, _p]),
+    "cb_bm_set_swap_slots": (ctypes.c_int, [_p, _i64]),
+    "cb_bm_swap_out": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p]),
+    "cb_bm_swap_in": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p]),
+    "cb_bm_swap_stats": (ctypes.c_int, [_p, _p, _p, _p]),
+    "cb_swap_out_blocks": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i64, _i64, _i64, _i32, _i64, _p]),
+    "cb_swap_in_blocks": (ctypes.c_int, [_p, _p, _p, _i32, _p, _p, _i64, _i64, _i64, _i32, _i64, _p]),
     "cb_graphs_create": (ctypes.c_int, [_p, _p]),
     "cb_graphs_destroy": (None, [_p]),
     "cb_graphs_run": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _p]),
@@ -402,6 +411,35 @@ class BlockManager:
         _check(lib.cb_bm_stats(self._h, *[ctypes.byref(x) for x in v]), "cb_bm_stats")
         return tuple(x.value for x in v)
 
+    def set_swap_slots(self, num_slots: int):
+        _check(lib.cb_bm_set_swap_slots(self._h, int(num_slots)), "cb_bm_set_swap_slots")
+
+    def _swap(self, fn, name, seq_id):
+        nb = self.sequence_info(seq_id)[2] if fn is lib.cb_bm_swap_out else None
+        cap = max(nb if nb is not None else self._swapped_len(seq_id), 1)
+        a, b = np.zeros(cap, np.int32), np.zeros(cap, np.int32)
+        n = ctypes.c_int32()
+        _check(fn(self._h, int(seq_id), _ptr(a), _ptr(b), cap, ctypes.byref(n)), name)
+        return a[:n.value], b[:n.value]
+
+    def _swapped_len(self, seq_id):
+        n, _, _ = self.sequence_info(seq_id)
+        return -(-n // self.block_size)
+
+    def swap_out(self, seq_id: int):
+        """(blocks, slots): copy block blocks[i] to pool slot slots[i]."""
+        return self._swap(lib.cb_bm_swap_out, "cb_bm_swap_out", seq_id)
+
+    def swap_in(self, seq_id: int):
+        """(slots, blocks): copy pool slot slots[i] to block blocks[i]."""
+        return self._swap(lib.cb_bm_swap_in, "cb_bm_swap_in", seq_id)
+
+    def swap_stats(self):
+        """(free, used, held) swap slots."""
+        v = [ctypes.c_int64() for _ in range(3)]
+        _check(lib.cb_bm_swap_stats(self._h, *[ctypes.byref(x) for x in v]), "cb_bm_swap_stats")
+        return tuple(x.value for x in v)
+
     def ref_counts(self):
         out = np.zeros(self.num_blocks, np.int32)
         _check(lib.cb_bm_ref_counts(self._h, _ptr(out), out.size), "cb_bm_ref_counts")
@@ -426,6 +464,49 @@ def cb_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, num_layers: int = 1
                               _dev(dst_blocks, "dst_blocks", torch.int32, 1), src_blocks.numel(),
                               block_bytes, NB, int(num_layers), layer_stride, _stream(stream)),
            "cb_copy_blocks")
+
+
+def _swap_shapes(k_cache, v_cache, pool, blocks, slots, num_layers):
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or blocks.shape != slots.shape:
+        raise ValueError("swap: inconsistent shapes")
+    nd = 5 if num_layers > 1 else 4
+    if k_cache.dim() != nd or (nd == 5 and k_cache.shape[0] != num_layers):
+        raise ValueError("swap: caches must be [NB, bs, Hkv, D] or [L, NB, bs, Hkv, D]")
+    NB = k_cache.shape[-4]
+    block_bytes = int(np.prod(k_cache.shape[-3:])) * k_cache.element_size()
+    if pool.device.type != "cpu" or not pool.is_pinned() or not pool.is_contiguous():
+        raise ValueError("swap: the pool must be a contiguous pinned host tensor")
+    if pool.dim() != 6 or tuple(pool.shape[1:]) != (2, num_layers) + tuple(k_cache.shape[-3:]) \
+            or pool.dtype != k_cache.dtype:
+        raise ValueError("swap: pool must be [num_slots, 2, L, bs, Hkv, D] of the caches' dtype")
+    return NB, block_bytes, NB * block_bytes
+
+
+def cb_swap_out_blocks(k_cache, v_cache, blocks, slots, pool, num_layers: int = 1, stream=None):
+    """Gather blocks[i] (K and V, every layer) into pool slot slots[i]; pool is a pinned host
+    tensor [num_slots, 2, L, bs, Hkv, D]; blocks, slots int32 device tensors."""
+    torch = _torch()
+    NB, bb, stride = _swap_shapes(k_cache, v_cache, pool, blocks, slots, num_layers)
+    nd = 5 if num_layers > 1 else 4
+    _check(lib.cb_swap_out_blocks(_dev(k_cache, "k_cache", torch.bfloat16, nd),
+                                  _dev(v_cache, "v_cache", torch.bfloat16, nd),
+                                  _dev(blocks, "blocks", torch.int32, 1), _dev(slots, "slots", torch.int32, 1),
+                                  blocks.numel(), ctypes.c_void_p(pool.data_ptr()), pool.shape[0], bb, NB,
+                                  int(num_layers), stride, _stream(stream)),
+           "cb_swap_out_blocks")
+
+
+def cb_swap_in_blocks(pool, slots, blocks, k_cache, v_cache, num_layers: int = 1, stream=None):
+    """Scatter pool slot slots[i] into block blocks[i] (K and V, every layer)."""
+    torch = _torch()
+    NB, bb, stride = _swap_shapes(k_cache, v_cache, pool, blocks, slots, num_layers)
+    nd = 5 if num_layers > 1 else 4
+    _check(lib.cb_swap_in_blocks(ctypes.c_void_p(pool.data_ptr()), _dev(slots, "slots", torch.int32, 1),
+                                 _dev(blocks, "blocks", torch.int32, 1), blocks.numel(),
+                                 _dev(k_cache, "k_cache", torch.bfloat16, nd),
+                                 _dev(v_cache, "v_cache", torch.bfloat16, nd), pool.shape[0], bb, NB,
+                                 int(num_layers), stride, _stream(stream)),
+           "cb_swap_in_blocks")
 
 
 # ---------------------------------------------------------------------------------------------

@@ -15,7 +15,12 @@
 //     holds the prompt's last token (that token is always computed);
 //   - a full block is keyed once its KV is computed (blocks holding the same prefix are all
 //     keyed; a lookup takes the lowest id) and is found by lookups only after the step that
-//     computes it has closed.
+//     computes it has closed;
+//   - swap tier ("Continuous batching architecture", Offloading): a swap-out copies every block
+//     of the sequence to host pool slots (lowest free id first) and releases the blocks, held
+//     until the step closes because the step's gather reads them; a swap-in takes new blocks,
+//     releases the slots (held until the step closes), keys the computed full blocks again and
+//     counts the blocks as written in the open step.
 // A full block's key is a chained 64-bit FNV-1a hash of its parent's key and its own tokens; a
 // hit is verified against the block's tokens and its parent's key.
 
@@ -37,6 +42,8 @@ struct cb_block_manager {
     int64_t computed = 0;        // leading positions whose KV is computed or in a built batch
     bool in_batch = false;       // part of a batch built since the step last closed
     uint64_t stamp = 0;          // the last cb_bm_build_batch call that named this sequence
+    bool swapped = false;        // its blocks live in host pool slots
+    std::vector<int32_t> slots;  // those slots, in table order
   };
 
   int64_t num_blocks = 0;
@@ -58,6 +65,12 @@ struct cb_block_manager {
   int64_t held = 0;                         // blocks in state kHeld
   uint64_t build_calls = 0;                 // cb_bm_build_batch calls so far
   std::vector<Seq*> batch;                  // scratch of cb_bm_build_batch
+  // swap pool
+  std::vector<uint8_t> slot_state;          // 0 free, 1 used, 2 held until the step closes
+  std::set<int32_t> free_slots;
+  std::vector<int32_t> held_slots;          // released in the open step
+  std::vector<int32_t> swap_src;            // blocks the open step's gathers read
+  int64_t swapped_seqs = 0;
 };
 
 namespace {
@@ -115,10 +128,9 @@ int32_t take_block(Mgr* m) {
 }
 
 void add_ref(Mgr* m, int32_t b) {
-  if (m->state[b] == kCached) {
-    m->lru.erase(m->lru_pos[b]);
-    m->state[b] = kUsed;
-  }
+  if (m->state[b] == kCached) m->lru.erase(m->lru_pos[b]);
+  if (m->state[b] == kHeld) --m->held;  // a held block found by a lookup is in use again
+  m->state[b] = kUsed;
   ++m->ref[b];
 }
 
@@ -263,6 +275,7 @@ extern "C" int cb_bm_append_tokens(cb_block_manager* m, int64_t seq_id, const in
   if (num_tokens > 0 && !tokens) return cb::fail(E, "tokens is NULL");
   Mgr::Seq* s = find_seq(m, seq_id);
   if (!s) return cb::fail(E, "unknown sequence id");
+  if (s->swapped) return cb::fail(E, "sequence is swapped out");
   if (num_tokens == 0) return cb::ok();
   const int32_t bs = m->bs;
   const int64_t len = (int64_t)s->tokens.size();
@@ -310,6 +323,7 @@ extern "C" int cb_bm_fork(cb_block_manager* m, int64_t parent, int64_t child) {
   if (!m) return cb::fail(E, "manager is NULL");
   Mgr::Seq* p = find_seq(m, parent);
   if (!p) return cb::fail(E, "unknown parent sequence id");
+  if (p->swapped) return cb::fail(E, "parent sequence is swapped out");
   if (m->seqs.count(child)) return cb::fail(E, "child sequence id already in use");
   if (p->computed != (int64_t)p->tokens.size())
     return cb::fail(E, "fork needs a parent whose every token is computed or in a built batch");
@@ -328,7 +342,106 @@ extern "C" int cb_bm_free_sequence(cb_block_manager* m, int64_t seq_id) {
     return cb::fail(E, "sequence is in a batch of the open step: close the step first");
   const auto& t = it->second.table;
   for (auto b = t.rbegin(); b != t.rend(); ++b) release(m, *b);
+  for (int32_t slot : it->second.slots) {
+    m->slot_state[slot] = 2;
+    m->held_slots.push_back(slot);
+  }
+  if (it->second.swapped) --m->swapped_seqs;
   m->seqs.erase(it);
+  return cb::ok();
+}
+
+extern "C" int cb_bm_set_swap_slots(cb_block_manager* m, int64_t num_slots) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  if (num_slots < 0 || num_slots > INT32_MAX) return cb::fail(E, "num_slots must be in [0, 2^31 - 1]");
+  if (m->swapped_seqs > 0 || !m->held_slots.empty())
+    return cb::fail(E, "the swap pool cannot be resized while it holds data");
+  m->slot_state.assign(num_slots, 0);
+  m->free_slots.clear();
+  for (int64_t i = 0; i < num_slots; ++i) m->free_slots.insert(m->free_slots.end(), (int32_t)i);
+  return cb::ok();
+}
+
+extern "C" int cb_bm_swap_out(cb_block_manager* m, int64_t seq_id, int32_t* blocks, int32_t* slots,
+                              int32_t capacity, int32_t* num_pairs) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  if (!num_pairs) return cb::fail(E, "num_pairs is NULL");
+  *num_pairs = 0;
+  Mgr::Seq* s = find_seq(m, seq_id);
+  if (!s) return cb::fail(E, "unknown sequence id");
+  if (s->swapped) return cb::fail(E, "sequence is swapped out");
+  bool dirty = s->in_batch;
+  for (int32_t b : s->table) dirty = dirty || m->dirty[b];
+  if (dirty) return cb::fail(E, "sequence has blocks written in the open step: close the step first");
+  const int32_t n = (int32_t)s->table.size();
+  if (n > capacity || (n > 0 && (!blocks || !slots)))
+    return cb::fail(E, "the output arrays hold fewer entries than the sequence's blocks");
+  if ((int64_t)m->free_slots.size() < n) return cb::fail(CB_ERR_OUT_OF_BLOCKS, "swap pool full");
+  s->slots.resize(n);
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t slot = *m->free_slots.begin();
+    m->free_slots.erase(m->free_slots.begin());
+    m->slot_state[slot] = 1;
+    const int32_t b = s->table[j];
+    ++m->pending[b];
+    m->swap_src.push_back(b);
+    blocks[j] = b;
+    slots[j] = slot;
+    s->slots[j] = slot;
+  }
+  for (auto b = s->table.rbegin(); b != s->table.rend(); ++b) release(m, *b);
+  s->table.clear();
+  s->swapped = true;
+  ++m->swapped_seqs;
+  *num_pairs = n;
+  return cb::ok();
+}
+
+extern "C" int cb_bm_swap_in(cb_block_manager* m, int64_t seq_id, int32_t* slots, int32_t* blocks,
+                             int32_t capacity, int32_t* num_pairs) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  if (!num_pairs) return cb::fail(E, "num_pairs is NULL");
+  *num_pairs = 0;
+  Mgr::Seq* s = find_seq(m, seq_id);
+  if (!s) return cb::fail(E, "unknown sequence id");
+  if (!s->swapped) return cb::fail(E, "sequence is not swapped out");
+  const int32_t n = (int32_t)s->slots.size();
+  if (n > available(m)) return cb::fail(CB_ERR_OUT_OF_BLOCKS, "not enough free KV blocks to swap in");
+  if (n > capacity || (n > 0 && (!blocks || !slots)))
+    return cb::fail(E, "the output arrays hold fewer entries than the sequence's slots");
+  s->table.resize(n);
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t b = take_block(m);
+    s->table[j] = b;
+    slots[j] = s->slots[j];
+    blocks[j] = b;
+    m->slot_state[s->slots[j]] = 2;
+    m->held_slots.push_back(s->slots[j]);
+    if (!m->dirty[b]) {
+      m->dirty[b] = 1;
+      m->step_blocks.push_back(b);
+    }
+  }
+  s->slots.clear();
+  s->swapped = false;
+  --m->swapped_seqs;
+  s->keys.clear();  // the computed full blocks are keyed again (found once the step closes)
+  key_computed_blocks(m, *s);
+  *num_pairs = n;
+  return cb::ok();
+}
+
+extern "C" int cb_bm_swap_stats(const cb_block_manager* m, int64_t* free_slots, int64_t* used_slots,
+                                int64_t* held_slots) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  int64_t used = 0, held = 0;
+  for (uint8_t st : m->slot_state) {
+    used += st == 1;
+    held += st == 2;
+  }
+  if (free_slots) *free_slots = (int64_t)m->free_slots.size();
+  if (used_slots) *used_slots = used;
+  if (held_slots) *held_slots = held;
   return cb::ok();
 }
 
@@ -349,6 +462,7 @@ extern "C" int cb_bm_build_batch(cb_block_manager* m, const int64_t* seq_ids, co
   for (int32_t i = 0; i < num_seqs; ++i) {
     Mgr::Seq* s = ss[i] = find_seq(m, seq_ids[i]);
     if (!s) return cb::fail(E, "unknown sequence id");
+    if (s->swapped) return cb::fail(E, "sequence is swapped out");
     if (s->stamp == stamp) return cb::fail(E, "a sequence appears twice in the batch");
     s->stamp = stamp;
     const int64_t left = (int64_t)s->tokens.size() - s->computed;
@@ -401,13 +515,19 @@ extern "C" int cb_bm_take_copies(cb_block_manager* m, int32_t* src, int32_t* dst
     src[i] = m->copy_src[i];
     dst[i] = m->copy_dst[i];
   }
-  for (int64_t i = 0; i < n; ++i) {
-    const int32_t b = m->copy_src[i];
+  for (int64_t i = 0; i < n + (int64_t)m->swap_src.size(); ++i) {
+    const int32_t b = i < n ? m->copy_src[i] : m->swap_src[i - n];
     if (--m->pending[b] == 0 && m->state[b] == kHeld) {
       --m->held;
       to_pool(m, b);
     }
   }
+  m->swap_src.clear();
+  for (int32_t slot : m->held_slots) {
+    m->slot_state[slot] = 0;
+    m->free_slots.insert(slot);
+  }
+  m->held_slots.clear();
   for (int32_t b : m->step_blocks) {
     m->dirty[b] = 0;
     if (m->keyed[b]) m->visible[b] = 1;

@@ -20,6 +20,7 @@ class Sim:
         self.m = ob.BlockManagerOracle(num_blocks, block_size)
         self.bs = block_size
         self.closed = {}   # sequence -> positions computed in closed steps
+        self.outs, self.ins = [], []   # the open step's swap gathers and scatters
 
     def add(self, sid, tokens):
         expect = self.expected_hit(tokens)
@@ -36,6 +37,17 @@ class Sim:
         self.m.free_sequence(sid)
         del self.closed[sid]
 
+    def swap_out(self, sid):
+        pairs = self.m.swap_out(sid)
+        self.outs += pairs
+        return pairs
+
+    def swap_in(self, sid):
+        pairs = self.m.swap_in(sid)
+        self.ins += pairs
+        self.closed[sid] = 0      # its new blocks are written by this step's scatter
+        return pairs
+
     def step(self, ids, qs, max_blocks=4096):
         cu, kv, bt, slots, toks = self.m.build_batch(ids, qs, max_blocks, int(sum(qs)))
         copies = self.m.take_copies()
@@ -43,7 +55,15 @@ class Sim:
         dsts = [d for _, d in copies]
         assert len(set(dsts)) == len(dsts), "two copies write one block"
         assert not set(dsts) & set(srcs), "a copy writes another copy's source"
-        self.m.apply_step(copies, (list(ids), cu, slots))
+        gathered = [b for b, _ in self.outs]
+        out_slots = [sl for _, sl in self.outs]
+        scattered = [b for _, b in self.ins]
+        assert len(set(out_slots)) == len(out_slots), "two gathers write one slot"
+        assert len(set(scattered)) == len(scattered), "two scatters write one block"
+        assert not set(scattered) & (set(gathered) | set(dsts) | set(srcs)), \
+            "a scatter writes a block another transfer of the step uses"
+        self.m.apply_step(copies, (list(ids), cu, slots), self.outs, self.ins)
+        self.outs, self.ins = [], []
         for sid in self.m.seqs:
             self.closed[sid] = self.m.seqs[sid]["computed"]
         self.check()
@@ -56,14 +76,16 @@ class Sim:
     def expected_hit(self, tokens):
         """Brute force from cache contents: the longest run of leading full blocks (short of the
         block holding the last token) each of which some block holds in full, where "holds"
-        means its simulated KV equals that prefix's and it sits in the cached pool or at that
-        index of a live sequence that computed it in a closed step."""
+        means its simulated KV equals that prefix's and it sits in the cached pool, is held
+        (released, read by a transfer of the open step) with a key, or sits at that index of a
+        live sequence that computed it in a closed step."""
         m, bs = self.m, self.bs
         n = len(tokens)
         j = 0
         while j < (n - 1) // bs:
             want = [tuple(tokens[:j * bs + o + 1]) for o in range(bs)]
-            cands = set(m.cached)
+            cands = set(m.cached) | {b for b in range(m.nb)
+                                     if m.state[b] == self.ob.HELD and m.key[b] is not None}
             for sid, s in m.seqs.items():
                 if len(s["table"]) > j and self.closed.get(sid, 0) >= (j + 1) * bs:
                     cands.add(s["table"][j])
@@ -286,6 +308,60 @@ def pin_protocol_rules(ob):
     assert m.stats()[2] == 0
 
 
+def pin_swap(ob):
+    """The offload tier: victims' blocks go to pool slots in one batched transfer, their device
+    blocks serve others meanwhile, and a swap-in resumes the request with nothing recomputed; a
+    request that does not fit the pool is refused (the caller soft-resets it)."""
+    bs = 4
+    sim = Sim(ob, 20, bs)
+    m = sim.m
+    m.set_swap_slots(6)
+
+    def refused(fn, *a, status=None):
+        try:
+            fn(*a)
+        except ob.BlockError as e:
+            return status is None or e.status == status
+        return False
+
+    A, B, C = [1, 2, 3, 4, 5, 6, 7], [9, 8, 7, 6, 5], [3, 3, 3, 3, 3, 3, 3, 3, 3]
+    E = [4, 4, 2, 2, 1]
+    for i, t in enumerate((A, B, C)):
+        sim.add(i, t)
+    sim.add(5, E)
+    sim.step([0, 1, 2, 5], [7, 5, 9, 5])
+    assert refused(m.swap_in, 0)                          # not swapped out
+    outs = sim.swap_out(0) + sim.swap_out(1)              # one batched transfer: 2 + 2 blocks
+    assert len(outs) == 4 and len({sl for _, sl in outs}) == 4
+    assert refused(m.swap_out, 2, status=ob.OUT_OF_BLOCKS)  # 3 blocks, 2 slots left
+    for fn, a in ((m.append_tokens, (0, [1])), (m.fork, (0, 7)), (m.build_batch, ([0], [1], 8, 1))):
+        assert refused(fn, *a, status=ob.INVALID)
+    assert m.sequence_info(0) == (7, 7, 0)
+    sim.step([], [])
+    free_after = m.stats()[0] + m.stats()[1]
+    assert free_after == 20 - 5                           # only C and E hold device blocks
+    # the victims' blocks serve a new request
+    D = [50 + i for i in range(16)]
+    sim.add(3, D)
+    sim.step([3], [16])
+    # swap A back in: nothing recomputed, its view is intact after the step's scatter
+    ins = sim.swap_in(0)
+    assert [sl for sl, _ in ins] == [sl for _, sl in outs[:2]]
+    assert m.sequence_info(0) == (7, 7, 2)
+    # A's slots are held until the step's scatter has read them: E's swap-out takes others
+    outs_e = sim.swap_out(5)
+    assert not {sl for _, sl in outs_e} & {sl for sl, _ in ins}
+    assert refused(m.swap_out, 0, status=ob.INVALID)      # its blocks are written this step
+    sim.step([], [])
+    m.append_tokens(0, [8])
+    sim.step([0], [1])
+    assert m.swap_stats() == (2, 4, 0)                    # B and E hold 2 slots each
+    # soft reset of C (freed, re-added with its tokens): its cached full blocks are reused
+    sim.free(2)
+    assert sim.add(4, C) == 8
+    sim.step([4], [1])
+
+
 def random_ops(rng, n_ops, vocab=3, bs=4, shared=(), max_prompt=14):
     """A random operation stream (host only): prompts from a few shared prefixes plus random
     suffixes over a tiny vocabulary, so prefixes collide often."""
@@ -300,8 +376,12 @@ def random_ops(rng, n_ops, vocab=3, bs=4, shared=(), max_prompt=14):
             ops.append(("append", [int(x) for x in rng.integers(0, vocab, rng.integers(1, 4))]))
         elif r < 0.45:
             ops.append(("append_batch", int(rng.integers(1, 1 << 30))))
-        elif r < 0.55:
+        elif r < 0.5:
             ops.append(("fork", None))
+        elif r < 0.53:
+            ops.append(("swap_out", None))
+        elif r < 0.56:
+            ops.append(("swap_in", None))
         elif r < 0.7:
             ops.append(("free", None))
         else:
@@ -314,6 +394,7 @@ def drive(sim_like, ops, rng_seed):
     (each raising an exception with .status on refusal); returns the log of outcomes."""
     rng = np.random.default_rng(rng_seed)
     live, next_id, log = [], 0, []
+    swapped = set()
     for kind, arg in ops:
         try:
             if kind == "add":
@@ -334,14 +415,20 @@ def drive(sim_like, ops, rng_seed):
                 out = sim_like.fork(sid, next_id)
                 live.append(next_id)
                 next_id += 1
+            elif kind in ("swap_out", "swap_in") and live:
+                pool = sorted(swapped) if kind == "swap_in" and swapped and rng.random() < 0.8 else live
+                sid = pool[rng.integers(len(pool))]
+                out = getattr(sim_like, kind)(sid)
+                (swapped.add if kind == "swap_out" else swapped.discard)(sid)
             elif kind == "free" and live:
                 sid = live[rng.integers(len(live))]
                 out = sim_like.free(sid)
                 live.remove(sid)
+                swapped.discard(sid)
             elif kind == "step":
-                pend = sim_like.pending(live)
+                pend = sim_like.pending([s for s in live if s not in swapped])
                 r2 = np.random.default_rng(arg)
-                ids = [s for s in live if pend[s] > 0 and r2.random() < 0.8]
+                ids = [s for s in live if s not in swapped and pend[s] > 0 and r2.random() < 0.8]
                 qs = [int(r2.integers(1, pend[s] + 1)) for s in ids]
                 out = sim_like.step(ids, qs)
             else:
@@ -373,6 +460,12 @@ class OracleDriver:
     def append_batch(self, ids, counts, toks):
         return self.sim.m.append_batch(ids, counts, toks)
 
+    def swap_out(self, sid):
+        return [tuple(p) for p in self.sim.swap_out(sid)]
+
+    def swap_in(self, sid):
+        return [tuple(p) for p in self.sim.swap_in(sid)]
+
     def fork(self, p, c):
         return self.sim.fork(p, c)
 
@@ -393,4 +486,6 @@ def pin_random_bruteforce(ob, seeds=range(12), n_ops=160):
         rng = np.random.default_rng(seed)
         shared = [list(rng.integers(0, 3, int(rng.integers(4, 12)))) for _ in range(3)]
         ops = random_ops(rng, n_ops, shared=shared)
-        drive(OracleDriver(ob, 40, 4), ops, seed + 1000)
+        d = OracleDriver(ob, 40, 4)
+        d.sim.m.set_swap_slots(24)
+        drive(d, ops, seed + 1000)

@@ -63,35 +63,72 @@ def contiguous_reference(seqs, ids, q_lens, kv_lens, q, src: KVSource, bs, scale
 
 
 class CpuBackend:
-    """The step's data path with the oracle's functions on numpy caches."""
+    """The step's data path with the oracle's functions on numpy caches and a numpy pool."""
 
-    def __init__(self, kc, vc):
+    def __init__(self, kc, vc, num_slots):
         self.kc, self.vc = kc, vc
+        self.pool = np.zeros((num_slots, 2, 1) + kc.shape[1:], np.uint16)
 
-    def step(self, src, dst, knew, vnew, slots, q, cu, kv_lens, tables, scale, max_q, max_kv):
+    def step(self, src, dst, outs, ins, knew, vnew, slots, q, cu, kv_lens, tables, scale, max_q,
+             max_kv):
         self.kc, self.vc = ob.copy_blocks(self.kc, self.vc, src, dst)
+        if len(outs[0]):
+            self.pool = ob.swap_out_blocks(self.kc, self.vc, outs[0], outs[1], self.pool)
+        if len(ins[0]):
+            self.kc, self.vc = ob.swap_in_blocks(self.pool, ins[0], ins[1], self.kc, self.vc)
         self.kc, self.vc = oracle.cache_write(self.kc, self.vc, knew, vnew, slots)
+        if q is None:
+            return None
         return oracle.paged_attention(q, cu, kv_lens, tables, self.kc, self.vc, scale)[0]
 
 
 def serving_run(cb, backend_factory, hq, hkv, d, bs, nb, n_steps=28, seed=0, log=print):
-    """Runs the steps; returns counters. backend_factory(kc, vc) takes the initial caches (stale
-    random data everywhere) and returns an object with step(...) -> float64 output."""
+    """Runs the steps; returns counters. backend_factory(kc, vc, num_slots) takes the initial
+    caches (stale random data everywhere) and the swap pool size, and returns an object with
+    step(...) -> float64 output."""
     rng = np.random.default_rng(seed)
     kvsrc = KVSource(seed + 7, hkv, d)
     scale = 1.0 / np.sqrt(d)
     m = cb.BlockManager(nb, bs)
-    backend = backend_factory(rand_bf16(rng, (nb, bs, hkv, d)), rand_bf16(rng, (nb, bs, hkv, d)))
+    num_slots = nb // 2
+    m.set_swap_slots(num_slots)
+    backend = backend_factory(rand_bf16(rng, (nb, bs, hkv, d)), rand_bf16(rng, (nb, bs, hkv, d)),
+                              num_slots)
     system = [int(x) for x in rng.integers(0, 50, 5 * bs + 3)]
-    seqs, live = {}, []
+    seqs, live, swapped = {}, [], []
     next_id = 0
-    stats = dict(hits=0, copies=0, steps=0, rows=0, refusals=0, forks=0)
+    stats = dict(hits=0, copies=0, steps=0, rows=0, refusals=0, forks=0, swap_outs=0, swap_ins=0)
 
     for step in range(n_steps):
+        outs, ins = ([], []), ([], [])
+        just_in = set()
         if step % 5 == 4 and len(live) > 3:
             sid = live[int(rng.integers(len(live)))]
             m.free_sequence(sid)
             live.remove(sid)
+        if step % 6 == 2 and len(live) > 2:       # offload one request
+            sid = live[int(rng.integers(len(live)))]
+            try:
+                b, sl = m.swap_out(sid)
+                outs = (outs[0] + b.tolist(), outs[1] + sl.tolist())
+                live.remove(sid)
+                swapped.append(sid)
+                stats["swap_outs"] += 1
+            except cb.CBError as e:
+                assert e.status == cb.CB_ERR_OUT_OF_BLOCKS
+                stats["refusals"] += 1
+        if step % 6 == 5 and swapped:             # and bring one back
+            sid = swapped[0]
+            try:
+                sl, b = m.swap_in(sid)
+                ins = (ins[0] + sl.tolist(), ins[1] + b.tolist())
+                swapped.remove(sid)
+                live.append(sid)
+                just_in.add(sid)
+                stats["swap_ins"] += 1
+            except cb.CBError as e:
+                assert e.status == cb.CB_ERR_OUT_OF_BLOCKS
+                stats["refusals"] += 1
         if step < n_steps - 8 and (step % 2 == 0 or len(live) < 2):
             own = [int(x) for x in rng.integers(0, 50, int(rng.integers(1, 3 * bs)))]
             tokens = (system if rng.random() < 0.8 else []) + own
@@ -105,7 +142,8 @@ def serving_run(cb, backend_factory, hq, hkv, d, bs, nb, n_steps=28, seed=0, log
             next_id += 1
         for sid in list(live):
             n, c, _ = m.sequence_info(sid)
-            if n == c and rng.random() < 0.2 and len(live) < 12:     # parallel sampling
+            # parallel sampling (not of a sequence whose blocks this step's scatter writes)
+            if n == c and sid not in just_in and rng.random() < 0.2 and len(live) < 12:
                 m.fork(sid, next_id)
                 seqs[next_id] = list(seqs[sid])
                 live.append(next_id)
@@ -128,7 +166,11 @@ def serving_run(cb, backend_factory, hq, hkv, d, bs, nb, n_steps=28, seed=0, log
                 ids.append(sid)
                 qs.append(min(n - c, 2 * bs + int(rng.integers(0, bs))))
         if not ids:
-            m.take_copies()
+            src, dst = m.take_copies()
+            if src.size or outs[0] or ins[0]:
+                backend.step(src, dst, outs, ins, np.zeros((0, hkv, d), np.uint16),
+                             np.zeros((0, hkv, d), np.uint16), np.zeros(0, np.int32), None, None,
+                             None, None, scale, 0, 0)
             continue
         mb = max(m.sequence_info(s)[2] for s in ids)
         cu, kv_lens, tables, slots, toks = m.build_batch(ids, qs, mb)
@@ -144,8 +186,8 @@ def serving_run(cb, backend_factory, hq, hkv, d, bs, nb, n_steps=28, seed=0, log
             assert toks[cu[i]:cu[i + 1]].tolist() == seqs[sid][L - q:L]
         qh = rand_bf16(np.random.default_rng(seed * 1000 + step), (T, hq, d))
         cb.cb_validate_batch(cu, kv_lens, tables, slots, bs, nb, max(qs), int(kv_lens.max()))
-        got = backend.step(src, dst, knew, vnew, slots, qh, cu, kv_lens, tables, scale, max(qs),
-                           int(kv_lens.max()))
+        got = backend.step(src, dst, outs, ins, knew, vnew, slots, qh, cu, kv_lens, tables, scale,
+                           max(qs), int(kv_lens.max()))
         ref = contiguous_reference(seqs, ids, qs, kv_lens, qh, kvsrc, bs, scale)
         ok, rep = oracle.within_tolerance(got, ref)
         assert ok, f"step {step}: {rep}"

@@ -28,6 +28,14 @@ class LibDriver:
     def append_batch(self, ids, counts, toks):
         return self.m.append_batch(ids, counts, toks)
 
+    def swap_out(self, sid):
+        a, b = self.m.swap_out(sid)
+        return list(zip(a.tolist(), b.tolist()))
+
+    def swap_in(self, sid):
+        a, b = self.m.swap_in(sid)
+        return list(zip(a.tolist(), b.tolist()))
+
     def fork(self, p, c):
         return self.m.fork(p, c)
 
@@ -53,6 +61,8 @@ def compare(seed, nb, bs, n_ops, vocab=3, max_prompt=14, n_shared=3):
     shared = [list(rng.integers(0, vocab, int(rng.integers(bs, 3 * bs)))) for _ in range(n_shared)]
     ops = random_ops(rng, n_ops, vocab=vocab, bs=bs, shared=shared, max_prompt=max_prompt)
     o, c = OracleDriver(ob, nb, bs), LibDriver(nb, bs)
+    o.sim.m.set_swap_slots(nb // 2)
+    c.m.set_swap_slots(nb // 2)
     lo = drive(o, ops, seed + 7)
     lc = drive(c, ops, seed + 7)
     assert len(lo) == len(lc)
@@ -62,6 +72,7 @@ def compare(seed, nb, bs, n_ops, vocab=3, max_prompt=14, n_shared=3):
         assert o.sim.m.block_table(sid) == c.m.block_table(sid).tolist()
         assert o.sim.m.sequence_info(sid) == c.m.sequence_info(sid)
     assert o.sim.m.stats() == c.m.stats()
+    assert o.sim.m.swap_stats() == c.m.swap_stats()
     return lo
 
 
@@ -179,6 +190,7 @@ def test_serving_steps_cpu_data_path(hq, hkv, d, bs, nb, seed):
     stats = serving_run(cb, CpuBackend, hq, hkv, d, bs, nb, n_steps=24, seed=seed,
                         log=lambda *a: None)
     assert stats["hits"] > 0 and stats["copies"] > 0 and stats["forks"] > 0
+    assert stats["swap_outs"] > 0 and stats["swap_ins"] > 0
 
 
 def test_copy_blocks_rejects_oversized_dispatch():

@@ -2,6 +2,8 @@
 exact), and serving steps driven by the library's block manager (prefix reuse, forks with
 copy-on-write, chunked prefill, decode, eviction) whose attention output, read through shared
 block tables, must match the oracle's attention over each sequence's own contiguous KV."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -50,12 +52,24 @@ def test_copy_blocks_bit_exact(layers, nb, bs, hkv, d, n):
 
 
 class GpuBackend:
-    def __init__(self, kc, vc):
+    def __init__(self, kc, vc, num_slots):
         self.kc, self.vc = dev_bf16(kc, "cuda"), dev_bf16(vc, "cuda")
+        self.pool = torch.zeros((num_slots, 2, 1) + tuple(self.kc.shape[1:]), dtype=torch.bfloat16,
+                                pin_memory=True)
 
-    def step(self, src, dst, knew, vnew, slots, q, cu, kv_lens, tables, scale, max_q, max_kv):
+    def step(self, src, dst, outs, ins, knew, vnew, slots, q, cu, kv_lens, tables, scale, max_q,
+             max_kv):
         if src.size:
             cb.cb_copy_blocks(self.kc, self.vc, dev_i32(src, "cuda"), dev_i32(dst, "cuda"))
+        if len(outs[0]):
+            cb.cb_swap_out_blocks(self.kc, self.vc, dev_i32(np.array(outs[0]), "cuda"),
+                                  dev_i32(np.array(outs[1]), "cuda"), self.pool)
+        if len(ins[0]):
+            cb.cb_swap_in_blocks(self.pool, dev_i32(np.array(ins[0]), "cuda"),
+                                 dev_i32(np.array(ins[1]), "cuda"), self.kc, self.vc)
+        if q is None:
+            torch.cuda.synchronize()
+            return None
         cb.cb_cache_write(dev_bf16(knew, "cuda"), dev_bf16(vnew, "cuda"), dev_i32(slots, "cuda"),
                           self.kc, self.vc)
         T, hq, d = q.shape
@@ -73,3 +87,48 @@ class GpuBackend:
 def test_serving_steps_through_block_manager(hq, hkv, d, bs, nb):
     stats = serving_run(cb, GpuBackend, hq, hkv, d, bs, nb, seed=hq * 100 + d + bs, log=say)
     assert stats["hits"] > 0 and stats["copies"] > 0 and stats["steps"] >= 20
+    assert stats["swap_outs"] > 0 and stats["swap_ins"] > 0
+
+
+@pytest.mark.parametrize("layers,nb,bs,hkv,d,n,num_slots", [
+    (1, 64, 16, 8, 128, 9, 20),       # 32 KiB blocks
+    (3, 40, 16, 2, 64, 5, 8),         # layer stride, 4 KiB blocks
+    (2, 512, 16, 8, 128, 200, 256),   # many pairs
+])
+def test_swap_blocks_bit_exact(layers, nb, bs, hkv, d, n, num_slots):
+    rng = np.random.default_rng(layers * 7 + nb + n)
+    shape = ((layers,) if layers > 1 else ()) + (nb, bs, hkv, d)
+    say(f"swap layers={layers} nb={nb} n={n} slots={num_slots}")
+    k, v = rand_bf16(rng, shape), rand_bf16(rng, shape)
+    pool0 = rand_bf16(rng, (num_slots, 2, layers, bs, hkv, d))
+    blocks = rng.permutation(nb)[:n].astype(np.int32)
+    slots = rng.permutation(num_slots)[:n].astype(np.int32)
+    # pairs with an id out of range are skipped (a block past the pool; a slot past the pool)
+    blocks_x = np.concatenate([blocks, [nb, 0]]).astype(np.int32)
+    slots_x = np.concatenate([slots, [int(slots[0]), num_slots]]).astype(np.int32)
+    pool = torch.from_numpy(pool0.view(np.int16)).view(torch.bfloat16).pin_memory()
+    kd, vd = dev_bf16(k, "cuda"), dev_bf16(v, "cuda")
+    cb.cb_swap_out_blocks(kd, vd, dev_i32(blocks_x, "cuda"), dev_i32(slots_x, "cuda"), pool,
+                          num_layers=layers)
+    torch.cuda.synchronize()
+    want_pool = ob.swap_out_blocks(k, v, blocks_x, slots_x, pool0)
+    assert np.array_equal(pool.view(torch.int16).numpy().view(np.uint16), want_pool)
+    # scatter back into other blocks
+    dst = rng.permutation(nb)[:n].astype(np.int32)
+    dst_x = np.concatenate([dst, [-1, nb]]).astype(np.int32)
+    cb.cb_swap_in_blocks(pool, dev_i32(slots_x, "cuda"), dev_i32(dst_x, "cuda"), kd, vd,
+                         num_layers=layers)
+    torch.cuda.synchronize()
+    ek, ev = ob.swap_in_blocks(want_pool, slots_x, dst_x, k, v)
+    assert np.array_equal(host_u16(kd), ek) and np.array_equal(host_u16(vd), ev)
+
+
+def test_swap_refuses_pageable_pool():
+    kd = torch.zeros((8, 16, 2, 64), dtype=torch.bfloat16, device="cuda")
+    idx = dev_i32(np.array([0], np.int32), "cuda")
+    pageable = np.zeros((2, 2, 1, 16, 2, 64), np.uint16)
+    st = cb.lib.cb_swap_out_blocks(ctypes.c_void_p(kd.data_ptr()), ctypes.c_void_p(kd.data_ptr()),
+                                   ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(idx.data_ptr()), 1,
+                                   ctypes.c_void_p(pageable.ctypes.data), 2, 16 * 2 * 64 * 2, 8, 1, 0,
+                                   None)
+    assert st == -1

@@ -8,7 +8,7 @@ import pytest
 from conftest import ROOT, read_golden
 from pins_blocks import (pin_block_table_example, pin_eviction_order, pin_fork_cow_example,
                          pin_last_token_block_not_reused, pin_prefix_worked_example,
-                         pin_protocol_rules, pin_random_bruteforce)
+                         pin_protocol_rules, pin_random_bruteforce, pin_swap)
 
 SRC = open(os.path.join(ROOT, "oracle", "blocks.py")).read()
 
@@ -22,7 +22,8 @@ MUTANTS = {
     # most recently freed cached block evicted first
     "mru-eviction": [("b = self.cached.pop(0)", "b = self.cached.pop()", 1)],
     # a sequence's blocks freed first block first
-    "free-forward": [('for b in reversed(s["table"]):', 'for b in s["table"]:', 1)],
+    "free-forward": [('raise BlockError(INVALID, "sequence in the open step\'s batch")\n        for b in reversed(s["table"]):',
+                      'raise BlockError(INVALID, "sequence in the open step\'s batch")\n        for b in s["table"]:', 1)],
     # an evicted block keeps its key
     "evict-keeps-key": [("            self.key[b] = None\n            self.visible[b] = False\n",
                          "", 1)],
@@ -43,6 +44,17 @@ MUTANTS = {
     "slot-offset": [("slots.append(b * bs + p % bs)", "slots.append(b * bs + (p - p0) % bs)", 1)],
     # fork does not take references
     "fork-no-ref": [('        for b in c["table"]:\n            self._add_ref(b)\n', "", 1)],
+    # a swapped-out block goes back to the pool before the step's gather has read it
+    "swap-no-hold": [("            self.pending[b] += 1\n            self.swap_src.append(b)\n", "", 1)],
+    # swapped-in blocks are not counted as written in the open step
+    "swap-in-not-dirty": [("        for b in table:\n            self.dirty[b] = True\n", "        for b in table:\n", 1)],
+    # slots released by a swap-in are free at once
+    "swap-slot-free-at-once": [("            self.slot_state[slot] = 2\n        for b in table:",
+                                "            self.slot_state[slot] = 0\n        for b in table:", 1)],
+    # a sequence with blocks written in the open step may be swapped out
+    "swap-out-dirty": [('if s["in_batch"] or any(self.dirty[b] for b in s["table"]):', 'if s["in_batch"]:', 1)],
+    # a swap-in reuses the sequence's old block ids instead of taking blocks
+    "swap-in-nothing-taken": [("table = [self._take() for _ in s[\"slots\"]]", "table = list(s[\"slots\"])", 1)],
 }
 
 
@@ -64,6 +76,7 @@ def caught(mod):
         lambda: pin_last_token_block_not_reused(mod),
         lambda: pin_eviction_order(mod),
         lambda: pin_protocol_rules(mod),
+        lambda: pin_swap(mod),
         lambda: pin_random_bruteforce(mod, seeds=range(6), n_ops=120),
     ]
     for pin in pins:
