@@ -31,6 +31,13 @@ Step graphs (its own JSON line, not the default run):
         through the Python binding and through the step-graph executor (one upload + one graph
         launch); wall time per step of back-to-back steps, and the GPU time per step.
 
+Async steps (its own JSON line, not the default run):
+    python bench.py --async [--steps K] [--warmup W]
+        64 decoding sequences of the Llama-3-8B shape (KV 512-2048): the CPU builds each step with
+        the block manager and the GPU runs carry-over + a stand-in embedding lookup + the attention
+        step + a stand-in greedy sampler; steps/s with each step waited for (synchronous) and with
+        step N+1 prepared and begun before step N's tokens are read (async).
+
 Measurement helpers (not part of the timed run):
     python bench.py --copy-calibration            # plain device copy of known size, for counters
     python bench.py --traffic-summary FETCH WRITE CFETCH CWRITE [--config N]
@@ -674,6 +681,110 @@ def bench_graphs(args):
     print(json.dumps(res), flush=True)
 
 
+ASYNC_SHAPE = dict(seqs=64, q_heads=32, kv_heads=8, head_dim=128, block_size=16, kv_lo=512,
+                   kv_hi=2048, vocab=32000)
+
+
+def bench_async(args):
+    """Synchronous vs async steps through the async runtime; prints one JSON line."""
+    import numpy as np
+    import torch
+    import ragged_paged_kv_amd as cb
+    sh = ASYNC_SHAPE
+    S, Hq, Hkv, D, bs, V = (sh[k] for k in ("seqs", "q_heads", "kv_heads", "head_dim",
+                                            "block_size", "vocab"))
+    steps = args.steps
+    rng = np.random.default_rng(11)
+    lens = rng.integers(sh["kv_lo"], sh["kv_hi"] + 1, S)
+    MB = -(-(sh["kv_hi"] + 2 * (steps + args.warmup) + 8) // bs)
+    NB = S * MB + 64
+    dev = "cuda"
+    kc = torch.randn((NB, bs, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.randn_like(kc)
+    T = 64
+    q = torch.zeros((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    out = torch.zeros_like(q)
+    eq = torch.randn((V, Hq, D), dtype=torch.bfloat16, device=dev)
+    ekv = torch.randn((V, Hkv, D), dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / np.sqrt(D)
+
+    def run(async_mode):
+        m = cb.BlockManager(NB, bs)
+        for i in range(S):   # prompts whose KV is taken as computed (the cache holds random KV)
+            m.add_sequence(i, rng.integers(0, V, int(lens[i])).tolist())
+        ids = np.arange(S, dtype=np.int64)
+        ones = np.ones(S, np.int32)
+        m.build_batch(ids, lens.astype(np.int32), MB)
+        m.take_copies()
+        bufs = (np.zeros(S + 1, np.int32), np.zeros(S, np.int32), np.full((S, MB), -1, np.int32),
+                np.zeros(S, np.int32), np.zeros(S, np.int32))
+        a = cb.AsyncSteps(q, k, v, out, kc, vc, scale, max_seqs=S + 8, max_kv_len=MB * bs,
+                          max_blocks_per_seq=MB)
+        tokens = np.zeros(S, np.int32)
+        dest = np.arange(S, dtype=np.int32)
+        pending = None
+        t_start = None
+        for n in range(steps + args.warmup):
+            if n == args.warmup:
+                torch.cuda.synchronize()
+                t_start = time.perf_counter()
+            # CPU preparation of step n: the manager appends each sequence's next token (known in
+            # the synchronous loop, a placeholder in the async one) and builds the batch
+            m.append_batch(ids, ones, tokens if not async_mode else np.zeros(S, np.int32))
+            cu, kv, tables, _, _ = m.build_batch(ids, ones, MB, out=bufs)
+            m.take_copies()
+            slot = a.slot()
+            a.in_ids_host[slot][:S].copy_(torch.from_numpy(tokens if not async_mode else np.zeros(S, np.int32)))
+            carried = S if (async_mode and n > 0) else 0
+            if carried:
+                a.carry_dest_host[slot][:S].copy_(torch.from_numpy(dest))
+            st = a.begin(cu, kv, tables, carried)
+            with torch.cuda.stream(st):
+                i = a.in_ids[slot][:S].long()
+                q[:S].copy_(eq[i])
+                k[:S].copy_(ekv[i])
+                v[:S].copy_(ekv[i])
+            a.attention()
+            with torch.cuda.stream(st):
+                a.out_ids[slot][:S].copy_((out[:S].float().sum(dim=1).argmax(dim=1) % V).to(torch.int32))
+            a.end(S)
+            if async_mode:
+                if pending is not None:                 # the previous step's tokens
+                    a.wait(pending)
+                    tokens = a.out_ids_host[pending][:S].numpy().copy()
+                pending = slot
+            else:
+                a.wait(slot)
+                tokens = a.out_ids_host[slot][:S].numpy().copy()
+        if pending is not None:
+            a.wait(pending)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t_start) / steps * 1e3
+        a.close()
+        return ms
+
+    sync_ms = run(False)
+    async_ms = run(True)
+    log(f"[bench] async steps: synchronous {sync_ms * 1e3:.1f} us/step, async {async_ms * 1e3:.1f} us/step "
+        f"({sync_ms / async_ms:.2f}x)")
+    res = {
+        "metric": "decode steps/s with async steps (CPU prepares step N+1 during step N)",
+        "value": round(1e3 / async_ms, 1), "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(async_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3-8b-decode-64seq-async", "num_seqs": S, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "block_size": bs,
+                   "step": "block manager prep + carry-over + stand-in embedding + attention step "
+                           "+ stand-in sampler"},
+        "synchronous_ms_per_step": round(sync_ms, 5), "async_ms_per_step": round(async_ms, 5),
+        "speedup": round(sync_ms / async_ms, 3),
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -687,6 +798,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR")
     ap.add_argument("--blocks", action="store_true", help="block copy and host manager measurement")
     ap.add_argument("--graphs", action="store_true", help="eager vs recorded steps, small decode batch")
+    ap.add_argument("--async", dest="async_steps", action="store_true",
+                    help="synchronous vs async steps with the block manager")
     args = ap.parse_args()
 
     if args.traffic_summary:
@@ -713,6 +826,9 @@ def main():
         return
     if args.graphs:
         bench_graphs(args)
+        return
+    if args.async_steps:
+        bench_async(args)
         return
 
     r = measure(args, args.config, args.steps, args.warmup)

@@ -27,7 +27,7 @@ __all__ = [
     "cb_paged_attention", "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
     "alloc_workspace", "EXPORTED_SYMBOLS", "CB_KERNEL_DECODE", "CB_KERNEL_PREFILL",
     "cb_copy_blocks", "BlockManager", "CB_ERR_OUT_OF_BLOCKS", "StepGraphs",
-    "cb_swap_out_blocks", "cb_swap_in_blocks",
+    "cb_swap_out_blocks", "cb_swap_in_blocks", "cb_carry_over", "AsyncSteps",
 ]
 
 EXPORTED_SYMBOLS = (
@@ -43,6 +43,9 @@ EXPORTED_SYMBOLS = (
     "cb_swap_out_blocks", "cb_swap_in_blocks",
     # include/cbgraphs.h
     "cb_graphs_create", "cb_graphs_destroy", "cb_graphs_run", "cb_graphs_stats",
+    # include/cbasync.h
+    "cb_carry_over", "cb_async_create", "cb_async_destroy", "cb_async_slot", "cb_async_begin",
+    "cb_async_attention", "cb_async_end", "cb_async_wait",
 )
 
 
@@ -104,6 +107,14 @@ _sig = {
     "cb_graphs_destroy": (None, [_p]),
     "cb_graphs_run": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _p]),
     "cb_graphs_stats": (ctypes.c_int, [_p, _p, _p, _p, _p]),
+    "cb_carry_over": (ctypes.c_int, [_p, _p, _i32, _p, _i32, _p]),
+    "cb_async_create": (ctypes.c_int, [_p, _p]),
+    "cb_async_destroy": (None, [_p]),
+    "cb_async_slot": (ctypes.c_int, [_p, _p]),
+    "cb_async_begin": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _p]),
+    "cb_async_attention": (ctypes.c_int, [_p]),
+    "cb_async_end": (ctypes.c_int, [_p, _i32]),
+    "cb_async_wait": (ctypes.c_int, [_p, _i32]),
 }
 
 CB_KERNEL_DECODE = 1
@@ -527,6 +538,24 @@ class GraphsConfig(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
 
 
+def _graphs_config(q, k, v, out, k_cache, v_cache, scale, max_seqs, max_kv_len,
+                   max_blocks_per_seq, token_interval, kv_interval, seq_interval, max_graphs,
+                   use_graphs):
+    torch = _torch()
+    T, Hq, D = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D) \
+            or tuple(out.shape) != (T, Hq, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("step configuration: inconsistent shapes")
+    return GraphsConfig(Hq, Hkv, D, bs, NB, int(max_blocks_per_seq), T, int(max_seqs),
+                        int(max_kv_len), int(token_interval), int(kv_interval), int(seq_interval),
+                        int(max_graphs), int(bool(use_graphs)), float(scale),
+                        _dev(q, "q", torch.bfloat16, 3), _dev(k, "k", torch.bfloat16, 3),
+                        _dev(v, "v", torch.bfloat16, 3), _dev(out, "out", torch.bfloat16, 3),
+                        _dev(k_cache, "k_cache", torch.bfloat16, 4),
+                        _dev(v_cache, "v_cache", torch.bfloat16, 4))
+
+
 class StepGraphs:
     """Owner of one cb_step_graphs executor over fixed torch buffers (kept referenced here):
     q [max_tokens, Hq, D], k, v [max_tokens, Hkv, D], out [max_tokens, Hq, D], caches
@@ -544,13 +573,9 @@ class StepGraphs:
                 or tuple(out.shape) != (T, Hq, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
             raise ValueError("StepGraphs: inconsistent shapes")
         self._bufs = (q, k, v, out, k_cache, v_cache)
-        cfg = GraphsConfig(Hq, Hkv, D, bs, NB, int(max_blocks_per_seq), T, int(max_seqs),
-                           int(max_kv_len), int(token_interval), int(kv_interval),
-                           int(seq_interval), int(max_graphs), int(bool(use_graphs)), float(scale),
-                           _dev(q, "q", torch.bfloat16, 3), _dev(k, "k", torch.bfloat16, 3),
-                           _dev(v, "v", torch.bfloat16, 3), _dev(out, "out", torch.bfloat16, 3),
-                           _dev(k_cache, "k_cache", torch.bfloat16, 4),
-                           _dev(v_cache, "v_cache", torch.bfloat16, 4))
+        cfg = _graphs_config(q, k, v, out, k_cache, v_cache, scale, max_seqs, max_kv_len,
+                             max_blocks_per_seq, token_interval, kv_interval, seq_interval,
+                             max_graphs, use_graphs)
         h = ctypes.c_void_p()
         _check(lib.cb_graphs_create(ctypes.byref(cfg), ctypes.byref(h)), "cb_graphs_create")
         self._h = h
@@ -585,3 +610,93 @@ class StepGraphs:
         _check(lib.cb_graphs_stats(self._h, ctypes.byref(c), ctypes.byref(r), ctypes.byref(e),
                                    ctypes.byref(n)), "cb_graphs_stats")
         return c.value, r.value, e.value, n.value
+
+
+# ---------------------------------------------------------------------------------------------
+# async steps (include/cbasync.h)
+
+
+def cb_carry_over(prev_outputs, dest, next_inputs, num_prev=None, num_next=None, stream=None):
+    """next_inputs[dest[i]] += prev_outputs[i] for dest[i] >= 0 (int32 device tensors)."""
+    torch = _torch()
+    n = dest.numel() if num_prev is None else int(num_prev)
+    m = next_inputs.numel() if num_next is None else int(num_next)
+    _check(lib.cb_carry_over(_dev(prev_outputs, "prev_outputs", torch.int32, 1),
+                             _dev(dest, "dest", torch.int32, 1), n,
+                             _dev(next_inputs, "next_inputs", torch.int32, 1), m, _stream(stream)),
+           "cb_carry_over")
+
+
+class AsyncConfig(ctypes.Structure):
+    """cb_async_config, field for field."""
+    _fields_ = [("step", GraphsConfig)] + [(name, ctypes.c_void_p * 2) for name in (
+        "in_ids", "out_ids", "carry_dest", "in_ids_host", "carry_dest_host", "out_ids_host")]
+
+
+class AsyncSteps:
+    """Owner of one cb_async_steps runtime over fixed torch buffers (as StepGraphs), with its
+    A/B token buffers allocated here: in_ids, out_ids, carry_dest (device int32 [2][max_tokens])
+    and in_ids_host, carry_dest_host, out_ids_host (pinned host int32 [2][max_tokens])."""
+
+    def __init__(self, q, k, v, out, k_cache, v_cache, scale: float, max_seqs: int,
+                 max_kv_len: int, max_blocks_per_seq: int, token_interval: int = 16,
+                 kv_interval: int = 256, seq_interval: int = 8, max_graphs: int = 32,
+                 use_graphs: bool = False):
+        torch = _torch()
+        T = q.shape[0]
+        dev = q.device
+        self.in_ids = [torch.zeros(T, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.out_ids = [torch.zeros(T, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.carry_dest = [torch.full((T,), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.in_ids_host = [torch.zeros(T, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.carry_dest_host = [torch.full((T,), -1, dtype=torch.int32).pin_memory() for _ in range(2)]
+        self.out_ids_host = [torch.zeros(T, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self._bufs = (q, k, v, out, k_cache, v_cache)
+        step = _graphs_config(q, k, v, out, k_cache, v_cache, scale, max_seqs, max_kv_len,
+                              max_blocks_per_seq, token_interval, kv_interval, seq_interval,
+                              max_graphs, use_graphs)
+        ptrs = lambda ts: (ctypes.c_void_p * 2)(*[t.data_ptr() for t in ts])  # noqa: E731
+        cfg = AsyncConfig(step, ptrs(self.in_ids), ptrs(self.out_ids), ptrs(self.carry_dest),
+                          ptrs(self.in_ids_host), ptrs(self.carry_dest_host), ptrs(self.out_ids_host))
+        h = ctypes.c_void_p()
+        _check(lib.cb_async_create(ctypes.byref(cfg), ctypes.byref(h)), "cb_async_create")
+        self._h = h
+        self._destroy = lib.cb_async_destroy
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+        self.compute_stream = None
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def slot(self) -> int:
+        s = ctypes.c_int32()
+        _check(lib.cb_async_slot(self._h, ctypes.byref(s)), "cb_async_slot")
+        return s.value
+
+    def begin(self, cu_seqlens_q, kv_lens, block_tables, num_carried: int):
+        """Uploads the step's inputs and runs the carry-over; returns the compute stream as a
+        torch stream for the caller's work."""
+        cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+        kv = np.ascontiguousarray(kv_lens, dtype=np.int32)
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        if cu.size != kv.size + 1 or bt.shape != (kv.size, self.max_blocks_per_seq):
+            raise ValueError("AsyncSteps.begin: inconsistent metadata shapes")
+        st = ctypes.c_void_p()
+        _check(lib.cb_async_begin(self._h, _ptr(cu), _ptr(kv), _ptr(bt), kv.size, int(num_carried),
+                                  ctypes.byref(st)), "cb_async_begin")
+        if self.compute_stream is None:
+            self.compute_stream = _torch().cuda.ExternalStream(st.value)
+        return self.compute_stream
+
+    def attention(self):
+        _check(lib.cb_async_attention(self._h), "cb_async_attention")
+
+    def end(self, num_outputs: int):
+        _check(lib.cb_async_end(self._h, int(num_outputs)), "cb_async_end")
+
+    def wait(self, slot: int):
+        _check(lib.cb_async_wait(self._h, int(slot)), "cb_async_wait")

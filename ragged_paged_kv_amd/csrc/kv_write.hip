@@ -53,7 +53,31 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   dst[(int64_t)slot * chunks_per_row + c] = src[t * chunks_per_row + c];
 }
 
+// One thread per output of the previous step (see cb_carry_over).
+__global__ __launch_bounds__(256) void carry_over_kernel(const int32_t* __restrict__ prev_out,
+                                                         const int32_t* __restrict__ dest,
+                                                         int32_t n, int32_t* __restrict__ next_in,
+                                                         int32_t n_next) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t d = dest[i];
+  if (d >= 0 && d < n_next) next_in[d] += prev_out[i];
+}
+
 }  // namespace
+
+extern "C" int cb_carry_over(const int32_t* prev_outputs, const int32_t* dest, int32_t num_prev,
+                             int32_t* next_inputs, int32_t num_next, void* stream) {
+  using cb::fail;
+  if (num_prev < 0 || num_next < 0) return fail(CB_ERR_INVALID_ARG, "cb_carry_over: negative size");
+  if (num_prev == 0 || num_next == 0) return cb::ok();
+  if (!prev_outputs || !dest || !next_inputs) return fail(CB_ERR_INVALID_ARG, "cb_carry_over: NULL pointer");
+  carry_over_kernel<<<(num_prev + 255) / 256, 256, 0, (hipStream_t)stream>>>(prev_outputs, dest, num_prev,
+                                                                           next_inputs, num_next);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CB_ERR_HIP, std::string("carry_over launch: ") + hipGetErrorString(e));
+  return cb::ok();
+}
 
 extern "C" int cb_slot_mapping(const int32_t* cu_seqlens_q, const int32_t* kv_lens,
                                const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,

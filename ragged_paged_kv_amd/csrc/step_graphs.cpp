@@ -200,16 +200,13 @@ extern "C" void cb_graphs_destroy(cb_step_graphs* g) {
   delete g;
 }
 
-extern "C" int cb_graphs_run(cb_step_graphs* g, const int32_t* cu_seqlens_q, const int32_t* kv_lens,
-                             const int32_t* block_tables, int32_t num_seqs, void* stream,
-                             int32_t* padded_shape) {
-  if (!g) return cb::fail(E, "executor is NULL");
+namespace {
+
+// Checks and pads a step's host metadata and uploads it on `upload` (the executor's metadata
+// buffers); *key receives the padded shape.
+int prepare(G* g, const int32_t* cu_seqlens_q, const int32_t* kv_lens, const int32_t* block_tables,
+            int32_t num_seqs, hipStream_t upload, Key* key) {
   const auto& c = g->cfg;
-  if (num_seqs < 0) return cb::fail(E, "num_seqs must be >= 0");
-  if (num_seqs > 0 && (!cu_seqlens_q || !kv_lens || !block_tables)) return cb::fail(E, "NULL array");
-  hipStream_t st = (hipStream_t)stream;
-  if (!st) return cb::fail(E, "cb_graphs_run needs a stream other than NULL (NULL cannot be recorded)");
-  if (num_seqs == 0) return cb::ok();
   const int32_t T = cu_seqlens_q[num_seqs];
   if (cu_seqlens_q[0] != 0 || T < 1 || T > c.max_tokens)
     return cb::fail(E, "cu_seqlens_q must start at 0 and end in [1, max_tokens]");
@@ -232,13 +229,7 @@ extern "C" int cb_graphs_run(cb_step_graphs* g, const int32_t* cu_seqlens_q, con
   while (mq2 < max_q) mq2 *= 2;
   const int32_t mqb = std::min(mq2, Tb);
   const int32_t mkvb = (int32_t)std::min<int64_t>(round_up(max_kv, c.kv_interval), c.max_kv_len);
-  const Key key{Sb, Tb, mqb, mkvb};
-  if (padded_shape) {
-    padded_shape[0] = Sb;
-    padded_shape[1] = Tb;
-    padded_shape[2] = mqb;
-    padded_shape[3] = mkvb;
-  }
+  *key = Key{Sb, Tb, mqb, mkvb};
 
   // metadata of the padded batch into a staging slot whose previous copy has run
   const int slot = g->next_slot;
@@ -259,12 +250,19 @@ extern "C" int cb_graphs_run(cb_step_graphs* g, const int32_t* cu_seqlens_q, con
   std::fill(htab + (size_t)num_seqs * MB, htab + (size_t)Sb * MB, -1);
   // the device copy: cu and kv_lens whole-capacity prefixes, tables for Sb rows
   const size_t head = (size_t)c.max_seqs + 1 + c.max_seqs;
-  if (hipMemcpyAsync(g->meta, hcu, sizeof(int32_t) * (head + (size_t)Sb * MB), hipMemcpyHostToDevice, st) != hipSuccess ||
-      hipEventRecord(g->staged[slot], st) != hipSuccess)
+  if (hipMemcpyAsync(g->meta, hcu, sizeof(int32_t) * (head + (size_t)Sb * MB), hipMemcpyHostToDevice, upload) != hipSuccess ||
+      hipEventRecord(g->staged[slot], upload) != hipSuccess)
     return cb::fail(CB_ERR_HIP, "metadata upload failed");
+  return CB_OK;
+}
 
-  const size_t need = cb_paged_attention_workspace_size(Sb, Tb, c.num_q_heads, c.num_kv_heads,
-                                                       c.head_dim, c.block_size, mqb, mkvb, 0);
+// Runs the padded step `key` on `st` (after its metadata upload): eagerly, by recording or by
+// replay.
+int launch(G* g, const Key& key, hipStream_t st) {
+  const auto& c = g->cfg;
+  const size_t need = cb_paged_attention_workspace_size(std::get<0>(key), std::get<1>(key), c.num_q_heads,
+                                                       c.num_kv_heads, c.head_dim, c.block_size,
+                                                       std::get<2>(key), std::get<3>(key), 0);
   int r = ensure_workspace(g, need, st);
   if (r != CB_OK) return r;
   if (!c.use_graphs) {  // direct launches: the same padded step, no recording
@@ -309,6 +307,29 @@ extern "C" int cb_graphs_run(cb_step_graphs* g, const int32_t* cu_seqlens_q, con
   return cb::ok();
 }
 
+}  // namespace
+
+extern "C" int cb_graphs_run(cb_step_graphs* g, const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                             const int32_t* block_tables, int32_t num_seqs, void* stream,
+                             int32_t* padded_shape) {
+  if (!g) return cb::fail(E, "executor is NULL");
+  if (num_seqs < 0) return cb::fail(E, "num_seqs must be >= 0");
+  if (num_seqs > 0 && (!cu_seqlens_q || !kv_lens || !block_tables)) return cb::fail(E, "NULL array");
+  hipStream_t st = (hipStream_t)stream;
+  if (!st) return cb::fail(E, "cb_graphs_run needs a stream other than NULL (NULL cannot be recorded)");
+  if (num_seqs == 0) return cb::ok();
+  Key key;
+  int r = prepare(g, cu_seqlens_q, kv_lens, block_tables, num_seqs, st, &key);
+  if (r != CB_OK) return r;
+  if (padded_shape) {
+    padded_shape[0] = std::get<0>(key);
+    padded_shape[1] = std::get<1>(key);
+    padded_shape[2] = std::get<2>(key);
+    padded_shape[3] = std::get<3>(key);
+  }
+  return launch(g, key, st);
+}
+
 extern "C" int cb_graphs_stats(const cb_step_graphs* g, int64_t* captures, int64_t* replays,
                                int64_t* eager_runs, int32_t* cached) {
   if (!g) return cb::fail(E, "executor is NULL");
@@ -316,5 +337,179 @@ extern "C" int cb_graphs_stats(const cb_step_graphs* g, int64_t* captures, int64
   if (replays) *replays = g->replays;
   if (eager_runs) *eager_runs = g->eager;
   if (cached) *cached = (int32_t)g->graphs.size();
+  return cb::ok();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Async steps ("Continuous batching in transformers", Async batching): the CPU prepares step
+// N + 1 while the GPU computes step N. Three streams (upload, compute, download) and, per I/O
+// slot, three events (upload over, compute over, download over); two I/O slots used alternately
+// (A/B), each with its own step executor (metadata buffers and recorded graphs: a graph records
+// one slot's addresses); the carry-over adds the tokens step N produces into step N + 1's inputs
+// on the compute stream, before the caller's forward pass.
+
+#include "cbasync.h"
+
+struct cb_async_steps {
+  cb_async_config cfg{};
+  cb_step_graphs* ex[2] = {nullptr, nullptr};
+  hipStream_t up = nullptr, compute = nullptr, down = nullptr;
+  hipEvent_t up_over[2] = {nullptr, nullptr}, compute_over[2] = {nullptr, nullptr},
+             down_over[2] = {nullptr, nullptr};
+  int64_t steps = 0;  // steps ended
+  int open = -1;      // slot of the step begun and not yet ended
+  bool attended = false;
+  Key key{};
+  int32_t tokens = 0;
+};
+
+namespace {
+
+using A = cb_async_steps;
+
+void async_release(A* a) {
+  for (hipStream_t s : {a->up, a->compute, a->down})
+    if (s) (void)hipStreamSynchronize(s);
+  for (int i = 0; i < 2; ++i) {
+    cb_graphs_destroy(a->ex[i]);
+    for (hipEvent_t e : {a->up_over[i], a->compute_over[i], a->down_over[i]})
+      if (e) (void)hipEventDestroy(e);
+  }
+  for (hipStream_t s : {a->up, a->compute, a->down})
+    if (s) (void)hipStreamDestroy(s);
+}
+
+bool pinned_host(const void* p) {
+  hipPointerAttribute_t attr{};
+  const bool ok = hipPointerGetAttributes(&attr, p) == hipSuccess && attr.type == hipMemoryTypeHost;
+  if (!ok) (void)hipGetLastError();
+  return ok;
+}
+
+}  // namespace
+
+extern "C" int cb_async_create(const cb_async_config* cfg, cb_async_steps** out) {
+  if (!out) return cb::fail(E, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return cb::fail(E, "cfg is NULL");
+  for (int i = 0; i < 2; ++i) {
+    if (!cfg->in_ids[i] || !cfg->out_ids[i] || !cfg->carry_dest[i] || !cfg->in_ids_host[i] ||
+        !cfg->carry_dest_host[i] || !cfg->out_ids_host[i])
+      return cb::fail(E, "cb_async_create: NULL buffer");
+  }
+  A* a = new (std::nothrow) A;
+  if (!a) return cb::fail(E, "out of host memory");
+  a->cfg = *cfg;
+  for (int i = 0; i < 2; ++i) {
+    const int r = cb_graphs_create(&cfg->step, &a->ex[i]);
+    if (r != CB_OK) {
+      async_release(a);
+      delete a;
+      return r;
+    }
+  }
+  for (int i = 0; i < 2; ++i)
+    if (!pinned_host(cfg->in_ids_host[i]) || !pinned_host(cfg->carry_dest_host[i]) ||
+        !pinned_host(cfg->out_ids_host[i])) {
+      async_release(a);
+      delete a;
+      return cb::fail(E, "cb_async_create: host buffers must be pinned (hipHostMalloc)");
+    }
+  bool ok = true;
+  for (hipStream_t* s : {&a->up, &a->compute, &a->down})
+    ok = ok && hipStreamCreateWithFlags(s, hipStreamNonBlocking) == hipSuccess;
+  for (int i = 0; i < 2; ++i)
+    for (hipEvent_t* e : {&a->up_over[i], &a->compute_over[i], &a->down_over[i]})
+      ok = ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    async_release(a);
+    delete a;
+    return cb::fail(CB_ERR_HIP, "cb_async_create: stream or event creation failed");
+  }
+  *out = a;
+  return cb::ok();
+}
+
+extern "C" void cb_async_destroy(cb_async_steps* a) {
+  if (!a) return;
+  async_release(a);
+  delete a;
+}
+
+extern "C" int cb_async_slot(cb_async_steps* a, int32_t* slot) {
+  if (!a || !slot) return cb::fail(E, "NULL argument");
+  const int s = (int)(a->steps % 2);
+  // the slot's host inputs were read by its previous upload: wait for that copy
+  if (hipEventSynchronize(a->up_over[s]) != hipSuccess) return cb::fail(CB_ERR_HIP, "upload wait failed");
+  *slot = s;
+  return cb::ok();
+}
+
+extern "C" int cb_async_begin(cb_async_steps* a, const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                              const int32_t* block_tables, int32_t num_seqs, int32_t num_carried,
+                              void** compute_stream) {
+  if (!a) return cb::fail(E, "NULL handle");
+  if (a->open >= 0) return cb::fail(E, "the previous step has not ended (cb_async_end)");
+  if (num_seqs < 1 || !cu_seqlens_q || !kv_lens || !block_tables)
+    return cb::fail(E, "a step needs at least one sequence and its metadata");
+  const int32_t max_t = a->cfg.step.max_tokens;
+  if (num_carried < 0 || num_carried > max_t || (a->steps == 0 && num_carried > 0))
+    return cb::fail(E, "num_carried must be in [0, max_tokens] (0 for the first step)");
+  const int s = (int)(a->steps % 2), prev = 1 - s;
+  // the slot's device inputs are free once its previous step's compute has read them
+  if (hipStreamWaitEvent(a->up, a->compute_over[s], 0) != hipSuccess)
+    return cb::fail(CB_ERR_HIP, "upload stream wait failed");
+  Key key;
+  int r = prepare(a->ex[s], cu_seqlens_q, kv_lens, block_tables, num_seqs, a->up, &key);
+  if (r != CB_OK) return r;
+  const int32_t T = cu_seqlens_q[num_seqs];
+  if (hipMemcpyAsync(a->cfg.in_ids[s], a->cfg.in_ids_host[s], sizeof(int32_t) * T,
+                     hipMemcpyHostToDevice, a->up) != hipSuccess ||
+      (num_carried > 0 && hipMemcpyAsync(a->cfg.carry_dest[s], a->cfg.carry_dest_host[s],
+                                         sizeof(int32_t) * num_carried, hipMemcpyHostToDevice, a->up) != hipSuccess) ||
+      hipEventRecord(a->up_over[s], a->up) != hipSuccess ||
+      hipStreamWaitEvent(a->compute, a->up_over[s], 0) != hipSuccess)
+    return cb::fail(CB_ERR_HIP, "input upload failed");
+  // carry-over: the previous step's output tokens into this step's placeholders
+  r = cb_carry_over(a->cfg.out_ids[prev], a->cfg.carry_dest[s], num_carried, a->cfg.in_ids[s], T,
+                    a->compute);
+  if (r != CB_OK) return r;
+  a->open = s;
+  a->attended = false;
+  a->key = key;
+  a->tokens = T;
+  if (compute_stream) *compute_stream = a->compute;
+  return cb::ok();
+}
+
+extern "C" int cb_async_attention(cb_async_steps* a) {
+  if (!a) return cb::fail(E, "NULL handle");
+  if (a->open < 0 || a->attended) return cb::fail(E, "no begun step awaits its attention");
+  const int r = launch(a->ex[a->open], a->key, a->compute);
+  if (r != CB_OK) return r;
+  a->attended = true;
+  return cb::ok();
+}
+
+extern "C" int cb_async_end(cb_async_steps* a, int32_t num_outputs) {
+  if (!a) return cb::fail(E, "NULL handle");
+  if (a->open < 0 || !a->attended) return cb::fail(E, "no step with its attention enqueued is open");
+  if (num_outputs < 0 || num_outputs > a->cfg.step.max_tokens)
+    return cb::fail(E, "num_outputs must be in [0, max_tokens]");
+  const int s = a->open;
+  if (hipEventRecord(a->compute_over[s], a->compute) != hipSuccess ||
+      hipStreamWaitEvent(a->down, a->compute_over[s], 0) != hipSuccess ||
+      (num_outputs > 0 && hipMemcpyAsync(a->cfg.out_ids_host[s], a->cfg.out_ids[s], sizeof(int32_t) * num_outputs,
+                                         hipMemcpyDeviceToHost, a->down) != hipSuccess) ||
+      hipEventRecord(a->down_over[s], a->down) != hipSuccess)
+    return cb::fail(CB_ERR_HIP, "output download failed");
+  a->open = -1;
+  ++a->steps;
+  return cb::ok();
+}
+
+extern "C" int cb_async_wait(cb_async_steps* a, int32_t slot) {
+  if (!a || slot < 0 || slot > 1) return cb::fail(E, "bad handle or slot");
+  if (hipEventSynchronize(a->down_over[slot]) != hipSuccess) return cb::fail(CB_ERR_HIP, "download wait failed");
   return cb::ok();
 }
