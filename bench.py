@@ -732,7 +732,7 @@ def bench_async(args):
                 t_start = time.perf_counter()
             # CPU preparation of step n: the manager appends each sequence's next token (known in
             # the synchronous loop, a placeholder in the async one) and builds the batch
-            m.append_batch(ids, ones, tokens if not async_mode else np.zeros(S, np.int32))
+            m.append_batch(ids, ones, tokens if not async_mode else None)
             cu, kv, tables, _, _ = m.build_batch(ids, ones, MB, out=bufs)
             m.take_copies()
             slot = a.slot()
@@ -754,6 +754,7 @@ def bench_async(args):
                 if pending is not None:                 # the previous step's tokens
                     a.wait(pending)
                     tokens = a.out_ids_host[pending][:S].numpy().copy()
+                    m.confirm_batch(ids, ones, tokens)  # the placeholders get their values
                 pending = slot
             else:
                 a.wait(slot)

@@ -33,8 +33,10 @@
  * Rules the manager enforces so that the data the copies and lookups read exists:
  *  - a copy-on-write whose source block is written by a batch built in the open step is refused
  *    (its KV would be written after the copy runs): close the step first;
- *  - a copy's source block stays out of the free pools until cb_bm_take_copies returns it, so no
- *    copy of one launch overwrites another copy's source; no copy's destination is a source;
+ *  - every block a transfer of the open step reads or writes (a copy's source or destination,
+ *    a swap gather's source, a swap scatter's destination) stays out of the free pools until the
+ *    step closes, even if its sequence is freed, so no two transfers of one launch touch one
+ *    block; no copy's destination is a source;
  *  - a sequence in a batch of the open step cannot be freed;
  *  - a fork needs a parent whose every token is computed or in a built batch;
  *  - swap (below): a sequence with blocks written in the open step cannot be swapped out; blocks
@@ -92,11 +94,30 @@ int cb_bm_append_tokens(cb_block_manager* m, int64_t seq_id, const int32_t* toke
 /* cb_bm_append_tokens for seq_ids[i] with counts[i] tokens taken in order from the packed host
  * array tokens (sum of counts entries), for i = 0, 1, ... until one fails: that failure's status is
  * returned, earlier appends stay done and *num_done receives how many succeeded (a decode step's
- * appends in one call; the scheduler preempts from the first refused sequence on). */
+ * appends in one call; the scheduler preempts from the first refused sequence on). tokens NULL:
+ * every appended token is a placeholder (cb_bm_append_placeholders). */
 int cb_bm_append_batch(cb_block_manager* m, const int64_t* seq_ids, const int32_t* counts,
                        const int32_t* tokens, int32_t num_seqs, int32_t* num_done);
 
-/* New sequence `child` sharing every block of `parent` (parallel sampling, beam search). */
+/*
+ * Placeholder tokens for async steps ("Continuous batching in transformers", Async batching: a
+ * step's inputs are built before the previous step's tokens exist). cb_bm_append_placeholders
+ * appends num_tokens tokens whose values are not known yet (as cb_bm_append_tokens otherwise:
+ * blocks, copy-on-write); cb_bm_confirm_tokens gives the values of the next num_tokens
+ * unconfirmed tokens, in order. A full block is keyed for prefix reuse only once all its tokens
+ * are confirmed (and its KV computed), so no request reuses KV computed from a token it does not
+ * have. Tokens appended with values after an unconfirmed one stay unconfirmed until confirmed.
+ */
+int cb_bm_append_placeholders(cb_block_manager* m, int64_t seq_id, int32_t num_tokens);
+int cb_bm_confirm_tokens(cb_block_manager* m, int64_t seq_id, const int32_t* tokens,
+                         int32_t num_tokens);
+/* cb_bm_confirm_tokens for seq_ids[i] with counts[i] values taken in order from tokens, until one
+ * fails (as cb_bm_append_batch). */
+int cb_bm_confirm_batch(cb_block_manager* m, const int64_t* seq_ids, const int32_t* counts,
+                        const int32_t* tokens, int32_t num_seqs, int32_t* num_done);
+
+/* New sequence `child` sharing every block of `parent` (parallel sampling, beam search); the
+ * parent's tokens must all be confirmed. */
 int cb_bm_fork(cb_block_manager* m, int64_t parent, int64_t child);
 
 /* Ends a sequence: drops its references; a block nobody references returns to a pool (cached if

@@ -28,11 +28,19 @@ Where the pages leave a choice open, the reading taken (the library follows the 
     step yields that token's output);
   * a block's key here is the exact token prefix it completes (the library hashes it and checks
     the hit), every block that completes a prefix is keyed, and a lookup takes the lowest id;
+  * every block a transfer of the open step reads or writes (a copy's source and destination, a
+    gather's source, a scatter's destination) stays out of the free pools until the step closes,
+    even if its sequence lets it go, so no two transfers of one launch touch one block;
   * swap: every block of the victim is copied (shared ones too) into pool slots taken lowest id
-    first; its blocks are released (held, like copy sources, until the step closes, since the
-    step's gather reads them); swap-in takes new blocks, releases the slots (held until the step
+    first; its blocks are released (held until the step closes, since the step's gather reads
+    them); swap-in takes new blocks, releases the slots (held until the step
     closes), keys the full computed blocks again and counts them as written in the open step; a
     swapped sequence cannot be appended to, forked or batched until it is swapped in;
+  * placeholder tokens (for async steps, "Continuous batching in transformers", Async batching:
+    a step's input is built before the previous step's token is known): a sequence may hold
+    placeholder tokens whose values are confirmed later, in order; a full block is keyed only
+    once all its tokens are confirmed (and its KV computed), and a fork needs a fully confirmed
+    parent;
   * the step protocol of the library header: KV is written by the GPU after the step closes,
     so keys become findable, copy sources leave the pools, and written blocks may be copied
     only after that; a copy whose source was written in the open step is refused; a sequence
@@ -153,10 +161,22 @@ class BlockManagerOracle:
         while len(table) < nblocks:
             table.append(self._take())
         self.seqs[sid] = dict(tokens=tokens, table=table, computed=len(hits) * bs,
-                              nkeys=len(hits), in_batch=False)
+                              nkeys=len(hits), in_batch=False, confirmed=n)
         return len(hits) * bs
 
-    def append_tokens(self, sid: int, tokens):
+    def _key_blocks(self, s):
+        """Keys the sequence's full blocks whose KV is computed and whose tokens are confirmed
+        (found by lookups once the step closes)."""
+        bs = self.bs
+        for j in range(s["nkeys"], min(s["computed"], s["confirmed"]) // bs):
+            b = s["table"][j]
+            if self.key[b] is None:
+                self.key[b] = tuple(s["tokens"][:(j + 1) * bs])
+                self.visible[b] = False
+                self.step_blocks.append(b)
+        s["nkeys"] = max(s["nkeys"], min(s["computed"], s["confirmed"]) // bs)
+
+    def append_tokens(self, sid: int, tokens, placeholders: bool = False):
         s = self._seq(sid)
         tokens = [int(t) for t in tokens]
         if not tokens:
@@ -172,12 +192,33 @@ class BlockManagerOracle:
         if cow:
             dst = self._take()
             self.pending[last] += 1
+            self.pending[dst] += 1      # a copy's destination is held until the step closes too
             self.ref[last] -= 1
             self.copies.append((last, dst))
             s["table"][-1] = dst
+        if placeholders:
+            tokens = [0] * len(tokens)
+        elif s["confirmed"] == len(s["tokens"]):
+            s["confirmed"] += len(tokens)
         s["tokens"].extend(tokens)
         while len(s["table"]) < nblocks:
             s["table"].append(self._take())
+
+    def append_placeholders(self, sid: int, n: int):
+        """n tokens whose values are not known yet (entered as 0)."""
+        self.append_tokens(sid, [0] * int(n), placeholders=True)
+
+    def confirm_tokens(self, sid: int, tokens):
+        """The values of the next len(tokens) unconfirmed tokens, in order."""
+        s = self._seq(sid, swapped_ok=True)
+        tokens = [int(t) for t in tokens]
+        c = s["confirmed"]
+        if c + len(tokens) > len(s["tokens"]):
+            raise BlockError(INVALID, "more values than unconfirmed tokens")
+        s["tokens"][c:c + len(tokens)] = tokens
+        s["confirmed"] = c + len(tokens)
+        if not s.get("swapped"):
+            self._key_blocks(s)
 
     def append_batch(self, seq_ids, counts, tokens):
         """append_tokens for each sequence in order until one is refused; returns how many were
@@ -196,10 +237,10 @@ class BlockManagerOracle:
         p = self._seq(parent)
         if child in self.seqs:
             raise BlockError(INVALID, "child id in use")
-        if p["computed"] != len(p["tokens"]):
-            raise BlockError(INVALID, "parent has tokens not yet computed")
+        if p["computed"] != len(p["tokens"]) or p["confirmed"] != len(p["tokens"]):
+            raise BlockError(INVALID, "parent has tokens not yet computed or confirmed")
         c = dict(tokens=list(p["tokens"]), table=list(p["table"]), computed=p["computed"],
-                 nkeys=p["nkeys"], in_batch=False)
+                 nkeys=p["nkeys"], in_batch=False, confirmed=p["confirmed"])
         for b in c["table"]:
             self._add_ref(b)
         self.seqs[child] = c
@@ -251,6 +292,9 @@ class BlockManagerOracle:
             raise BlockError(OUT_OF_BLOCKS, "pool exhausted")
         table = [self._take() for _ in s["slots"]]
         pairs = list(zip(s["slots"], table))
+        for b in table:                  # the scatter's destinations are held like the gathers'
+            self.pending[b] += 1
+            self.swap_src.append(b)
         for slot in s["slots"]:
             self.slot_state[slot] = 2
         for b in table:
@@ -258,11 +302,7 @@ class BlockManagerOracle:
             self.step_blocks.append(b)
         s["table"], s["slots"], s["swapped"] = table, [], False
         s["nkeys"] = 0
-        for j in range(s["computed"] // self.bs):   # key the computed full blocks again
-            b = table[j]
-            self.key[b] = tuple(s["tokens"][:(j + 1) * self.bs])
-            self.visible[b] = False
-        s["nkeys"] = s["computed"] // self.bs
+        self._key_blocks(s)              # the computed, confirmed full blocks are keyed again
         return pairs
 
     def swap_stats(self):
@@ -308,13 +348,7 @@ class BlockManagerOracle:
             kv_lens[i] = p0 + q
             tables[i, :len(s["table"])] = s["table"]
             s["computed"] = p0 + q
-            for j in range(s["nkeys"], s["computed"] // bs):   # key the newly completed blocks
-                b = s["table"][j]
-                if self.key[b] is None:
-                    self.key[b] = tuple(s["tokens"][:(j + 1) * bs])
-                    self.visible[b] = False
-                    self.step_blocks.append(b)
-            s["nkeys"] = max(s["nkeys"], s["computed"] // bs)
+            self._key_blocks(s)
             if not s["in_batch"]:
                 s["in_batch"] = True
                 self.step_seqs.append(sid)
@@ -325,7 +359,7 @@ class BlockManagerOracle:
         if capacity is not None and len(self.copies) > capacity:
             raise BlockError(INVALID, "capacity too small")
         out = list(self.copies)
-        for src in [s_ for s_, _ in out] + self.swap_src:
+        for src in [b for pair in out for b in pair] + self.swap_src:
             self.pending[src] -= 1
             if self.pending[src] == 0 and self.state[src] == HELD:
                 self._to_pool(src)
@@ -354,7 +388,7 @@ class BlockManagerOracle:
         return len(s["tokens"]), s["computed"], len(s["table"])
 
     # -- the GPU's part of a step, simulated -------------------------------------------------
-    def apply_step(self, copies, batch, swap_outs=(), swap_ins=()):
+    def apply_step(self, copies, batch, swap_outs=(), swap_ins=(), real=None):
         """Copies first (whole blocks), then the swap gathers (block -> pool slot) and scatters
         (pool slot -> block), then the batch's new KV at its slots: the KV of the token at
         position p of a sequence is the tuple of that sequence's tokens 0..p."""
@@ -368,22 +402,25 @@ class BlockManagerOracle:
         bs = self.bs
         for i, sid in enumerate(seq_ids):
             s = self.seqs[sid]
+            toks = real[sid] if real is not None else s["tokens"]   # the GPU sees real tokens
             q = int(cu[i + 1] - cu[i])
             p0 = s["computed"] - q
             for k in range(q):
                 p = p0 + k
                 sl = int(slots[cu[i] + k])
-                self.kv[sl // bs][sl % bs] = tuple(s["tokens"][:p + 1])
+                self.kv[sl // bs][sl % bs] = tuple(toks[:p + 1])
 
-    def check_views(self):
-        """Brute force: every computed position of every live sequence reads its own prefix."""
+    def check_views(self, real=None):
+        """Brute force: every computed position of every live sequence reads its own prefix
+        (real token values where the manager holds placeholders)."""
         bs = self.bs
         for sid, s in self.seqs.items():
             if s.get("swapped"):
                 continue
+            toks = real[sid] if real is not None else s["tokens"]
             for p in range(s["computed"]):
                 b = s["table"][p // bs]
-                if self.kv[b][p % bs] != tuple(s["tokens"][:p + 1]):
+                if self.kv[b][p % bs] != tuple(toks[:p + 1]):
                     return f"sequence {sid} position {p} reads the wrong KV (block {b})"
         return None
 

@@ -40,7 +40,8 @@ EXPORTED_SYMBOLS = (
     "cb_bm_free_sequence", "cb_bm_build_batch", "cb_bm_take_copies", "cb_bm_sequence_info",
     "cb_bm_block_table", "cb_bm_stats", "cb_bm_ref_counts", "cb_copy_blocks",
     "cb_bm_set_swap_slots", "cb_bm_swap_out", "cb_bm_swap_in", "cb_bm_swap_stats",
-    "cb_swap_out_blocks", "cb_swap_in_blocks",
+    "cb_swap_out_blocks", "cb_swap_in_blocks", "cb_bm_append_placeholders", "cb_bm_confirm_tokens",
+    "cb_bm_confirm_batch",
     # include/cbgraphs.h
     "cb_graphs_create", "cb_graphs_destroy", "cb_graphs_run", "cb_graphs_stats",
     # include/cbasync.h
@@ -98,6 +99,9 @@ _sig = {
     "cb_bm_ref_counts": (ctypes.c_int, [_p, _p, _i64]),
     "cb_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i64, _i64, _i32, _i64, _p]),
     "cb_bm_set_swap_slots": (ctypes.c_int, [_p, _i64]),
+    "cb_bm_append_placeholders": (ctypes.c_int, [_p, _i64, _i32]),
+    "cb_bm_confirm_tokens": (ctypes.c_int, [_p, _i64, _p, _i32]),
+    "cb_bm_confirm_batch": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p]),
     "cb_bm_swap_out": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p]),
     "cb_bm_swap_in": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p]),
     "cb_bm_swap_stats": (ctypes.c_int, [_p, _p, _p, _p]),
@@ -341,19 +345,34 @@ class BlockManager:
         _check(lib.cb_bm_append_tokens(self._h, int(seq_id), _ptr(t), t.size), "cb_bm_append_tokens")
 
     def append_batch(self, seq_ids, counts, tokens) -> int:
-        """Appends counts[i] tokens (packed in order in `tokens`) to seq_ids[i] until one is refused;
-        returns how many sequences were appended (all of them, or raises CBError with the count
-        in .num_done)."""
+        """Appends counts[i] tokens (packed in order in `tokens`; None: placeholders) to
+        seq_ids[i] until one is refused; returns how many sequences were appended (all of them,
+        or raises CBError with the count in .num_done)."""
+        return self._batch(lib.cb_bm_append_batch, "cb_bm_append_batch", seq_ids, counts, tokens)
+
+    def confirm_batch(self, seq_ids, counts, tokens) -> int:
+        """Confirms the next counts[i] tokens of seq_ids[i] (values packed in `tokens`)."""
+        return self._batch(lib.cb_bm_confirm_batch, "cb_bm_confirm_batch", seq_ids, counts, tokens)
+
+    def _batch(self, fn, name, seq_ids, counts, tokens):
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         c = np.ascontiguousarray(counts, dtype=np.int32)
-        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        t = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
         done = ctypes.c_int32()
-        st = lib.cb_bm_append_batch(self._h, _ptr(ids), _ptr(c), _ptr(t), ids.size, ctypes.byref(done))
+        st = fn(self._h, _ptr(ids), _ptr(c), None if t is None else _ptr(t), ids.size, ctypes.byref(done))
         if st != 0:
-            e = CBError(st, "cb_bm_append_batch", cb_last_error())
+            e = CBError(st, name, cb_last_error())
             e.num_done = done.value
             raise e
         return done.value
+
+    def append_placeholders(self, seq_id: int, num_tokens: int):
+        _check(lib.cb_bm_append_placeholders(self._h, int(seq_id), int(num_tokens)),
+               "cb_bm_append_placeholders")
+
+    def confirm_tokens(self, seq_id: int, tokens):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(lib.cb_bm_confirm_tokens(self._h, int(seq_id), _ptr(t), t.size), "cb_bm_confirm_tokens")
 
     def fork(self, parent: int, child: int):
         _check(lib.cb_bm_fork(self._h, int(parent), int(child)), "cb_bm_fork")

@@ -16,6 +16,9 @@
 //   - a full block is keyed once its KV is computed (blocks holding the same prefix are all
 //     keyed; a lookup takes the lowest id) and is found by lookups only after the step that
 //     computes it has closed;
+//   - every block a transfer of the open step reads or writes (a copy's source and destination,
+//     a gather's source, a scatter's destination) stays out of the free pools until the step
+//     closes, even if its sequence lets it go, so no two transfers of one launch touch one block;
 //   - swap tier ("Continuous batching architecture", Offloading): a swap-out copies every block
 //     of the sequence to host pool slots (lowest free id first) and releases the blocks, held
 //     until the step closes because the step's gather reads them; a swap-in takes new blocks,
@@ -24,6 +27,7 @@
 // A full block's key is a chained 64-bit FNV-1a hash of its parent's key and its own tokens; a
 // hit is verified against the block's tokens and its parent's key.
 
+#include <algorithm>
 #include <cstring>
 #include <list>
 #include <new>
@@ -42,6 +46,7 @@ struct cb_block_manager {
     int64_t computed = 0;        // leading positions whose KV is computed or in a built batch
     bool in_batch = false;       // part of a batch built since the step last closed
     uint64_t stamp = 0;          // the last cb_bm_build_batch call that named this sequence
+    int64_t confirmed = 0;       // leading tokens whose values are known (not placeholders)
     bool swapped = false;        // its blocks live in host pool slots
     std::vector<int32_t> slots;  // those slots, in table order
   };
@@ -69,7 +74,7 @@ struct cb_block_manager {
   std::vector<uint8_t> slot_state;          // 0 free, 1 used, 2 held until the step closes
   std::set<int32_t> free_slots;
   std::vector<int32_t> held_slots;          // released in the open step
-  std::vector<int32_t> swap_src;            // blocks the open step's gathers read
+  std::vector<int32_t> swap_src;            // blocks the open step's gathers and scatters use
   int64_t swapped_seqs = 0;
 };
 
@@ -172,12 +177,12 @@ Mgr::Seq* find_seq(Mgr* m, int64_t id) {
   return it == m->seqs.end() ? nullptr : &it->second;
 }
 
-// Extends the keys of the sequence's full blocks up to `computed` and keys each such block
-// (visible to lookups once the step closes). Blocks holding the same prefix are all keyed, so
-// evicting one leaves the others findable.
+// Extends the keys of the sequence's full blocks whose KV is computed and whose tokens are all
+// confirmed, and keys each such block (visible to lookups once the step closes). Blocks holding
+// the same prefix are all keyed, so evicting one leaves the others findable.
 void key_computed_blocks(Mgr* m, Mgr::Seq& s) {
   const int32_t bs = m->bs;
-  const int64_t full = s.computed / bs;
+  const int64_t full = std::min(s.computed, s.confirmed) / bs;
   for (int64_t j = (int64_t)s.keys.size(); j < full; ++j) {
     const uint64_t parent = j ? s.keys[j - 1] : 0;
     const int32_t* tok = s.tokens.data() + j * bs;
@@ -263,16 +268,18 @@ extern "C" int cb_bm_add_sequence(cb_block_manager* m, int64_t seq_id, const int
   while ((int64_t)s.table.size() < nblocks) s.table.push_back(take_block(m));
   s.keys = std::move(keys);
   s.computed = (int64_t)hit.size() * bs;
+  s.confirmed = num_tokens;
   m->seqs.emplace(seq_id, std::move(s));
   if (num_cached) *num_cached = (int32_t)(hit.size() * bs);
   return cb::ok();
 }
 
-extern "C" int cb_bm_append_tokens(cb_block_manager* m, int64_t seq_id, const int32_t* tokens,
-                                   int32_t num_tokens) {
-  if (!m) return cb::fail(E, "manager is NULL");
+namespace {
+
+// Appends num_tokens tokens (values from `tokens`, or placeholders 0 whose values come later).
+int append_impl(Mgr* m, int64_t seq_id, const int32_t* tokens, int32_t num_tokens, bool placeholders) {
   if (num_tokens < 0) return cb::fail(E, "num_tokens must be >= 0");
-  if (num_tokens > 0 && !tokens) return cb::fail(E, "tokens is NULL");
+  if (num_tokens > 0 && !tokens && !placeholders) return cb::fail(E, "tokens is NULL");
   Mgr::Seq* s = find_seq(m, seq_id);
   if (!s) return cb::fail(E, "unknown sequence id");
   if (s->swapped) return cb::fail(E, "sequence is swapped out");
@@ -291,13 +298,46 @@ extern "C" int cb_bm_append_tokens(cb_block_manager* m, int64_t seq_id, const in
     const int32_t src = s->table.back();
     const int32_t dst = take_block(m);
     ++m->pending[src];
+    ++m->pending[dst];  // the destination too is held until the step closes
     --m->ref[src];  // others still hold it: it stays in use
     m->copy_src.push_back(src);
     m->copy_dst.push_back(dst);
     s->table.back() = dst;
   }
-  s->tokens.insert(s->tokens.end(), tokens, tokens + num_tokens);
+  if (placeholders) {
+    s->tokens.insert(s->tokens.end(), num_tokens, 0);
+  } else {
+    if (s->confirmed == len) s->confirmed += num_tokens;
+    s->tokens.insert(s->tokens.end(), tokens, tokens + num_tokens);
+  }
   while ((int64_t)s->table.size() < nblocks) s->table.push_back(take_block(m));
+  return cb::ok();
+}
+
+}  // namespace
+
+extern "C" int cb_bm_append_tokens(cb_block_manager* m, int64_t seq_id, const int32_t* tokens,
+                                   int32_t num_tokens) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  return append_impl(m, seq_id, tokens, num_tokens, false);
+}
+
+extern "C" int cb_bm_append_placeholders(cb_block_manager* m, int64_t seq_id, int32_t num_tokens) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  return append_impl(m, seq_id, nullptr, num_tokens, true);
+}
+
+extern "C" int cb_bm_confirm_tokens(cb_block_manager* m, int64_t seq_id, const int32_t* tokens,
+                                    int32_t num_tokens) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens)) return cb::fail(E, "bad tokens");
+  Mgr::Seq* s = find_seq(m, seq_id);
+  if (!s) return cb::fail(E, "unknown sequence id");
+  if (s->confirmed + num_tokens > (int64_t)s->tokens.size())
+    return cb::fail(E, "more values than unconfirmed tokens");
+  std::copy(tokens, tokens + num_tokens, s->tokens.begin() + s->confirmed);
+  s->confirmed += num_tokens;
+  if (!s->swapped) key_computed_blocks(m, *s);
   return cb::ok();
 }
 
@@ -311,7 +351,26 @@ extern "C" int cb_bm_append_batch(cb_block_manager* m, const int64_t* seq_ids,
   if (num_seqs > 0 && (!seq_ids || !counts)) return cb::fail(E, "NULL array");
   int64_t off = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
-    const int st = cb_bm_append_tokens(m, seq_ids[i], tokens ? tokens + off : nullptr, counts[i]);
+    // tokens NULL: every appended token is a placeholder
+    const int st = append_impl(m, seq_ids[i], tokens ? tokens + off : nullptr, counts[i], !tokens);
+    if (st != CB_OK) return st;
+    off += counts[i];
+    *num_done = i + 1;
+  }
+  return cb::ok();
+}
+
+extern "C" int cb_bm_confirm_batch(cb_block_manager* m, const int64_t* seq_ids,
+                                   const int32_t* counts, const int32_t* tokens, int32_t num_seqs,
+                                   int32_t* num_done) {
+  if (!m) return cb::fail(E, "manager is NULL");
+  if (!num_done) return cb::fail(E, "num_done is NULL");
+  *num_done = 0;
+  if (num_seqs < 0) return cb::fail(E, "num_seqs must be >= 0");
+  if (num_seqs > 0 && (!seq_ids || !counts || !tokens)) return cb::fail(E, "NULL array");
+  int64_t off = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int st = cb_bm_confirm_tokens(m, seq_ids[i], tokens + off, counts[i]);
     if (st != CB_OK) return st;
     off += counts[i];
     *num_done = i + 1;
@@ -325,8 +384,8 @@ extern "C" int cb_bm_fork(cb_block_manager* m, int64_t parent, int64_t child) {
   if (!p) return cb::fail(E, "unknown parent sequence id");
   if (p->swapped) return cb::fail(E, "parent sequence is swapped out");
   if (m->seqs.count(child)) return cb::fail(E, "child sequence id already in use");
-  if (p->computed != (int64_t)p->tokens.size())
-    return cb::fail(E, "fork needs a parent whose every token is computed or in a built batch");
+  if (p->computed != (int64_t)p->tokens.size() || p->confirmed != (int64_t)p->tokens.size())
+    return cb::fail(E, "fork needs a parent whose every token is confirmed and computed or in a built batch");
   Mgr::Seq c = *p;
   c.in_batch = false;
   for (int32_t b : c.table) add_ref(m, b);
@@ -415,6 +474,8 @@ extern "C" int cb_bm_swap_in(cb_block_manager* m, int64_t seq_id, int32_t* slots
     s->table[j] = b;
     slots[j] = s->slots[j];
     blocks[j] = b;
+    ++m->pending[b];  // the scatter's destination is held until the step closes
+    m->swap_src.push_back(b);
     m->slot_state[s->slots[j]] = 2;
     m->held_slots.push_back(s->slots[j]);
     if (!m->dirty[b]) {
@@ -515,8 +576,8 @@ extern "C" int cb_bm_take_copies(cb_block_manager* m, int32_t* src, int32_t* dst
     src[i] = m->copy_src[i];
     dst[i] = m->copy_dst[i];
   }
-  for (int64_t i = 0; i < n + (int64_t)m->swap_src.size(); ++i) {
-    const int32_t b = i < n ? m->copy_src[i] : m->swap_src[i - n];
+  for (int64_t i = 0; i < 2 * n + (int64_t)m->swap_src.size(); ++i) {
+    const int32_t b = i < n ? m->copy_src[i] : i < 2 * n ? m->copy_dst[i - n] : m->swap_src[i - 2 * n];
     if (--m->pending[b] == 0 && m->state[b] == kHeld) {
       --m->held;
       to_pool(m, b);

@@ -20,6 +20,8 @@ class Sim:
         self.m = ob.BlockManagerOracle(num_blocks, block_size)
         self.bs = block_size
         self.closed = {}   # sequence -> positions computed in closed steps
+        self.conf_closed = {}   # sequence -> positions confirmed when the last step closed
+        self.real = {}     # sequence -> its real tokens (placeholders included, by value)
         self.outs, self.ins = [], []   # the open step's swap gathers and scatters
 
     def add(self, sid, tokens):
@@ -27,11 +29,40 @@ class Sim:
         got = self.m.add_sequence(sid, tokens)
         assert got == expect, f"prefix hit {got} != brute force {expect}"
         self.closed[sid] = got
+        self.conf_closed[sid] = len(tokens)
+        self.real[sid] = [int(t) for t in tokens]
         return got
+
+    def append(self, sid, tokens):
+        self.m.append_tokens(sid, tokens)
+        self.real[sid] += [int(t) for t in tokens]
+
+    def append_batch(self, ids, counts, tokens):
+        off = 0
+        done = 0
+        try:
+            for sid, n in zip(ids, counts):
+                self.m.append_tokens(sid, list(tokens[off:off + n]))
+                self.real[sid] += [int(t) for t in tokens[off:off + n]]
+                off += n
+                done += 1
+        except self.ob.BlockError as e:
+            e.num_done = done
+            raise
+        return len(ids)
+
+    def append_placeholders(self, sid, values):
+        self.m.append_placeholders(sid, len(values))
+        self.real[sid] += [int(t) for t in values]
+
+    def confirm(self, sid, values):
+        self.m.confirm_tokens(sid, values)
 
     def fork(self, parent, child):
         self.m.fork(parent, child)
         self.closed[child] = self.closed[parent]
+        self.conf_closed[child] = self.conf_closed[parent]
+        self.real[child] = list(self.real[parent])
 
     def free(self, sid):
         self.m.free_sequence(sid)
@@ -62,15 +93,16 @@ class Sim:
         assert len(set(scattered)) == len(scattered), "two scatters write one block"
         assert not set(scattered) & (set(gathered) | set(dsts) | set(srcs)), \
             "a scatter writes a block another transfer of the step uses"
-        self.m.apply_step(copies, (list(ids), cu, slots), self.outs, self.ins)
+        self.m.apply_step(copies, (list(ids), cu, slots), self.outs, self.ins, real=self.real)
         self.outs, self.ins = [], []
         for sid in self.m.seqs:
             self.closed[sid] = self.m.seqs[sid]["computed"]
+            self.conf_closed[sid] = self.m.seqs[sid]["confirmed"]
         self.check()
         return cu, kv, bt, slots, toks, copies
 
     def check(self):
-        err = self.m.check_views() or self.m.check_counts()
+        err = self.m.check_views(real=self.real) or self.m.check_counts()
         assert err is None, err
 
     def expected_hit(self, tokens):
@@ -87,7 +119,8 @@ class Sim:
             cands = set(m.cached) | {b for b in range(m.nb)
                                      if m.state[b] == self.ob.HELD and m.key[b] is not None}
             for sid, s in m.seqs.items():
-                if len(s["table"]) > j and self.closed.get(sid, 0) >= (j + 1) * bs:
+                if len(s["table"]) > j and min(self.closed.get(sid, 0),
+                                               self.conf_closed.get(sid, 0)) >= (j + 1) * bs:
                     cands.add(s["table"][j])
             if not any(m.kv[b] == want for b in cands):
                 break
@@ -112,7 +145,7 @@ def pin_fork_cow_example(ob, rows):
     for c in kids:
         sim.fork(0, c)
     for c in kids:
-        m.append_tokens(c, [200 + c])
+        sim.append(c, [200 + c])
     t0 = m.block_table(0)
     tabs = [m.block_table(c) for c in kids]
     assert all(t[0] == t0[0] for t in tabs), "the first block must stay shared"
@@ -300,12 +333,21 @@ def pin_protocol_rules(ob):
     sim.step([0, 1], [6, 6])
     sim.fork(0, 2)
     sim.fork(1, 3)
-    m.append_tokens(2, [7])            # copy of sequence 0's last block
+    sim.append(2, [7])                 # copy of sequence 0's last block
     sim.free(0)                        # its only other holder leaves
     assert m.stats()[2] == 1
-    m.append_tokens(3, [8])            # this copy's destination must be a different block
+    sim.append(3, [8])                 # this copy's destination must be a different block
     sim.step([2, 3], [1, 1])
     assert m.stats()[2] == 0
+
+    # a copy's destination whose sequence is freed in the same step is held as well, so it
+    # cannot become the destination of a second copy of that step
+    sim.fork(2, 4)
+    sim.fork(2, 5)
+    sim.append(4, [1])                 # copy into a new block D
+    sim.free(4)                        # D's only holder leaves before the copy has run
+    sim.append(5, [2])                 # its copy must not write D too
+    sim.step([5], [1])
 
 
 def pin_swap(ob):
@@ -353,13 +395,48 @@ def pin_swap(ob):
     assert not {sl for _, sl in outs_e} & {sl for sl, _ in ins}
     assert refused(m.swap_out, 0, status=ob.INVALID)      # its blocks are written this step
     sim.step([], [])
-    m.append_tokens(0, [8])
+    sim.append(0, [8])
     sim.step([0], [1])
     assert m.swap_stats() == (2, 4, 0)                    # B and E hold 2 slots each
+    # a swapped-in sequence freed in the same step: its new blocks stay held, so another swap-in
+    # of that step scatters elsewhere
+    sim.swap_in(1)                     # B comes back ...
+    sim.free(1)                        # ... and leaves again before the scatter has run
+    sim.swap_in(5)                     # E's scatter must not target B's blocks
+    sim.step([], [])
     # soft reset of C (freed, re-added with its tokens): its cached full blocks are reused
     sim.free(2)
     assert sim.add(4, C) == 8
     sim.step([4], [1])
+
+
+def pin_placeholders(ob):
+    """Async steps append a token before its value is known: the block it completes is keyed only
+    once the value is confirmed, so no request reuses KV computed from a token it does not have."""
+    bs = 4
+    sim = Sim(ob, 16, bs)
+    m = sim.m
+
+    def refused(fn, *a):
+        try:
+            fn(*a)
+        except ob.BlockError as e:
+            return e.status == ob.INVALID
+        return False
+
+    sim.add(0, [1, 2, 3])
+    sim.step([0], [3])
+    sim.append_placeholders(0, [4])          # the GPU will see token 4; the manager holds 0
+    sim.step([0], [1])                       # block 0 is full and computed, but unconfirmed
+    assert refused(m.fork, 0, 9)             # a fork needs confirmed tokens
+    assert sim.add(1, [1, 2, 3, 0, 9]) == 0  # the placeholder value must not match
+    sim.step([1], [5])
+    assert refused(m.confirm_tokens, 0, [4, 5])
+    sim.confirm(0, [4])                      # now block 0 is keyed as (1, 2, 3, 4)
+    sim.step([], [])
+    assert sim.add(2, [1, 2, 3, 4, 5]) == 4
+    sim.step([2], [1])
+    sim.fork(0, 3)
 
 
 def random_ops(rng, n_ops, vocab=3, bs=4, shared=(), max_prompt=14):
@@ -372,8 +449,12 @@ def random_ops(rng, n_ops, vocab=3, bs=4, shared=(), max_prompt=14):
             base = list(shared[rng.integers(len(shared))]) if shared and rng.random() < 0.7 else []
             extra = rng.integers(1, max_prompt)
             ops.append(("add", base + [int(x) for x in rng.integers(0, vocab, extra)]))
-        elif r < 0.4:
+        elif r < 0.35:
             ops.append(("append", [int(x) for x in rng.integers(0, vocab, rng.integers(1, 4))]))
+        elif r < 0.38:
+            ops.append(("placeholders", [int(x) for x in rng.integers(0, vocab, rng.integers(1, 3))]))
+        elif r < 0.4:
+            ops.append(("confirm", None))
         elif r < 0.45:
             ops.append(("append_batch", int(rng.integers(1, 1 << 30))))
         elif r < 0.5:
@@ -395,6 +476,7 @@ def drive(sim_like, ops, rng_seed):
     rng = np.random.default_rng(rng_seed)
     live, next_id, log = [], 0, []
     swapped = set()
+    unconfirmed = {}   # sequence -> real values of its placeholders not yet confirmed
     for kind, arg in ops:
         try:
             if kind == "add":
@@ -404,6 +486,14 @@ def drive(sim_like, ops, rng_seed):
             elif kind == "append" and live:
                 sid = live[rng.integers(len(live))]
                 out = sim_like.append(sid, arg)
+            elif kind == "placeholders" and live:
+                sid = live[rng.integers(len(live))]
+                out = sim_like.append_placeholders(sid, arg)
+                unconfirmed.setdefault(sid, []).extend(arg)
+            elif kind == "confirm" and unconfirmed:
+                sid = sorted(unconfirmed)[rng.integers(len(unconfirmed))]
+                vals = unconfirmed.pop(sid)
+                out = sim_like.confirm(sid, vals)
             elif kind == "append_batch" and live:
                 r2 = np.random.default_rng(arg)
                 ids = [s for s in live if r2.random() < 0.5]
@@ -425,6 +515,7 @@ def drive(sim_like, ops, rng_seed):
                 out = sim_like.free(sid)
                 live.remove(sid)
                 swapped.discard(sid)
+                unconfirmed.pop(sid, None)
             elif kind == "step":
                 pend = sim_like.pending([s for s in live if s not in swapped])
                 r2 = np.random.default_rng(arg)
@@ -455,10 +546,16 @@ class OracleDriver:
         return self.sim.add(sid, toks)
 
     def append(self, sid, toks):
-        return self.sim.m.append_tokens(sid, toks)
+        return self.sim.append(sid, toks)
 
     def append_batch(self, ids, counts, toks):
-        return self.sim.m.append_batch(ids, counts, toks)
+        return self.sim.append_batch(ids, counts, toks)
+
+    def append_placeholders(self, sid, vals):
+        return self.sim.append_placeholders(sid, vals)
+
+    def confirm(self, sid, vals):
+        return self.sim.confirm(sid, vals)
 
     def swap_out(self, sid):
         return [tuple(p) for p in self.sim.swap_out(sid)]

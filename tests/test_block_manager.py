@@ -28,6 +28,12 @@ class LibDriver:
     def append_batch(self, ids, counts, toks):
         return self.m.append_batch(ids, counts, toks)
 
+    def append_placeholders(self, sid, vals):
+        return self.m.append_placeholders(sid, len(vals))
+
+    def confirm(self, sid, vals):
+        return self.m.confirm_tokens(sid, vals)
+
     def swap_out(self, sid):
         a, b = self.m.swap_out(sid)
         return list(zip(a.tolist(), b.tolist()))
@@ -228,3 +234,25 @@ def test_append_batch_stops_at_first_refusal():
         m.append_batch([0, 1, 0], [1, 1, 4], list(range(6)))
     assert e.value.status == cb.CB_ERR_OUT_OF_BLOCKS and e.value.num_done == 2
     assert m.sequence_info(0)[0] == 5 and m.sequence_info(1)[0] == 5
+
+
+def test_batched_placeholders_and_confirmation_match_single_calls():
+    a, b = cb.BlockManager(64, 4), cb.BlockManager(64, 4)
+    for m in (a, b):
+        for s_ in range(3):
+            m.add_sequence(s_, [5 + s_] * 6)
+        m.build_batch([0, 1, 2], [6, 6, 6], 8)
+        m.take_copies()
+    a.append_batch([0, 1, 2], [1, 2, 1], None)
+    for s_, n in ((0, 1), (1, 2), (2, 1)):
+        b.append_placeholders(s_, n)
+    a.confirm_batch([0, 1, 2], [1, 2, 1], [7, 8, 9, 10])
+    b.confirm_tokens(0, [7])
+    b.confirm_tokens(1, [8, 9])
+    b.confirm_tokens(2, [10])
+    for s_ in range(3):
+        assert a.sequence_info(s_) == b.sequence_info(s_)
+        assert a.block_table(s_).tolist() == b.block_table(s_).tolist()
+    with pytest.raises(cb.CBError) as e:
+        a.confirm_batch([0, 1], [0, 1], [3])   # sequence 1 has no unconfirmed token left
+    assert e.value.num_done == 1

@@ -2,7 +2,7 @@
 brute force over random operation streams (CPU only)."""
 import oracle.blocks as ob
 from pins_blocks import (pin_block_table_example, pin_eviction_order, pin_fork_cow_example,
-                         pin_last_token_block_not_reused, pin_prefix_worked_example, pin_protocol_rules, pin_swap,
+                         pin_last_token_block_not_reused, pin_prefix_worked_example, pin_placeholders, pin_protocol_rules, pin_swap,
                          pin_random_bruteforce)
 
 
@@ -36,3 +36,7 @@ def test_protocol_rules():
 
 def test_swap():
     pin_swap(ob)
+
+
+def test_placeholders():
+    pin_placeholders(ob)

@@ -8,7 +8,7 @@ import pytest
 from conftest import ROOT, read_golden
 from pins_blocks import (pin_block_table_example, pin_eviction_order, pin_fork_cow_example,
                          pin_last_token_block_not_reused, pin_prefix_worked_example,
-                         pin_protocol_rules, pin_random_bruteforce, pin_swap)
+                         pin_placeholders, pin_protocol_rules, pin_random_bruteforce, pin_swap)
 
 SRC = open(os.path.join(ROOT, "oracle", "blocks.py")).read()
 
@@ -31,8 +31,8 @@ MUTANTS = {
     "no-hold": [("        if self.pending[b] > 0:\n            self.state[b] = HELD\n        elif",
                  "        if", 1)],
     # blocks computed in the open step are found at once
-    "visible-at-once": [("                    self.visible[b] = False\n",
-                         "                    self.visible[b] = True\n", 1)],
+    "visible-at-once": [("                self.visible[b] = False\n                self.step_blocks.append(b)",
+                         "                self.visible[b] = True\n                self.step_blocks.append(b)", 1)],
     # a copy of a block written in the open step is allowed
     "cow-of-dirty": [("if cow and self.dirty[last]:", "if False:", 1)],
     # a block keyed by its own tokens only, not by the whole prefix
@@ -45,7 +45,14 @@ MUTANTS = {
     # fork does not take references
     "fork-no-ref": [('        for b in c["table"]:\n            self._add_ref(b)\n', "", 1)],
     # a swapped-out block goes back to the pool before the step's gather has read it
-    "swap-no-hold": [("            self.pending[b] += 1\n            self.swap_src.append(b)\n", "", 1)],
+    "swap-no-hold": [("            self.slot_state[slot] = 1\n            self.pending[b] += 1\n            self.swap_src.append(b)\n",
+                      "            self.slot_state[slot] = 1\n", 1)],
+    # a swap-in's destination blocks are not held until the step closes
+    "scatter-no-hold": [("        for b in table:                  # the scatter's destinations are held like the gathers'\n            self.pending[b] += 1\n            self.swap_src.append(b)\n", "", 1)],
+    # a copy's destination is not held until the step closes
+    "copy-dst-no-hold": [("            self.pending[dst] += 1      # a copy's destination is held until the step closes too\n", "", 1),
+                         ("for src in [b for pair in out for b in pair] + self.swap_src:",
+                          "for src in [s_ for s_, _ in out] + self.swap_src:", 1)],
     # swapped-in blocks are not counted as written in the open step
     "swap-in-not-dirty": [("        for b in table:\n            self.dirty[b] = True\n", "        for b in table:\n", 1)],
     # slots released by a swap-in are free at once
@@ -53,6 +60,12 @@ MUTANTS = {
                                 "            self.slot_state[slot] = 0\n        for b in table:", 1)],
     # a sequence with blocks written in the open step may be swapped out
     "swap-out-dirty": [('if s["in_batch"] or any(self.dirty[b] for b in s["table"]):', 'if s["in_batch"]:', 1)],
+    # blocks are keyed whatever their tokens' confirmation
+    "key-unconfirmed": [('min(s["computed"], s["confirmed"]) // bs', 's["computed"] // bs', 2)],
+    # placeholders count as confirmed
+    "placeholders-confirmed": [('elif s["confirmed"] == len(s["tokens"]):', 'if s["confirmed"] == len(s["tokens"]):', 1)],
+    # a fork of a parent with unconfirmed tokens
+    "fork-unconfirmed": [(' or p["confirmed"] != len(p["tokens"]):', ':', 1)],
     # a swap-in reuses the sequence's old block ids instead of taking blocks
     "swap-in-nothing-taken": [("table = [self._take() for _ in s[\"slots\"]]", "table = list(s[\"slots\"])", 1)],
 }
@@ -77,6 +90,7 @@ def caught(mod):
         lambda: pin_eviction_order(mod),
         lambda: pin_protocol_rules(mod),
         lambda: pin_swap(mod),
+        lambda: pin_placeholders(mod),
         lambda: pin_random_bruteforce(mod, seeds=range(6), n_ops=120),
     ]
     for pin in pins:
