@@ -1,8 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of one forward-pass step of the hot path on one MI355X.
 
-A step = cb_slot_mapping + cb_cache_write + cb_paged_attention (planning prepass, decode/split-KV
-and prefill kernels, log-sum-exp merge) over one synthetic packed batch, inputs resident in HBM.
+A step = slot mapping + cache write + paged attention over one synthetic packed batch, inputs
+resident in HBM, as one call of cb_paged_attention_write (the cache write, with its slots computed
+in place, runs beside the planning workgroup; then the decode/split-KV and prefill kernels and the
+log-sum-exp merge); --separate times the same step as the three entry points cb_slot_mapping,
+cb_cache_write, cb_paged_attention.
 Default workload: the Llama-3-8B-shaped decode batch (32 q-heads, 8 KV heads, head_dim 128,
 block 16, 256 sequences with KV length uniform in [128, 4096], physical blocks shuffled); the
 mixed continuous batch of the same model shape (64 decode tokens + 1984 prefill-chunk tokens) is
@@ -209,13 +212,18 @@ def measure(args, config, steps, warmup):
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        cb.cb_slot_mapping(cu, kvl, bt, slots, b.block_size, stream=stream)
-        cb.cb_cache_write(k, v, slots, kc, vc, stream=stream)
+        if args.separate:  # the three entry points one after the other
+            cb.cb_slot_mapping(cu, kvl, bt, slots, b.block_size, stream=stream)
+            cb.cb_cache_write(k, v, slots, kc, vc, stream=stream)
         if ev is not None:
             ev[0].record(stream)
             cb.cb_time_next_kernel(kernel, ev[2], ev[3], stream=stream)
-        cb.cb_paged_attention(q, cu, kvl, bt, kc, vc, out, b.scale, b.max_q_len, b.max_kv_len, ws,
-                              kv_split_tokens=args.split, stream=stream)
+        if args.separate:
+            cb.cb_paged_attention(q, cu, kvl, bt, kc, vc, out, b.scale, b.max_q_len, b.max_kv_len,
+                                  ws, kv_split_tokens=args.split, stream=stream)
+        else:  # one call: the cache write runs beside the planning workgroup
+            cb.cb_paged_attention_write(q, k, v, cu, kvl, bt, kc, vc, out, b.scale, b.max_q_len,
+                                        b.max_kv_len, ws, kv_split_tokens=args.split, stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -795,6 +803,9 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="KV partition tokens (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-batch measurement")
+    ap.add_argument("--separate", action="store_true",
+                    help="time the step as cb_slot_mapping + cb_cache_write + cb_paged_attention "
+                         "(default: cb_paged_attention_write, the same work in one call)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR")
     ap.add_argument("--blocks", action="store_true", help="block copy and host manager measurement")
@@ -857,7 +868,8 @@ def main():
             "num_seqs": b.num_seqs, "num_tokens": b.num_tokens, "q_heads": b.num_q_heads,
             "kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
             "kv_tokens": int(b.kv_lens.sum()), "kv_split_tokens": int(r["split"]), "seed": b.seed,
-            "step": "slot_mapping + cache_write + paged_attention",
+            "step": ("slot_mapping + cache_write + paged_attention" if args.separate else
+                     "paged_attention_write (slot mapping + cache write + paged attention)"),
         },
         "hbm_frac": round(w["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w["T"] / step_s, 1),

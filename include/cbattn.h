@@ -149,6 +149,26 @@ int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlens_q, const 
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * cb_paged_attention_write — cb_slot_mapping + cb_cache_write + cb_paged_attention in one call:
+ * the step's new K/V rows k_new, v_new [T, Hkv, D] (bf16, 16-byte aligned) are written at the
+ * slots the slot mapping would give ("3.3 Batching & Memory Management", PagedAttention: block
+ * tables), then attention runs as in cb_paged_attention. The write's slots are computed in place
+ * (no slot array), and it runs in the first launch beside the planning workgroup, which reads
+ * no cache, instead of in two launches before it. Results are those of the three calls, bit for
+ * bit; rows whose position or slot the slot mapping would mark -1 (and slots past the pool) are
+ * not written. Arguments, preconditions and errors as cb_paged_attention's, plus
+ * num_blocks * block_size < 2^31.
+ */
+int cb_paged_attention_write(const void* q_packed, const void* k_new, const void* v_new,
+                             const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                             const int32_t* block_tables, void* k_cache, void* v_cache, void* out,
+                             float scale, int32_t num_seqs, int32_t num_tokens,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * cb_split_kv_reduce — merge per-partition attention results (log-sum-exp merge).
  * For each token t with n = num_splits[t] >= 1 and each head h:
  *     M = max_k lse[t][h][k];  w_k = exp(lse[t][h][k] - M)

@@ -1,6 +1,7 @@
 /*
- * cbgraphs — one step of the hot path (cb_slot_mapping, cb_cache_write, cb_paged_attention)
- * recorded as a HIP graph per padded batch shape and replayed.
+ * cbgraphs — one step of the hot path (slot mapping, cache write, paged attention: one
+ * cb_paged_attention_write) recorded as a HIP graph per padded batch shape and replayed, or
+ * launched directly.
  *
  * Source: "Continuous batching architecture", section "CUDA graphs": a step's GPU work is
  * recorded once and replayed for batches of the same shape, which removes the CPU cost of

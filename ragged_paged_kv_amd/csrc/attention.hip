@@ -260,17 +260,17 @@ __device__ inline int seq_items(const int32_t* __restrict__ cu, const int32_t* _
   return 1;
 }
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu,
-                                                    const int32_t* __restrict__ kv_lens,
-                                                    int32_t num_seqs, int32_t G, int32_t P,
-                                                    int32_t qmaxd, int32_t max_splits,
-                                                    int32_t bq, int32_t bs, int32_t max_blocks,
-                                                    int32_t max_kv, DecWork* __restrict__ dec,
-                                                    int64_t dec_cap, Work* __restrict__ pre,
-                                                    int64_t pre_cap, int32_t* __restrict__ counts,
-                                                    int32_t Hkv, int32_t cus, int32_t maxs,
-                                                    int32_t num_tokens, int32_t kv_token_bytes,
-                                                    int32_t* __restrict__ nsplit_tok) {
+__device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
+                                          const int32_t* __restrict__ kv_lens,
+                                          int32_t num_seqs, int32_t G, int32_t P,
+                                          int32_t qmaxd, int32_t max_splits,
+                                          int32_t bq, int32_t bs, int32_t max_blocks,
+                                          int32_t max_kv, DecWork* __restrict__ dec,
+                                          int64_t dec_cap, Work* __restrict__ pre,
+                                          int64_t pre_cap, int32_t* __restrict__ counts,
+                                          int32_t Hkv, int32_t cus, int32_t maxs,
+                                          int32_t num_tokens, int32_t kv_token_bytes,
+                                          int32_t* __restrict__ nsplit_tok) {
   __shared__ int32_t sd[1024];
   __shared__ int32_t sp[1024];
   __shared__ int32_t base[2];
@@ -408,6 +408,84 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       if (pos < dec_cap) dec[pos] = DecWork{s, nfull, cu[s], cu[s + 1] - cu[s], kv_lens[s], 0, 0, 0};
     }
   }
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu,
+                                                    const int32_t* __restrict__ kv_lens,
+                                                    int32_t num_seqs, int32_t G, int32_t P,
+                                                    int32_t qmaxd, int32_t max_splits,
+                                                    int32_t bq, int32_t bs, int32_t max_blocks,
+                                                    int32_t max_kv, DecWork* __restrict__ dec,
+                                                    int64_t dec_cap, Work* __restrict__ pre,
+                                                    int64_t pre_cap, int32_t* __restrict__ counts,
+                                                    int32_t Hkv, int32_t cus, int32_t maxs,
+                                                    int32_t num_tokens, int32_t kv_token_bytes,
+                                                    int32_t* __restrict__ nsplit_tok) {
+  plan_body(cu, kv_lens, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, dec,
+            dec_cap, pre, pre_cap, counts, Hkv, cus, maxs, num_tokens, kv_token_bytes, nsplit_tok);
+}
+
+// The step's cache write with its slots computed in place: the new K/V row of packed token t of
+// sequence s (cu[s] <= t < cu[s + 1]) goes to position p = kv_lens[s] - q_s + (t - cu[s]), slot
+// table[s][p / bs] * bs + p % bs ("3.3 Batching & Memory Management", PagedAttention: block
+// tables). Rows with no valid position or slot (p < 0, past the table row, a negative or
+// out-of-pool block) are skipped, as the slot mapping's -1 is. Grid-stride over 16-byte chunks.
+struct WriteArgs {
+  const uint4* k;
+  const uint4* v;
+  uint4* k_cache;
+  uint4* v_cache;
+  const int32_t* tables;
+  int32_t chunks;     // 16-byte chunks per token row (Hkv * D * 2 / 16)
+  int64_t slots;      // num_blocks * bs
+};
+
+__device__ __forceinline__ void write_body(const WriteArgs& w, const int32_t* __restrict__ cu,
+                                           const int32_t* __restrict__ kv_lens, int32_t num_seqs,
+                                           int32_t num_tokens, int32_t bs, int32_t max_blocks,
+                                           int64_t first, int64_t stride) {
+  const int64_t per_tensor = (int64_t)num_tokens * w.chunks;
+  for (int64_t idx = first; idx < 2 * per_tensor; idx += stride) {
+    const bool is_v = idx >= per_tensor;
+    const int64_t r = is_v ? idx - per_tensor : idx;
+    const int32_t t = (int32_t)(r / w.chunks);
+    const int32_t c = (int32_t)(r - (int64_t)t * w.chunks);
+    // the sequence of token t: the last s with cu[s] <= t
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int32_t q = cu[lo + 1] - cu[lo];
+    const int32_t p = kv_lens[lo] - q + (t - cu[lo]);
+    if (p < 0) continue;
+    const int32_t j = p / bs;
+    if (j >= max_blocks) continue;
+    const int32_t blk = w.tables[(int64_t)lo * max_blocks + j];
+    const int64_t slot = (int64_t)blk * bs + p % bs;
+    if (blk < 0 || slot >= w.slots) continue;
+    const uint4* src = is_v ? w.v : w.k;
+    uint4* dst = is_v ? w.v_cache : w.k_cache;
+    dst[slot * w.chunks + c] = src[(int64_t)t * w.chunks + c];
+  }
+}
+
+// Workgroup 0 plans the attention work while the other workgroups write the step's K/V into the
+// cache: the plan does not read the cache, so the two need not wait for each other.
+__global__ __launch_bounds__(1024) void plan_write_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_lens, int32_t num_seqs,
+    int32_t G, int32_t P, int32_t qmaxd, int32_t max_splits, int32_t bq, int32_t bs,
+    int32_t max_blocks, int32_t max_kv, DecWork* __restrict__ dec, int64_t dec_cap,
+    Work* __restrict__ pre, int64_t pre_cap, int32_t* __restrict__ counts, int32_t Hkv,
+    int32_t cus, int32_t maxs, int32_t num_tokens, int32_t kv_token_bytes,
+    int32_t* __restrict__ nsplit_tok, WriteArgs w) {
+  if (blockIdx.x == 0) {
+    plan_body(cu, kv_lens, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, dec,
+              dec_cap, pre, pre_cap, counts, Hkv, cus, maxs, num_tokens, kv_token_bytes, nsplit_tok);
+    return;
+  }
+  write_body(w, cu, kv_lens, num_seqs, num_tokens, bs, max_blocks,
+             (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x, (int64_t)(gridDim.x - 1) * blockDim.x);
 }
 
 // Division of keys (0 <= key < 2^31) by the block size with a multiply and a shift. With
@@ -777,7 +855,6 @@ void prefill_kernel(
   constexpr int LOADERS = kPrefillWaves * 64 < KS * CPR ? kPrefillWaves * 64 : KS * CPR;
   constexpr int RPP = LOADERS / CPR;
   constexpr int PASSES = KS / RPP;
-  constexpr int GPP = RPP / 16;                  // 16-key groups per pass
   static_assert(RPP % 16 == 0 && KS % RPP == 0 && LOADERS % 64 == 0,
                 "a load pass must cover whole 16-key groups");
   using SmemT = PrefillSmem<D>;
@@ -1428,14 +1505,17 @@ extern "C" int cb_time_next_kernel(int32_t which, void* start_event, void* stop_
   return cb::ok();
 }
 
-extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlens_q,
-                                  const int32_t* kv_lens, const int32_t* block_tables,
-                                  const void* k_cache, const void* v_cache, void* out, float scale,
-                                  int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
-                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                  int32_t max_blocks_per_seq, int64_t num_blocks,
-                                  int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// cb_paged_attention, and with k_new / v_new given, cb_paged_attention_write (the cache write
+// runs beside the planning workgroup in the first launch).
+int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                   const int32_t* block_tables, const void* k_cache, const void* v_cache, void* out,
+                   float scale, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_q_len,
+                   int32_t max_kv_len, int32_t kv_split_tokens, void* workspace,
+                   size_t workspace_bytes, void* stream, const void* k_new, const void* v_new) {
   using cb::fail;
   const int E = CB_ERR_INVALID_ARG;
   const KernelTimer tm = g_timer;  // one-shot: consumed by this call
@@ -1487,10 +1567,23 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
   const __bf16* vc = static_cast<const __bf16*>(v_cache);
   __bf16* op = static_cast<__bf16*>(out);
 
-  plan_kernel<<<1, 1024, 0, st>>>(cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd,
-                                  p.max_splits, p.bq, block_size, max_blocks_per_seq, max_kv_len, dec,
-                                  p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus, p.pre_splits,
-                                  num_tokens, 4 * head_dim, nsplit_tok);
+  if (k_new) {
+    WriteArgs w{static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                static_cast<uint4*>(const_cast<void*>(k_cache)), static_cast<uint4*>(const_cast<void*>(v_cache)),
+                block_tables, (int32_t)((int64_t)num_kv_heads * head_dim * 2 / 16),
+                num_blocks * block_size};
+    const int64_t threads = 2 * (int64_t)num_tokens * w.chunks;
+    const int64_t nw = std::min<int64_t>(cb::ceil_div(threads, 1024), 4 * (int64_t)cus);
+    plan_write_kernel<<<(unsigned)(1 + nw), 1024, 0, st>>>(
+        cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd, p.max_splits, p.bq, block_size,
+        max_blocks_per_seq, max_kv_len, dec, p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus,
+        p.pre_splits, num_tokens, 4 * head_dim, nsplit_tok, w);
+  } else {
+    plan_kernel<<<1, 1024, 0, st>>>(cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd,
+                                    p.max_splits, p.bq, block_size, max_blocks_per_seq, max_kv_len, dec,
+                                    p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus, p.pre_splits,
+                                    num_tokens, 4 * head_dim, nsplit_tok);
+  }
   // With prefill work, the decode kernel goes to the second stream and overlaps the prefill.
   hipStream_t dst = st;
   AuxStream aux;
@@ -1580,6 +1673,44 @@ extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlen
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(CB_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   return cb::ok();
+}
+
+}  // namespace
+
+extern "C" int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlens_q,
+                                  const int32_t* kv_lens, const int32_t* block_tables,
+                                  const void* k_cache, const void* v_cache, void* out, float scale,
+                                  int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(q_packed, cu_seqlens_q, kv_lens, block_tables, k_cache, v_cache, out, scale,
+                        num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks, max_q_len, max_kv_len, kv_split_tokens,
+                        workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" int cb_paged_attention_write(const void* q_packed, const void* k_new, const void* v_new,
+                                        const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                        const int32_t* block_tables, void* k_cache, void* v_cache,
+                                        void* out, float scale, int32_t num_seqs, int32_t num_tokens,
+                                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_blocks_per_seq,
+                                        int64_t num_blocks, int32_t max_q_len, int32_t max_kv_len,
+                                        int32_t kv_split_tokens, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && num_tokens > 0) {
+    if (!k_new || !v_new) return cb::fail(CB_ERR_INVALID_ARG, "cb_paged_attention_write: NULL k_new or v_new");
+    if (!cb::aligned16(k_new) || !cb::aligned16(v_new))
+      return cb::fail(CB_ERR_INVALID_ARG, "cb_paged_attention_write: k_new and v_new must be 16-byte aligned");
+    if (num_blocks > 0 && block_size > 0 && num_blocks * (int64_t)block_size > INT32_MAX)
+      return cb::fail(CB_ERR_INVALID_ARG, "num_blocks * block_size must stay below 2^31");
+  }
+  return attention_impl(q_packed, cu_seqlens_q, kv_lens, block_tables, k_cache, v_cache, out, scale,
+                        num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks, max_q_len, max_kv_len, kv_split_tokens,
+                        workspace, workspace_bytes, stream, k_new ? k_new : nullptr, v_new);
 }
 
 extern "C" int cb_split_kv_reduce(const float* o_part, const float* lse_part,

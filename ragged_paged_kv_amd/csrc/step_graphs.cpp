@@ -101,22 +101,18 @@ void release(G* g) {
   if (g->workspace) (void)hipFree(g->workspace);
 }
 
-// The step's three calls on `st` with the device metadata of a padded shape.
+// The step on `st` with the device metadata of a padded shape: slot mapping, cache write and
+// paged attention in one call (the write runs beside the planning workgroup).
 int enqueue_step(G* g, const Key& k, hipStream_t st) {
   const auto& c = g->cfg;
   const int32_t S = std::get<0>(k), T = std::get<1>(k), mq = std::get<2>(k), mkv = std::get<3>(k);
   const int32_t* cu = g->meta;
   const int32_t* kv = cu + c.max_seqs + 1;
   const int32_t* tables = kv + c.max_seqs;
-  int r = cb_slot_mapping(cu, kv, tables, S, T, c.max_blocks_per_seq, c.block_size, g->slots, st);
-  if (r != CB_OK) return r;
-  r = cb_cache_write(c.k, c.v, g->slots, c.k_cache, c.v_cache, T, c.num_kv_heads, c.head_dim,
-                     c.block_size, c.num_blocks, st);
-  if (r != CB_OK) return r;
-  return cb_paged_attention(c.q, cu, kv, tables, c.k_cache, c.v_cache, c.out, c.scale, S, T,
-                            c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size,
-                            c.max_blocks_per_seq, c.num_blocks, mq, mkv, 0, g->workspace,
-                            g->workspace_bytes, st);
+  return cb_paged_attention_write(c.q, c.k, c.v, cu, kv, tables, c.k_cache, c.v_cache, c.out,
+                                  c.scale, S, T, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                  c.block_size, c.max_blocks_per_seq, c.num_blocks, mq, mkv, 0,
+                                  g->workspace, g->workspace_bytes, st);
 }
 
 // A workspace of at least `need` bytes; a replacement drops every recorded graph.
