@@ -111,19 +111,45 @@ def traffic_record_path(workload, op="paged_attention"):
     return os.path.join(ROOT, "profiles", f"{op}_{workload}_hbm_traffic.json")
 
 
-def source_sha256(name="attention.hip"):
-    src = open(os.path.join(ROOT, "ragged_paged_kv_amd", "csrc", name), "rb").read()
-    return hashlib.sha256(src).hexdigest()
+def strip_comments(text):
+    """C/C++ source without its comments, trailing blanks and blank lines: the code itself."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c in "\"'":  # string or character literal, escapes included
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    lines = (l.rstrip() for l in "".join(out).split("\n"))
+    return "\n".join(l for l in lines if l)
+
+
+def code_sha256(name="attention.hip"):
+    """Hash of a kernel source's code (comments and blank lines do not count): counter records
+    taken on one code hash stay valid across comment edits, and only there."""
+    src = open(os.path.join(ROOT, "ragged_paged_kv_amd", "csrc", name), encoding="utf-8").read()
+    return hashlib.sha256(strip_comments(src).encode()).hexdigest()
 
 
 def traffic_from_profile(workload, op="paged_attention", source="attention.hip"):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current kernel code; else None."""
     path = traffic_record_path(workload, op)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256", rec.get("attention_hip_sha256")) != source_sha256(source):
+    if rec.get("code_sha256") != code_sha256(source):
         return None
     return rec.get("bytes_per_launch")
 
@@ -371,7 +397,7 @@ def traffic_summary(args):
     fetch_b = fetch_kib * 1024 * f_fetch
     write_b = write_kib * 1024 * f_write
     rec = {
-        "workload": workload, "kernel": kn, "source": source, "source_sha256": source_sha256(source),
+        "workload": workload, "kernel": kn, "source": source, "code_sha256": code_sha256(source),
         "fetch_kib_per_launch": round(fetch_kib, 1), "write_kib_per_launch": round(write_kib, 1),
         "launches": [nf, nw], "launches_measured": measured,
         "copy_kernel": cn, "copy_bytes": COPY_BYTES,
