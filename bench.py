@@ -17,7 +17,8 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 value = algorithmic bytes of the step / step time (GB/s) for the decode workloads, tokens/s for
 the mixed ones. The roofline object covers the dominant kernel (the decode kernel, HBM-bound, or
 the prefill-chunk kernel, MFMA-bound), timed with HIP events that the library records around
-that kernel on the stream it runs on (cb_time_next_kernel).
+that kernel on the stream it runs on (cb_time_next_kernel): average, median, p10 and p90 over the
+timed steps, and the median after reading a 1 GiB scratch buffer (no input left in any cache).
 
 Block manager data path (its own JSON line, not the default run):
     python bench.py --blocks [--steps K] [--warmup W]
@@ -202,6 +203,16 @@ def cpu_baseline(batch, budget_s=20.0):
     }
 
 
+def pct(xs, q):
+    """The q-quantile (0..1) of xs, nearest rank."""
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, max(0, round(q * (len(ys) - 1))))]
+
+
+FLUSH_BYTES = 1 << 30  # larger than the 256 MB Infinity Cache and the L2s together
+FLUSH_LAUNCHES = 8
+
+
 def measure(args, config, steps, warmup):
     """Generate workload `config`, run warmup + timed steps; returns the batch, its work and the
     timings (step wall time, dominant kernel times from the library's events)."""
@@ -273,8 +284,28 @@ def measure(args, config, steps, warmup):
         "ms_per_step": elapsed / steps * 1e3,
         "attn_ms": sum(attn_ms) / len(attn_ms),
         "kernel_ms": sum(kern_ms) / len(kern_ms),
-        "kernel_ms_median": sorted(kern_ms)[len(kern_ms) // 2],
+        "kernel_ms_median": pct(kern_ms, 0.5),
+        "kernel_ms_p10": pct(kern_ms, 0.1), "kernel_ms_p90": pct(kern_ms, 0.9),
     }
+    # Cache check, outside the timed steps: the same launch after reading a scratch buffer larger
+    # than every cache, so that none of its inputs can still be cached from the previous launch.
+    # A read, not a write: written lines would be dirty, and the measured kernel would pay for
+    # writing them back to HBM as its own reads evict them.
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def flushed(launch):
+        ms = []
+        for i in range(FLUSH_LAUNCHES):
+            torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
+            ev = tuple(torch.cuda.Event(enable_timing=True) for _ in range(4))
+            launch(ev)
+            torch.cuda.synchronize()
+            ms.append(ev[2].elapsed_time(ev[3]))
+        return pct(ms, 0.5)
+
+    if kernel == cb.CB_KERNEL_DECODE:
+        r["kernel_ms_flushed"] = flushed(step)
     log(f"[bench] {b.name}: {steps} steps, {r['ms_per_step']:.4f} ms/step; attention "
         f"{r['attn_ms']:.4f} ms; {'decode' if kernel == cb.CB_KERNEL_DECODE else 'prefill'} kernel "
         f"avg {r['kernel_ms']:.4f} ms (median {r['kernel_ms_median']:.4f}, min {min(kern_ms):.4f}, "
@@ -304,8 +335,21 @@ def measure(args, config, steps, warmup):
         iso_ms = [e0.elapsed_time(e1) for e0, e1 in iso]
         r["step_kernel_ms"] = r["kernel_ms"]
         r["kernel_ms"] = sum(iso_ms) / len(iso_ms)
+        r["kernel_ms_median"] = pct(iso_ms, 0.5)
+        r["kernel_ms_p10"], r["kernel_ms_p90"] = pct(iso_ms, 0.1), pct(iso_ms, 0.9)
+
+        def alone(ev):
+            cb.cb_time_next_kernel(kernel, ev[2], ev[3], stream=stream)
+            cb.cb_paged_attention(qs, cus, kvs, bts, kc, vc, outs, b.scale, mq, mkv, wss,
+                                  stream=stream)
+
+        r["kernel_ms_flushed"] = flushed(alone)
         log(f"[bench] {b.name} prefill chunks alone ({len(pre)} sequences, {len(rows)} tokens): "
             f"prefill kernel avg {r['kernel_ms']:.4f} ms (min {min(iso_ms):.4f}, max {max(iso_ms):.4f})")
+    log(f"[bench] {b.name} {'decode' if kernel == cb.CB_KERNEL_DECODE else 'prefill'} kernel "
+        f"p10 / median / p90 {r['kernel_ms_p10']:.4f} / {r['kernel_ms_median']:.4f} / "
+        f"{r['kernel_ms_p90']:.4f} ms; after reading {FLUSH_BYTES >> 20} MiB to flush the caches (median of "
+        f"{FLUSH_LAUNCHES}) {r['kernel_ms_flushed']:.4f} ms")
     return r
 
 
@@ -318,14 +362,21 @@ def roofline_of(r):
         return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(b.name), "kernel": "decode_kernel",
-                "kernel_ms": round(r["kernel_ms"], 5), "bytes_per_launch": w["decode_kernel_bytes"]}
+                "kernel_ms": round(r["kernel_ms"], 5), "bytes_per_launch": w["decode_kernel_bytes"],
+                **timing_of(r)}
     achieved = w["prefill_flops"] / sec / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_from_profile(b.name), "kernel": "prefill_kernel",
             "kernel_ms": round(r["kernel_ms"], 5), "flops_per_launch": w["prefill_flops"],
             "timed_on": "the batch's prefill chunks alone",
-            "kernel_ms_in_step": round(r["step_kernel_ms"], 5)}
+            "kernel_ms_in_step": round(r["step_kernel_ms"], 5), **timing_of(r)}
+
+
+def timing_of(r):
+    """Spread of the dominant kernel's launch times, and its median time after a cache flush."""
+    return {k: round(r[k], 5) for k in ("kernel_ms_median", "kernel_ms_p10", "kernel_ms_p90",
+                                        "kernel_ms_flushed")}
 
 
 def copy_calibration():

@@ -90,9 +90,9 @@ int cb_slot_mapping(const int32_t* cu_seqlens_q, const int32_t* kv_lens,
  * blocks, and the block-size trade" (a page is one token's K or V in one layer; the cache
  * tensor is the physical store), and "Continuous batching architecture", section "Memory
  * management" (each request holds block ids the attention kernel reads from and writes to).
- * For every token t with slot_mapping[t] >= 0:
+ * For every token t with 0 <= slot = slot_mapping[t] < num_blocks * block_size:
  *     k_cache[slot] = k[t]; v_cache[slot] = v[t]   (all Hkv heads, bit copy)
- * Tokens with slot -1 are skipped. k, v, k_cache, v_cache must be 16-byte aligned and
+ * Tokens with slot -1 are skipped, and so are slots past the pool (nothing is written outside it). k, v, k_cache, v_cache must be 16-byte aligned and
  * Hkv * D must be a multiple of 8. Slots must be distinct (two tokens writing one slot race).
  */
 int cb_cache_write(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache,

@@ -34,11 +34,12 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
 }
 
 // One thread per 16-byte chunk of a token's K row or V row; rows of all Hkv heads are one
-// contiguous [Hkv * D] run in both the new-token tensors and a cache slot.
+// contiguous [Hkv * D] run in both the new-token tensors and a cache slot. Slots outside
+// [0, num_slots) are skipped (-1 marks a token with no slot; larger ones are not in the pool).
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int32_t* __restrict__ slots,
     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int32_t num_tokens,
-    int32_t chunks_per_row) {
+    int32_t chunks_per_row, int64_t num_slots) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_tensor = (int64_t)num_tokens * chunks_per_row;
   if (idx >= 2 * per_tensor) return;
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int64_t t = r / chunks_per_row;
   const int64_t c = r - t * chunks_per_row;
   const int32_t slot = slots[t];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= num_slots) return;
   const uint4* src = is_v ? v : k;
   uint4* dst = is_v ? v_cache : k_cache;
   dst[(int64_t)slot * chunks_per_row + c] = src[t * chunks_per_row + c];
@@ -125,7 +126,7 @@ extern "C" int cb_cache_write(const void* k, const void* v, const int32_t* slot_
   if (grid * 256 > (int64_t)UINT32_MAX) return fail(CB_ERR_UNSUPPORTED, "cb_cache_write: batch too large");
   cache_write_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(
       (const uint4*)k, (const uint4*)v, slot_mapping, (uint4*)k_cache, (uint4*)v_cache,
-      num_tokens, chunks);
+      num_tokens, chunks, num_blocks * block_size);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(CB_ERR_HIP, std::string("cache_write launch: ") + hipGetErrorString(e));

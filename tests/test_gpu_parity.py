@@ -219,6 +219,24 @@ def test_empty_batch_leaves_output(torch_cuda):
     torch.cuda.synchronize()
 
 
+def test_cache_write_skips_slots_outside_the_pool(torch_cuda):
+    """Slot -1 and slots at or past num_blocks * block_size write nothing; the rest are written."""
+    import ragged_paged_kv_amd as cb
+    b = synth.make_config(1, small=True)
+    st = Step(b)
+    pool = b.k_cache.shape[0] * b.block_size
+    slots = np.array([-1, pool, pool + 7, 3, pool - 1], np.int32)
+    n = len(slots)
+    assert st.k.shape[0] >= n
+    kc, vc = dev_bf16(b.k_cache, "cuda"), dev_bf16(b.v_cache, "cuda")
+    cb.cb_cache_write(st.k[:n], st.v[:n], dev_i32(slots, "cuda"), kc, vc)
+    torch_cuda.cuda.synchronize()
+    inside = np.where((slots >= 0) & (slots < pool), slots, -1)
+    k_new, v_new = host_u16(st.k[:n]), host_u16(st.v[:n])
+    ref_k, ref_v = oracle.cache_write(b.k_cache, b.v_cache, k_new, v_new, inside)
+    assert np.array_equal(host_u16(kc), ref_k) and np.array_equal(host_u16(vc), ref_v)
+
+
 def test_workspace_too_small_is_rejected(torch_cuda):
     import ragged_paged_kv_amd as cb
     b = synth.make_config(2, small=True)
