@@ -260,6 +260,41 @@ __device__ inline int seq_items(const int32_t* __restrict__ cu, const int32_t* _
   return 1;
 }
 
+// Inclusive prefix sums of two values over the 1024 threads of the planning workgroup: within
+// each wave by shuffles, then over the 16 wave totals by the first wave. Two barriers; wsum
+// ([16], shared) may be reused after the caller's next barrier.
+__device__ __forceinline__ int2 block_scan2(int a, int b, int2* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ya = __shfl_up(a, off, 64), yb = __shfl_up(b, off, 64);
+    if (lane >= off) {
+      a += ya;
+      b += yb;
+    }
+  }
+  if (lane == 63) wsum[w] = make_int2(a, b);
+  __syncthreads();
+  if (w == 0) {
+    int2 v = lane < 16 ? wsum[lane] : make_int2(0, 0);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int ya = __shfl_up(v.x, off, 64), yb = __shfl_up(v.y, off, 64);
+      if (lane >= off) {
+        v.x += ya;
+        v.y += yb;
+      }
+    }
+    if (lane < 16) wsum[lane] = v;
+  }
+  __syncthreads();
+  if (w > 0) {
+    a += wsum[w - 1].x;
+    b += wsum[w - 1].y;
+  }
+  return make_int2(a, b);
+}
+
 __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
                                           const int32_t* __restrict__ kv_lens,
                                           int32_t num_seqs, int32_t G, int32_t P,
@@ -271,8 +306,7 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
                                           int32_t Hkv, int32_t cus, int32_t maxs,
                                           int32_t num_tokens, int32_t kv_token_bytes,
                                           int32_t* __restrict__ nsplit_tok) {
-  __shared__ int32_t sd[1024];
-  __shared__ int32_t sp[1024];
+  __shared__ int2 wsum[16];
   __shared__ int32_t base[2];
   __shared__ int32_t split_on;
   __shared__ unsigned long long dec_keys;  // sum of decode sequences' lengths
@@ -306,24 +340,14 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
       for (int t = 0; t < np; ++t) stp += (L - qn + min(qn, (t + 1) * bq) + 31) / 32;
       atomicAdd(&pre_steps, stp);
     }
-    sd[tid] = nfull;
-    sp[tid] = np;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int a = tid >= off ? sd[tid - off] : 0;
-      const int b = tid >= off ? sp[tid - off] : 0;
-      __syncthreads();
-      sd[tid] += a;
-      sp[tid] += b;
-      __syncthreads();
-    }
-    const int64_t ed = (int64_t)base[0] + sd[tid] - nfull;
+    const int2 inc = block_scan2(nfull, np, wsum);
+    const int64_t ed = (int64_t)base[0] + inc.x - nfull;
     for (int k = 0; k < nfull; ++k)
       if (ed + k < dec_cap) dec[ed + k] = DecWork{s, k, cu[s], cu[s + 1] - cu[s], kv_lens[s], 0, 0, 0};
     __syncthreads();
     if (tid == 1023) {
-      base[0] += sd[1023];
-      base[1] += sp[1023];
+      base[0] += inc.x;
+      base[1] += inc.y;
     }
     __syncthreads();
   }
@@ -371,15 +395,8 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
         nit += ns;
       }
     }
-    sp[tid] = nit;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int b = tid >= off ? sp[tid - off] : 0;
-      __syncthreads();
-      sp[tid] += b;
-      __syncthreads();
-    }
-    int64_t ep = (int64_t)base[1] + sp[tid] - nit;
+    const int incp = block_scan2(nit, 0, wsum).x;
+    int64_t ep = (int64_t)base[1] + incp - nit;
     if (emax > 1) {
       for (int tl = np - 1; tl >= 0; --tl) {
         int ns, chunk;
@@ -392,7 +409,7 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
         if (ep + k < pre_cap) pre[ep + k] = Work{s, (np - 1 - k) * kMaxPreSplits};
     }
     __syncthreads();
-    if (tid == 1023) base[1] += sp[1023];
+    if (tid == 1023) base[1] += incp;
     __syncthreads();
   }
   if (tid == 0) counts[1] = (int32_t)min((int64_t)base[1], pre_cap);
