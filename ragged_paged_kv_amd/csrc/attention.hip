@@ -635,14 +635,16 @@ void decode_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (4 * g + i) * row_bytes + n * (D / 16) * (uint32_t)sizeof(__bf16);
 
-  // Each wave pulls (partition, KV head) items until the queue is exhausted; every wave leaves
-  // the loop once the shared counter passes `total`. (Taking the next index while the current
+  // Each wave takes (partition, KV head) items until they run out: the active wave w first takes
+  // item w, then items nwaves + k for k = 0, 1, ... from the shared counter, and leaves once its
+  // index passes `total`, so every item is taken once. The first items need no atomic: all
+  // waves starting at once on one counter serialise. (Taking the next index while the current
   // item still streams was measured slower: near the end of the queue it binds short items to
   // waves that are still busy.)
-  while (true) {
-    int idx = 0;
-    if (lane == 0) idx = atomicAdd(queue, 1);
-    idx = __builtin_amdgcn_readfirstlane(idx);
+  const int wpb = (int)(blockDim.x >> 6);
+  const int nwaves = min((int)gridDim.x, counts[4]) * wpb;
+  int idx = __builtin_amdgcn_readfirstlane((int)blockIdx.x * wpb + (int)(threadIdx.x >> 6));
+  for (;; ) {
     if (idx >= total) break;
     const int e = idx / Hkv;
     const int kvh = idx - e * Hkv;
@@ -750,6 +752,9 @@ void decode_kernel(
         if (g == 0) lse_part[base] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
       }
     }
+    int next = 0;
+    if (lane == 0) next = atomicAdd(queue, 1);
+    idx = nwaves + __builtin_amdgcn_readfirstlane(next);
   }
 }
 
