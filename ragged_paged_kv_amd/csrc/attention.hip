@@ -307,6 +307,7 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
                                           int32_t num_tokens, int32_t kv_token_bytes,
                                           int32_t* __restrict__ nsplit_tok) {
   __shared__ int2 wsum[16];
+  __shared__ int32_t first_item[1024];  // index of each thread's first full partition
   __shared__ int32_t base[2];
   __shared__ int32_t split_on;
   __shared__ unsigned long long dec_keys;  // sum of decode sequences' lengths
@@ -341,9 +342,23 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
       atomicAdd(&pre_steps, stp);
     }
     const int2 inc = block_scan2(nfull, np, wsum);
-    const int64_t ed = (int64_t)base[0] + inc.x - nfull;
-    for (int k = 0; k < nfull; ++k)
-      if (ed + k < dec_cap) dec[ed + k] = DecWork{s, k, cu[s], cu[s + 1] - cu[s], kv_lens[s], 0, 0, 0};
+    first_item[tid] = inc.x - nfull;
+    __syncthreads();
+    // The full partitions of these 1024 sequences, written by all threads: item i belongs to the
+    // last thread t with first_item[t] <= i (threads with no full partition share the next one's
+    // first index, so the last such t has one), as partition i - first_item[t] of sequence s0 + t.
+    const int total_items = wsum[15].x;
+    for (int i = tid; i < total_items; i += 1024) {
+      int lo = 0, hi = 1023;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first_item[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      const int sq = s0 + lo;
+      const int64_t ed = (int64_t)base[0] + i;
+      if (ed < dec_cap)
+        dec[ed] = DecWork{sq, i - first_item[lo], cu[sq], cu[sq + 1] - cu[sq], kv_lens[sq], 0, 0, 0};
+    }
     __syncthreads();
     if (tid == 1023) {
       base[0] += inc.x;
@@ -446,7 +461,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 // sequence s (cu[s] <= t < cu[s + 1]) goes to position p = kv_lens[s] - q_s + (t - cu[s]), slot
 // table[s][p / bs] * bs + p % bs ("3.3 Batching & Memory Management", PagedAttention: block
 // tables). Rows with no valid position or slot (p < 0, past the table row, a negative or
-// out-of-pool block) are skipped, as the slot mapping's -1 is. Grid-stride over 16-byte chunks.
+// out-of-pool block) are skipped, as the slot mapping's -1 is. One wave per token (grid-stride):
+// the wave finds the token's sequence, then its lanes copy the K and V rows 16 bytes each.
 struct WriteArgs {
   const uint4* k;
   const uint4* v;
@@ -457,33 +473,42 @@ struct WriteArgs {
   int64_t slots;      // num_blocks * bs
 };
 
+// The sequence of packed token t (0 <= t < cu[num_seqs], num_seqs >= 1): the last s < num_seqs
+// with cu[s] <= t. The lanes compare 64 evenly spaced entries of cu[0 .. num_seqs) at once and the
+// range shrinks 64-fold per round (two rounds up to 4096 sequences). cu is non-decreasing, so
+// the lanes that pass form a prefix; only cu[0 .. num_seqs) is read.
+__device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int num_seqs, int t,
+                                            int lane) {
+  int lo = 0, len = num_seqs;  // cu[lo] <= t holds throughout (cu[0] = 0)
+  while (len > 1) {
+    const int step = (len + 63) / 64;
+    const bool ok = lane * step < len && cu[lo + lane * step] <= t;
+    const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok)) - 1;
+    lo += k * step;
+    len = min(step, len - k * step);
+  }
+  return lo;
+}
+
 __device__ __forceinline__ void write_body(const WriteArgs& w, const int32_t* __restrict__ cu,
                                            const int32_t* __restrict__ kv_lens, int32_t num_seqs,
                                            int32_t num_tokens, int32_t bs, int32_t max_blocks,
-                                           int64_t first, int64_t stride) {
-  const int64_t per_tensor = (int64_t)num_tokens * w.chunks;
-  for (int64_t idx = first; idx < 2 * per_tensor; idx += stride) {
-    const bool is_v = idx >= per_tensor;
-    const int64_t r = is_v ? idx - per_tensor : idx;
-    const int32_t t = (int32_t)(r / w.chunks);
-    const int32_t c = (int32_t)(r - (int64_t)t * w.chunks);
-    // the sequence of token t: the last s with cu[s] <= t
-    int lo = 0, hi = num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cu[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int32_t q = cu[lo + 1] - cu[lo];
-    const int32_t p = kv_lens[lo] - q + (t - cu[lo]);
+                                           int first_wave, int num_waves) {
+  const int lane = threadIdx.x & 63;
+  for (int t = first_wave; t < num_tokens; t += num_waves) {
+    const int s = seq_of_token(cu, num_seqs, t, lane);
+    const int32_t q = cu[s + 1] - cu[s];
+    const int32_t p = kv_lens[s] - q + (t - cu[s]);
     if (p < 0) continue;
     const int32_t j = p / bs;
     if (j >= max_blocks) continue;
-    const int32_t blk = w.tables[(int64_t)lo * max_blocks + j];
+    const int32_t blk = w.tables[(int64_t)s * max_blocks + j];
     const int64_t slot = (int64_t)blk * bs + p % bs;
     if (blk < 0 || slot >= w.slots) continue;
-    const uint4* src = is_v ? w.v : w.k;
-    uint4* dst = is_v ? w.v_cache : w.k_cache;
-    dst[slot * w.chunks + c] = src[(int64_t)t * w.chunks + c];
+    for (int c = lane; c < w.chunks; c += 64) {
+      w.k_cache[slot * w.chunks + c] = w.k[(int64_t)t * w.chunks + c];
+      w.v_cache[slot * w.chunks + c] = w.v[(int64_t)t * w.chunks + c];
+    }
   }
 }
 
@@ -501,8 +526,10 @@ __global__ __launch_bounds__(1024) void plan_write_kernel(
               dec_cap, pre, pre_cap, counts, Hkv, cus, maxs, num_tokens, kv_token_bytes, nsplit_tok);
     return;
   }
+  const int wpb = (int)(blockDim.x >> 6);
   write_body(w, cu, kv_lens, num_seqs, num_tokens, bs, max_blocks,
-             (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x, (int64_t)(gridDim.x - 1) * blockDim.x);
+             __builtin_amdgcn_readfirstlane((int)(blockIdx.x - 1) * wpb + (int)(threadIdx.x >> 6)),
+             (int)(gridDim.x - 1) * wpb);
 }
 
 // Division of keys (0 <= key < 2^31) by the block size with a multiply and a shift. With
@@ -1241,12 +1268,12 @@ void prefill_kernel(
 // the count are read but never used), so a typical row costs one memory round trip.
 constexpr int kReduceBatch = 8;
 
-template <int D>
-__device__ inline void merge_accumulate(const float4 (&a)[kReduceBatch], const float4 (&b)[kReduceBatch],
-                                        const float (&lk)[kReduceBatch], int kmax, float M,
+template <int N>
+__device__ inline void merge_accumulate(const float4 (&a)[N], const float4 (&b)[N],
+                                        const float (&lk)[N], int kmax, float M,
                                         float& wsum, float (&acc)[8]) {
 #pragma unroll
-  for (int k = 0; k < kReduceBatch; ++k) {
+  for (int k = 0; k < N; ++k) {
     // an empty partition (lse = -inf) has no weight and its o is never used
     if (k < kmax && lk[k] != -INFINITY) {
       const float wk = __builtin_amdgcn_exp2f((lk[k] - M) * kLog2e);
@@ -1317,24 +1344,36 @@ __device__ inline void merge_one(int64_t gid, const float* __restrict__ o_part,
 #pragma unroll
   for (int k = 0; k < kReduceBatch; ++k)
     if (k < ns) M = fmaxf(M, lk[k]);
-  for (int k = kReduceBatch; k < ns; ++k) M = fmaxf(M, lse_part[base + k]);
+  // the other partitions' lse, 16 loads in flight at a time (one at a time, a long context's
+  // hundred partitions cost a hundred dependent cache round trips)
+  for (int k0 = kReduceBatch; k0 < ns; k0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = k0 + k < ns ? lse_part[base + k0 + k] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) M = fmaxf(M, x[k]);
+  }
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   float wsum = 0.f;
   if (M != -INFINITY) {
-    merge_accumulate<D>(a, b, lk, ns, M, wsum, acc);
-    for (int k0 = kReduceBatch; k0 < ns; k0 += kReduceBatch) {
+    merge_accumulate(a, b, lk, ns, M, wsum, acc);
+    // the other partitions 16 at a time (more loads in flight per round trip)
+    for (int k0 = kReduceBatch; k0 < ns; k0 += 16) {
+      float lx[16];
+      float4 ax[16], bx[16];
 #pragma unroll
-      for (int k = 0; k < kReduceBatch; ++k) {
+      for (int k = 0; k < 16; ++k) {
+        lx[k] = -INFINITY;
         if (k0 + k < ns) {
-          lk[k] = lse_part[base + k0 + k];
+          lx[k] = lse_part[base + k0 + k];
           const float4* p = reinterpret_cast<const float4*>(o_part + (base + k0 + k) * D + c * 8);
-          a[k] = p[0];
-          b[k] = p[1];
+          ax[k] = p[0];
+          bx[k] = p[1];
         }
       }
-      merge_accumulate<D>(a, b, lk, ns - k0, M, wsum, acc);
+      merge_accumulate(ax, bx, lx, ns - k0, M, wsum, acc);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -1598,8 +1637,8 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
                 static_cast<uint4*>(const_cast<void*>(k_cache)), static_cast<uint4*>(const_cast<void*>(v_cache)),
                 block_tables, (int32_t)((int64_t)num_kv_heads * head_dim * 2 / 16),
                 num_blocks * block_size};
-    const int64_t threads = 2 * (int64_t)num_tokens * w.chunks;
-    const int64_t nw = std::min<int64_t>(cb::ceil_div(threads, 1024), 4 * (int64_t)cus);
+    // one wave per token, 16 waves per workgroup
+    const int64_t nw = std::min<int64_t>(cb::ceil_div(num_tokens, 16), 4 * (int64_t)cus);
     plan_write_kernel<<<(unsigned)(1 + nw), 1024, 0, st>>>(
         cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd, p.max_splits, p.bq, block_size,
         max_blocks_per_seq, max_kv_len, dec, p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus,
