@@ -153,6 +153,46 @@ def test_split_kv_reduce_entry(torch_cuda):
     assert np.all(got[~keep] == 7.0)
 
 
+def _many_partition_batch(which):
+    if which == "d128":
+        return synth.make_config(3, small=True)
+    return tiny_batch([synth.SeqSpec(1, 120), synth.SeqSpec(3, 90), synth.SeqSpec(20, 70)],
+                      16, 2, 64, 16, seed=12)
+
+
+@pytest.mark.parametrize("which", ["d64", "d128"])
+def test_split_kv_reduce_many_partitions(torch_cuda, which):
+    """Rows of more than four load batches of partitions (the merge then splits a row over a group
+    of threads), head_dim 64 and 128, an empty partition first, a token left unwritten."""
+    import ragged_paged_kv_amd as cb
+    torch = torch_cuda
+    b = _many_partition_batch(which)
+    sl, (kc, vc), ref, _ = oracle_step(b)
+    rng = np.random.default_rng(41)
+    bounds = []
+    for L in b.kv_lens.tolist():
+        cuts = sorted(set(rng.integers(1, L, size=min(L - 1, 80)).tolist())) if L > 1 else []
+        bounds.append([0] + cuts + [L])
+    o, lse, ns = oracle.split_partials(b.q, b.cu_seqlens_q, b.kv_lens, b.block_tables, kc, vc,
+                                       b.scale, bounds)
+    assert ns.max() + 1 > 32, "the rows must span more than four load batches"
+    o = np.concatenate([np.full(o.shape[:2] + (1,) + o.shape[3:], np.nan), o], axis=2)
+    lse = np.concatenate([np.full(lse.shape[:2] + (1,), -np.inf), lse], axis=2)
+    ns = ns + 1
+    ns[1] = 0
+    want = oracle.merge_partials(o, lse, ns)
+    out = torch.full(ref.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    cb.cb_split_kv_reduce(torch.from_numpy(o.astype(np.float32)).cuda(),
+                          torch.from_numpy(lse.astype(np.float32)).cuda(),
+                          dev_i32(ns, "cuda"), out)
+    torch.cuda.synchronize()
+    got = oracle.bf16_to_f64(host_u16(out))
+    keep = ns > 0
+    assert_close(got[keep], want[keep], "reduce vs oracle merge")
+    assert_close(got[keep], ref[keep], "reduce vs unsplit oracle")
+    assert np.all(got[~keep] == 7.0)
+
+
 EDGE = {
     # (specs, Hq, Hkv, D, bs)
     "single-key": ([synth.SeqSpec(1, 1)] * 3, 8, 2, 128, 16),
