@@ -122,6 +122,14 @@ def test_workspace_size_and_split_choice():
     p = cb.cb_paged_attention_split_tokens(256, 8, 4096)
     assert p % 32 == 0 and 256 <= p <= 4096
     assert cb.cb_paged_attention_split_tokens(4, 2, 40, 100) == 128   # rounded up to 32
+    # automatic: ~5461 (partition, KV head) items over the upper-bound keys, steps of 256 keys
+    assert cb.cb_paged_attention_split_tokens(256, 8, 4096) == 1536
+    assert cb.cb_paged_attention_split_tokens(64, 8, 8192) == 768
+    assert cb.cb_paged_attention_split_tokens(16, 8, 131072) == 2048     # the cap
+    assert cb.cb_paged_attention_split_tokens(4, 2, 40) == 256          # the floor
+    for S, L in ((1, 100000), (300, 3000), (2048, 512), (7, 65536)):
+        p = cb.cb_paged_attention_split_tokens(S, 8, L)
+        assert p % 256 == 0 and 256 <= p <= 2048
     assert cb.cb_paged_attention_split_tokens(4, 2, 40, 100000) == 2048
     one = cb.cb_paged_attention_workspace_size(4, 27, 4, 2, 64, 16, 24, 40, 64)
     assert one > 0
