@@ -245,7 +245,8 @@ def measure(args, config, steps, warmup):
     out = torch.empty((b.num_tokens, b.num_q_heads, b.head_dim), dtype=torch.bfloat16, device=dev)
     ws = cb.alloc_workspace(b.num_seqs, b.num_tokens, b.num_q_heads, b.num_kv_heads, b.head_dim,
                             b.block_size, b.max_q_len, b.max_kv_len, args.split, device=dev)
-    split = cb.cb_paged_attention_split_tokens(b.num_seqs, b.num_kv_heads, b.max_kv_len, args.split)
+    split = cb.cb_paged_attention_split_tokens(b.num_seqs, b.num_q_heads, b.num_kv_heads,
+                                               b.max_q_len, b.max_kv_len, args.split)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):

@@ -78,7 +78,7 @@ _sig = {
     "cb_slot_mapping": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p]),
     "cb_cache_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _p]),
     "cb_paged_attention_workspace_size": (_sz, [_i32] * 9),
-    "cb_paged_attention_split_tokens": (_i32, [_i32] * 4),
+    "cb_paged_attention_split_tokens": (_i32, [_i32] * 6),
     "cb_paged_attention": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _f, _i32, _i32, _i32, _i32,
                                           _i32, _i32, _i32, _i64, _i32, _i32, _i32, _p, _sz, _p]),
     "cb_paged_attention_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _f, _i32, _i32,
@@ -213,9 +213,10 @@ def cb_paged_attention_workspace_size(num_seqs, num_tokens, num_q_heads, num_kv_
                                                      max_q_len, max_kv_len, kv_split_tokens))
 
 
-def cb_paged_attention_split_tokens(num_seqs, num_kv_heads, max_kv_len, kv_split_tokens=0) -> int:
-    return int(lib.cb_paged_attention_split_tokens(num_seqs, num_kv_heads, max_kv_len,
-                                                   kv_split_tokens))
+def cb_paged_attention_split_tokens(num_seqs, num_q_heads, num_kv_heads, max_q_len, max_kv_len,
+                                    kv_split_tokens=0) -> int:
+    return int(lib.cb_paged_attention_split_tokens(num_seqs, num_q_heads, num_kv_heads, max_q_len,
+                                                   max_kv_len, kv_split_tokens))
 
 
 def alloc_workspace(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,

@@ -119,18 +119,22 @@ def test_kernel_timing_hook_host_checks():
 
 def test_workspace_size_and_split_choice():
     # decode-only batch: only partials and the work list
-    p = cb.cb_paged_attention_split_tokens(256, 8, 4096)
+    p = cb.cb_paged_attention_split_tokens(256, 32, 8, 1, 4096)
     assert p % 32 == 0 and 256 <= p <= 4096
-    assert cb.cb_paged_attention_split_tokens(4, 2, 40, 100) == 128   # rounded up to 32
+    assert cb.cb_paged_attention_split_tokens(4, 4, 2, 1, 40, 100) == 128   # rounded up to 32
     # automatic: ~5461 (partition, KV head) items over the upper-bound keys, steps of 256 keys
-    assert cb.cb_paged_attention_split_tokens(256, 8, 4096) == 1536
-    assert cb.cb_paged_attention_split_tokens(64, 8, 8192) == 768
-    assert cb.cb_paged_attention_split_tokens(16, 8, 131072) == 2048     # the cap
-    assert cb.cb_paged_attention_split_tokens(4, 2, 40) == 256          # the floor
+    assert cb.cb_paged_attention_split_tokens(256, 32, 8, 1, 4096) == 1536
+    assert cb.cb_paged_attention_split_tokens(64, 32, 8, 1, 8192) == 768
+    assert cb.cb_paged_attention_split_tokens(16, 32, 8, 1, 131072) == 2048     # the cap
+    assert cb.cb_paged_attention_split_tokens(4, 4, 2, 1, 40) == 256          # the floor
     for S, L in ((1, 100000), (300, 3000), (2048, 512), (7, 65536)):
-        p = cb.cb_paged_attention_split_tokens(S, 8, L)
+        p = cb.cb_paged_attention_split_tokens(S, 32, 8, 1, L)
         assert p % 256 == 0 and 256 <= p <= 2048
-    assert cb.cb_paged_attention_split_tokens(4, 2, 40, 100000) == 2048
+    # with prefill-type sequences possible (q > 16 / G), 1.5 times the decode-only size
+    assert cb.cb_paged_attention_split_tokens(68, 32, 8, 1024, 8192) == 1280
+    assert cb.cb_paged_attention_split_tokens(68, 32, 8, 4, 8192) == 768      # q = 4: decode-type
+    assert cb.cb_paged_attention_split_tokens(131, 64, 8, 4096, 16384) == 2048
+    assert cb.cb_paged_attention_split_tokens(4, 4, 2, 1, 40, 100000) == 2048
     one = cb.cb_paged_attention_workspace_size(4, 27, 4, 2, 64, 16, 24, 40, 64)
     assert one > 0
     assert cb.cb_paged_attention_workspace_size(0, 0, 4, 2, 64, 16, 1, 1) == 0
