@@ -17,8 +17,9 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 value = algorithmic bytes of the step / step time (GB/s) for the decode workloads, tokens/s for
 the mixed ones. The roofline object covers the dominant kernel (the decode kernel, HBM-bound, or
 the prefill-chunk kernel, MFMA-bound), timed with HIP events that the library records around
-that kernel on the stream it runs on (cb_time_next_kernel): average, median, p10 and p90 over the
-timed steps, and the median after reading a 1 GiB scratch buffer (no input left in any cache).
+that kernel on the stream it runs on (cb_time_next_kernel): average, median, p10 and p90 over K
+further steps (the K timed steps run with no events enqueued), and the median after reading a
+1 GiB scratch buffer (no input left in any cache).
 
 Block manager data path (its own JSON line, not the default run):
     python bench.py --blocks [--steps K] [--warmup W]
@@ -268,16 +269,21 @@ def measure(args, config, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # the K timed steps, with nothing but the step enqueued
+    t_start = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    # K more steps with HIP events around the attention call and the dominant kernel
     events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
-    for ev in events:  # create the events before the timed region
+    for ev in events:  # create the events before the measured steps
         for e in ev:
             e.record(stream)
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
     attn_ms = [e[0].elapsed_time(e[1]) for e in events]
     kern_ms = [e[2].elapsed_time(e[3]) for e in events]
     r = {
