@@ -10,7 +10,7 @@ import pytest
 import synth
 from gpu_helpers import Step, dev_bf16, host_u16, oracle_step, assert_close, say
 from pins import tiny_batch
-from test_gpu_parity import EDGE, _sample_tokens
+from test_gpu_parity import EDGE, _sample_tokens, check_full
 
 pytestmark = pytest.mark.gpu
 
@@ -64,3 +64,22 @@ def test_full_size(n):
         _, _, ref, _ = oracle_step(b, tokens=toks)
         got = out.float().cpu().numpy().astype(np.float64)
         assert_close(got[toks], ref[toks], b.name)
+
+
+@pytest.mark.parametrize("split", [0, 64])
+def test_more_sequences_than_one_planning_pass(split):
+    """1102 sequences: the planning workgroup takes sequences 1024 at a time, and the fused write
+    searches 1102 sequences. Fused and separate paths agree bit for bit, every output row is
+    written, and rows on both sides of the 1024 boundary and the prefill chunks' rows match the
+    oracle (slot mapping and caches whole)."""
+    rng = np.random.default_rng(77)
+    specs = [synth.SeqSpec(1, int(L)) for L in rng.integers(1, 200, 1100)]
+    specs += [synth.SeqSpec(40, 300), synth.SeqSpec(70, 70)]
+    b = tiny_batch(specs, 8, 2, 64, 16, seed=77)
+    say(f"[fused] 1102 sequences split {split}")
+    out = same_as_separate(b, split)
+    assert torch.isfinite(out.float()).all(), "an output row was not written"
+    step = Step(b, kv_split_tokens=split).run()
+    toks = np.concatenate([np.arange(0, 40), np.arange(1000, 1100),
+                           np.arange(b.num_tokens - 110, b.num_tokens)])
+    check_full(b, step, tokens=toks)
