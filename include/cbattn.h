@@ -23,8 +23,10 @@
  *        block_tables  [S, MB]           int32
  *        slot_mapping  [T]               int32   slot of each new token, or -1 = do not write
  *        out           [T, Hq, D]        bf16
- *  - The caller owns every buffer. The library allocates no device memory, does not
- *    synchronize, and keeps no pointer to caller buffers after it returns. Work is enqueued on
+ *  - The caller owns every buffer. The library allocates no device memory (its one device
+ *    array, the scratch of cb_paged_attention_write_noalloc, is placed by the HIP runtime when
+ *    the library's code is loaded on a device), does not synchronize, and keeps no pointer to
+ *    caller buffers after it returns. Work is enqueued on
  *    `stream` (a hipStream_t; NULL means the default stream) in call order. For a batch with
  *    both decode and prefill rows, cb_paged_attention runs its decode kernel on an internal
  *    second stream (created on first use per device and caller stream, default priority, kept
@@ -172,6 +174,37 @@ int cb_paged_attention_write(const void* q_packed, const void* k_new, const void
                              int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                              int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cb_paged_attention_write_noalloc — cb_paged_attention_write with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ * The scratch it needs (work lists, counters, split-KV partials) lives in a device array of
+ * CB_NOALLOC_SCRATCH_BYTES that the library holds, one per device, from the first call on that
+ * device until the process ends; the call allocates nothing (no hipMalloc, hipFree, stream or
+ * event creation). The caller still passes inputs and outputs, as to cb_paged_attention_write.
+ * Differences from cb_paged_attention_write:
+ *  - A batch whose work needs more scratch than CB_NOALLOC_SCRATCH_BYTES returns
+ *    CB_ERR_WORKSPACE (cb_last_error() gives both sizes) and enqueues nothing. Prefill tiles are
+ *    split along the keys only while their partials fit a quarter of the scratch, so results of
+ *    mixed batches may differ from cb_paged_attention_write's by rounding (both are within the
+ *    same tolerance of the exact result); decode-only batches give the same bits.
+ *  - Every kernel runs on `stream` (no internal second stream): with prefill rows the decode
+ *    kernel follows the prefill kernel instead of running beside it.
+ *  - All calls on one device share its scratch, and each call leaves its contents behind: calls
+ *    that may overlap on one device (different streams, or host threads) race and must be
+ *    ordered by the caller. The kernels clear what must start at zero themselves (no memset).
+ * Arguments, preconditions and other errors as cb_paged_attention_write's.
+ */
+#define CB_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int cb_paged_attention_write_noalloc(const void* q_packed, const void* k_new, const void* v_new,
+                                     const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                     const int32_t* block_tables, void* k_cache, void* v_cache,
+                                     void* out, float scale, int32_t num_seqs, int32_t num_tokens,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t max_blocks_per_seq,
+                                     int64_t num_blocks, int32_t max_q_len, int32_t max_kv_len,
+                                     int32_t kv_split_tokens, void* stream);
 
 /*
  * cb_split_kv_reduce — merge per-partition attention results (log-sum-exp merge).

@@ -24,7 +24,8 @@ from ._build import LIB_PATH
 __all__ = [
     "CBError", "LIB_PATH", "lib", "cb_status_string", "cb_last_error", "cb_slot_mapping",
     "cb_cache_write", "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens",
-    "cb_paged_attention", "cb_paged_attention_write", "cb_split_kv_reduce", "cb_validate_batch",
+    "cb_paged_attention", "cb_paged_attention_write", "cb_paged_attention_write_noalloc",
+    "CB_NOALLOC_SCRATCH_BYTES", "cb_split_kv_reduce", "cb_validate_batch",
     "cb_time_next_kernel", "alloc_workspace", "EXPORTED_SYMBOLS", "CB_KERNEL_DECODE", "CB_KERNEL_PREFILL",
     "cb_copy_blocks", "BlockManager", "CB_ERR_OUT_OF_BLOCKS", "StepGraphs",
     "cb_swap_out_blocks", "cb_swap_in_blocks", "cb_carry_over", "AsyncSteps",
@@ -33,7 +34,8 @@ __all__ = [
 EXPORTED_SYMBOLS = (
     "cb_status_string", "cb_last_error", "cb_slot_mapping", "cb_cache_write",
     "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens", "cb_paged_attention",
-    "cb_paged_attention_write", "cb_split_kv_reduce", "cb_validate_batch", "cb_time_next_kernel",
+    "cb_paged_attention_write", "cb_paged_attention_write_noalloc", "cb_split_kv_reduce",
+    "cb_validate_batch", "cb_time_next_kernel",
     # include/cbblocks.h
     "cb_bm_create", "cb_bm_destroy", "cb_bm_add_sequence", "cb_bm_append_tokens",
     "cb_bm_append_batch", "cb_bm_fork",
@@ -84,6 +86,9 @@ _sig = {
     "cb_paged_attention_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _f, _i32, _i32,
                                                 _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
                                                 _p, _sz, _p]),
+    "cb_paged_attention_write_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _f,
+                                                        _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                        _i64, _i32, _i32, _i32, _p]),
     "cb_split_kv_reduce": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "cb_validate_batch": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _i32]),
     "cb_time_next_kernel": (ctypes.c_int, [_i32, _p, _p]),
@@ -274,6 +279,36 @@ def cb_paged_attention_write(q_packed, k_new, v_new, cu_seqlens_q, kv_lens, bloc
         block_tables.shape[1], NB, int(max_q_len), int(max_kv_len), int(kv_split_tokens),
         _dev(workspace, "workspace", torch.uint8, 1), workspace.numel(), _stream(stream)),
         "cb_paged_attention_write")
+
+
+# Bytes of the scratch cb_paged_attention_write_noalloc holds per device (include/cbattn.h).
+CB_NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def cb_paged_attention_write_noalloc(q_packed, k_new, v_new, cu_seqlens_q, kv_lens, block_tables,
+                                     k_cache, v_cache, out, scale: float, max_q_len: int,
+                                     max_kv_len: int, kv_split_tokens: int = 0, stream=None):
+    """cb_paged_attention_write with the library's own scratch instead of a workspace (no device
+    allocation in the call; see include/cbattn.h)."""
+    torch = _torch()
+    T, Hq, D = q_packed.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    S = kv_lens.shape[0]
+    if tuple(out.shape) != (T, Hq, D) or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or k_cache.shape[3] != D or cu_seqlens_q.shape[0] != S + 1 \
+            or block_tables.shape[0] != S or tuple(k_new.shape) != (T, Hkv, D) \
+            or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("cb_paged_attention_write_noalloc: inconsistent shapes")
+    _check(lib.cb_paged_attention_write_noalloc(
+        _dev(q_packed, "q_packed", torch.bfloat16, 3), _dev(k_new, "k_new", torch.bfloat16, 3),
+        _dev(v_new, "v_new", torch.bfloat16, 3),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1), _dev(kv_lens, "kv_lens", torch.int32, 1),
+        _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(k_cache, "k_cache", torch.bfloat16, 4), _dev(v_cache, "v_cache", torch.bfloat16, 4),
+        _dev(out, "out", torch.bfloat16, 3), float(scale), S, T, Hq, Hkv, D, bs,
+        block_tables.shape[1], NB, int(max_q_len), int(max_kv_len), int(kv_split_tokens),
+        _stream(stream)),
+        "cb_paged_attention_write_noalloc")
 
 
 def cb_split_kv_reduce(o_part, lse_part, num_splits, out, stream=None):

@@ -305,7 +305,7 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
                                           int64_t pre_cap, int32_t* __restrict__ counts,
                                           int32_t Hkv, int32_t cus, int32_t maxs,
                                           int32_t num_tokens, int32_t kv_token_bytes,
-                                          int32_t* __restrict__ nsplit_tok) {
+                                          int32_t* __restrict__ nsplit_tok, int32_t beside) {
   __shared__ int2 wsum[16];
   __shared__ int32_t first_item[1024];  // index of each thread's first full partition
   __shared__ int32_t base[2];
@@ -382,10 +382,11 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
     counts[3] = split_on;
     // Compute units for the decode kernel when it runs beside the prefill kernel (one workgroup
     // each): its share of the estimated work, at least half of them (below that its streaming
-    // rate drops). Without prefill work every workgroup of the decode grid works.
+    // rate drops). Without prefill work, or when the decode kernel runs after the prefill kernel
+    // on the same stream (beside = 0), every workgroup of the decode grid works.
     const float t_prefill = (float)pre_steps * Hkv * kPrefillStepUs / cus;
     int n_dec = 1 << 30;
-    if (t_prefill > 0.f && t_decode > 0.f)
+    if (beside && t_prefill > 0.f && t_decode > 0.f)
       n_dec = max(cus / 2, min(cus, (int)(cus * t_decode / (t_decode + t_prefill) + 0.5f)));
     counts[4] = n_dec;
   }
@@ -452,9 +453,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int64_t pre_cap, int32_t* __restrict__ counts,
                                                     int32_t Hkv, int32_t cus, int32_t maxs,
                                                     int32_t num_tokens, int32_t kv_token_bytes,
-                                                    int32_t* __restrict__ nsplit_tok) {
+                                                    int32_t* __restrict__ nsplit_tok,
+                                                    int32_t beside) {
   plan_body(cu, kv_lens, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, dec,
-            dec_cap, pre, pre_cap, counts, Hkv, cus, maxs, num_tokens, kv_token_bytes, nsplit_tok);
+            dec_cap, pre, pre_cap, counts, Hkv, cus, maxs, num_tokens, kv_token_bytes, nsplit_tok,
+            beside);
 }
 
 // The step's cache write with its slots computed in place: the new K/V row of packed token t of
@@ -520,10 +523,11 @@ __global__ __launch_bounds__(1024) void plan_write_kernel(
     int32_t max_blocks, int32_t max_kv, DecWork* __restrict__ dec, int64_t dec_cap,
     Work* __restrict__ pre, int64_t pre_cap, int32_t* __restrict__ counts, int32_t Hkv,
     int32_t cus, int32_t maxs, int32_t num_tokens, int32_t kv_token_bytes,
-    int32_t* __restrict__ nsplit_tok, WriteArgs w) {
+    int32_t* __restrict__ nsplit_tok, int32_t beside, WriteArgs w) {
   if (blockIdx.x == 0) {
     plan_body(cu, kv_lens, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, dec,
-              dec_cap, pre, pre_cap, counts, Hkv, cus, maxs, num_tokens, kv_token_bytes, nsplit_tok);
+              dec_cap, pre, pre_cap, counts, Hkv, cus, maxs, num_tokens, kv_token_bytes, nsplit_tok,
+              beside);
     return;
   }
   const int wpb = (int)(blockDim.x >> 6);
@@ -1478,6 +1482,14 @@ constexpr size_t kPrefillPartialBudget = size_t(256) << 20;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Scratch of the no-allocation entry point (cb_paged_attention_write_noalloc): device memory the
+// library holds for the life of the process, one copy per device, in place of a caller
+// workspace. 128 MiB holds the decode partials of every workload measured here (the largest,
+// 131 sequences of up to 16K keys with 64 query heads, needs 69 MB); prefill partials are held
+// to a quarter of it (tiles whose partials would need more are not split along the keys).
+constexpr size_t kNoAllocScratchBytes = CB_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kNoAllocPrefillBudget = kNoAllocScratchBytes / 4;
+
 int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t requested,
                      bool prefill) {
   if (requested > 0) {
@@ -1499,7 +1511,8 @@ int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t 
 }
 
 Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, int32_t D,
-               int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens) {
+               int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens,
+               size_t pre_budget = kPrefillPartialBudget) {
   Plan p;
   p.G = Hq / Hkv;
   const int32_t dec_q = 16 / p.G;  // longest decode-type chunk
@@ -1510,7 +1523,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, in
   p.dec_cap = (int64_t)num_seqs * p.max_splits;
   if (max_q_len > dec_q) {
     const size_t per_split = (size_t)num_tokens * Hq * (D + 1) * sizeof(float);
-    const size_t fit = per_split > 0 ? kPrefillPartialBudget / per_split : 0;
+    const size_t fit = per_split > 0 ? pre_budget / per_split : 0;
     p.pre_splits = (int32_t)std::min<size_t>(kMaxPreSplits, std::max<size_t>(1, fit));
     if (p.pre_splits < 2) p.pre_splits = 1;
   }
@@ -1639,6 +1652,33 @@ extern "C" int cb_time_next_kernel(int32_t which, void* start_event, void* stop_
 
 namespace {
 
+// The no-allocation entry point's scratch. In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress, once per device, and
+// only that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device (looked up on the first call per device).
+bool scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return false;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return true;
+}
+
+}  // namespace
+
+namespace {
+
 // cb_paged_attention, and with k_new / v_new given, cb_paged_attention_write (the cache write
 // runs beside the planning workgroup in the first launch).
 int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int32_t* kv_lens,
@@ -1647,7 +1687,8 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_q_len,
                    int32_t max_kv_len, int32_t kv_split_tokens, void* workspace,
-                   size_t workspace_bytes, void* stream, const void* k_new, const void* v_new) {
+                   size_t workspace_bytes, void* stream, const void* k_new, const void* v_new,
+                   bool no_alloc = false) {
   using cb::fail;
   const int E = CB_ERR_INVALID_ARG;
   const KernelTimer tm = g_timer;  // one-shot: consumed by this call
@@ -1672,7 +1713,17 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
   if (max_kv_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(E, "max_kv_len exceeds the block-table capacity max_blocks_per_seq * block_size");
   const Plan p = make_plan(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_q_len,
-                           max_kv_len, kv_split_tokens);
+                           max_kv_len, kv_split_tokens,
+                           no_alloc ? kNoAllocPrefillBudget : kPrefillPartialBudget);
+  if (no_alloc) {
+    if (p.total > kNoAllocScratchBytes)
+      return fail(CB_ERR_WORKSPACE, "cb_paged_attention_write_noalloc: this batch needs " +
+                                        std::to_string(p.total) + " bytes of scratch, more than the " +
+                                        std::to_string(kNoAllocScratchBytes) + " the library holds");
+    if (!scratch_address(&workspace))
+      return fail(CB_ERR_HIP, "cb_paged_attention_write_noalloc: hipGetSymbolAddress(scratch) failed");
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (!workspace || workspace_bytes < p.total)
     return fail(CB_ERR_WORKSPACE, "workspace needs " + std::to_string(p.total) + " bytes, got " +
                                       std::to_string(workspace_bytes));
@@ -1709,17 +1760,19 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
     plan_write_kernel<<<(unsigned)(1 + nw), 1024, 0, st>>>(
         cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd, p.max_splits, p.bq, block_size,
         max_blocks_per_seq, max_kv_len, dec, p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus,
-        p.pre_splits, num_tokens, 4 * head_dim, nsplit_tok, w);
+        p.pre_splits, num_tokens, 4 * head_dim, nsplit_tok, no_alloc ? 0 : 1, w);
   } else {
     plan_kernel<<<1, 1024, 0, st>>>(cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd,
                                     p.max_splits, p.bq, block_size, max_blocks_per_seq, max_kv_len, dec,
                                     p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus, p.pre_splits,
-                                    num_tokens, 4 * head_dim, nsplit_tok);
+                                    num_tokens, 4 * head_dim, nsplit_tok, no_alloc ? 0 : 1);
   }
-  // With prefill work, the decode kernel goes to the second stream and overlaps the prefill.
+  // With prefill work, the decode kernel goes to the second stream and overlaps the prefill
+  // (not in the no-allocation variant, which creates no stream: there it follows the prefill
+  // kernel on the caller's stream, with the whole GPU).
   hipStream_t dst = st;
   AuxStream aux;
-  if (p.pre_cap > 0 && p.dec_cap > 0) {
+  if (p.pre_cap > 0 && p.dec_cap > 0 && !no_alloc) {
     if (!aux_stream(st, &aux)) return fail(CB_ERR_HIP, "creating the decode stream failed");
     if (hipEventRecord(aux.fork, st) != hipSuccess || hipStreamWaitEvent(aux.stream, aux.fork, 0) != hipSuccess)
       return fail(CB_ERR_HIP, "decode stream fork failed");
@@ -1837,6 +1890,28 @@ extern "C" int cb_paged_attention_write(const void* q_packed, const void* k_new,
                         num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
                         max_blocks_per_seq, num_blocks, max_q_len, max_kv_len, kv_split_tokens,
                         workspace, workspace_bytes, stream, k_new ? k_new : nullptr, v_new);
+}
+
+
+extern "C" int cb_paged_attention_write_noalloc(
+    const void* q_packed, const void* k_new, const void* v_new, const int32_t* cu_seqlens_q,
+    const int32_t* kv_lens, const int32_t* block_tables, void* k_cache, void* v_cache, void* out,
+    float scale, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    int32_t max_q_len, int32_t max_kv_len, int32_t kv_split_tokens, void* stream) {
+  if (num_seqs > 0 && num_tokens > 0) {
+    if (!k_new || !v_new)
+      return cb::fail(CB_ERR_INVALID_ARG, "cb_paged_attention_write_noalloc: NULL k_new or v_new");
+    if (!cb::aligned16(k_new) || !cb::aligned16(v_new))
+      return cb::fail(CB_ERR_INVALID_ARG,
+                      "cb_paged_attention_write_noalloc: k_new and v_new must be 16-byte aligned");
+    if (num_blocks > 0 && block_size > 0 && num_blocks * (int64_t)block_size > INT32_MAX)
+      return cb::fail(CB_ERR_INVALID_ARG, "num_blocks * block_size must stay below 2^31");
+  }
+  return attention_impl(q_packed, cu_seqlens_q, kv_lens, block_tables, k_cache, v_cache, out, scale,
+                        num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks, max_q_len, max_kv_len, kv_split_tokens,
+                        nullptr, 0, stream, k_new, v_new, /*no_alloc=*/true);
 }
 
 extern "C" int cb_split_kv_reduce(const float* o_part, const float* lse_part,

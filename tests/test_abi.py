@@ -218,3 +218,39 @@ def test_graphs_host_checks():
     assert cb.lib.cb_graphs_run(None, None, None, None, 0, None, None) == -1
     assert cb.lib.cb_graphs_stats(None, None, None, None, None) == -1
     cb.lib.cb_graphs_destroy(None)
+
+
+def noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, kv=FAKE, bt=FAKE, kc=FAKE, vc=FAKE, out=FAKE,
+             scale=0.125, S=4, T=27, Hq=4, Hkv=2, D=64, bs=16, mb=3, nb=32, mq=24, mkv=40, split=0,
+             stream=N)
+    a.update(kw)
+    return cb.lib.cb_paged_attention_write_noalloc(
+        a["q"], a["k"], a["v"], a["cu"], a["kv"], a["bt"], a["kc"], a["vc"], a["out"], a["scale"],
+        a["S"], a["T"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"], a["mq"], a["mkv"],
+        a["split"], a["stream"])
+
+
+def test_noalloc_host_checks():
+    """The no-allocation entry point takes the fused entry point's host checks, and a batch whose
+    work needs more than the library's scratch is refused with both sizes in the message, before
+    anything touches a GPU."""
+    for kw, status in ((dict(bs=3), -1), (dict(D=96), -2), (dict(k=N), -1),
+                       (dict(v=ctypes.c_void_p(0x10008)), -1), (dict(scale=0.0), -1),
+                       (dict(mkv=49), -1)):
+        assert noalloc(**kw) == status, (kw, cb.cb_last_error())
+    assert noalloc(T=0, q=N, k=N, v=N, cu=N, kv=N, bt=N, kc=N, vc=N, out=N) == 0
+    # 512 decode sequences of up to 128K keys, 32 query heads: the split-KV partials alone are
+    # 512 x 64 partitions x 32 heads x 129 floats = 541 MB
+    big = dict(S=512, T=512, Hq=32, Hkv=8, D=128, mb=8192, nb=1 << 17, mq=1, mkv=131072)
+    need = cb.cb_paged_attention_workspace_size(512, 512, 32, 8, 128, 16, 1, 131072, 0)
+    assert need > cb.CB_NOALLOC_SCRATCH_BYTES
+    assert noalloc(**big) == -3
+    msg = cb.cb_last_error()
+    assert str(need) in msg and str(cb.CB_NOALLOC_SCRATCH_BYTES) in msg, msg
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "cbattn.h")).read()
+    m = re.search(r"#define CB_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == cb.CB_NOALLOC_SCRATCH_BYTES
