@@ -7,9 +7,14 @@ in place, runs beside the planning workgroup; then the decode/split-KV and prefi
 log-sum-exp merge); --separate times the same step as the three entry points cb_slot_mapping,
 cb_cache_write, cb_paged_attention.
 Default workload: the Llama-3-8B-shaped decode batch (32 q-heads, 8 KV heads, head_dim 128,
-block 16, 256 sequences with KV length uniform in [128, 4096], physical blocks shuffled); the
-mixed continuous batch of the same model shape (64 decode tokens + 1984 prefill-chunk tokens) is
-measured after it and reported under "mixed_batch".
+block 16, 256 sequences with KV length uniform in [128, 4096], physical blocks shuffled). The
+other full-size workloads of the metric follow it in the same run, each as a sub-object with its
+own roofline and oracle sample: "mixed_batch" (the same model shape, 64 decode tokens + 1984
+prefill-chunk tokens), "long_context_decode" (16 sequences of 32K-128K keys, split-KV partitions
+and the log-sum-exp merge) and "mixed_batch_70b" (64 q-heads / 8 KV heads, block 32, 8192 tokens:
+128 decodes + chunked prefills, a 2048-token prefix shared by a quarter of the sequences).
+"stream_read" is the measured streaming-read rate of this GPU (cb_stream_read over 2 GiB), which
+the decode rooflines are also reported against.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
 
@@ -156,17 +161,38 @@ def traffic_from_profile(workload, op="paged_attention", source="attention.hip")
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(batch, budget_s=20.0):
-    """The oracle (numpy float64, test infrastructure) on this host's cores over a bounded sample
-    of the same workload: slot mapping + cache write over the whole batch, attention over the
-    first sequences that fit the time budget (estimated from a probe)."""
-    import numpy as np
-    import oracle
+def host_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS build numpy's oracle runs on."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    blas, threads = "", 0
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                blas = f"{d.get('internal_api', '')} {d.get('version', '')} ({d.get('threading_layer', '')})"
+                threads = max(threads, int(d.get("num_threads", 1)))
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        pass
+    return {"cpu_model": model, "blas": blas.strip(),
+            "cores": threads or len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(batch, budget_s=20.0, mixed=False):
+    """The oracle (numpy float64, test infrastructure) on this host's cores over a bounded sample
+    of the same workload: slot mapping + cache write over the whole batch, attention over a
+    sample that fits the time budget. Decode workloads: the first sequences (GB/s of their KV).
+    Mixed workloads: every k-th packed token, k chosen from a probe so that the sample fits the
+    budget (tokens/s = sampled tokens / time, an unbiased estimate of the whole batch's rate)."""
+    import numpy as np
+    import oracle
+    info = host_info()
     t0 = time.perf_counter()
     sl = oracle.slot_mapping(batch.cu_seqlens_q, batch.kv_lens, batch.block_tables,
                              batch.block_size)
@@ -174,19 +200,39 @@ def cpu_baseline(batch, budget_s=20.0):
     t_write = time.perf_counter() - t0
     cu = batch.cu_seqlens_q
     Hkv, D = batch.num_kv_heads, batch.head_dim
-    done_tokens = []
+    T = batch.num_tokens
+
+    def attend(toks):
+        t1 = time.perf_counter()
+        oracle.paged_attention(batch.q, cu, batch.kv_lens, batch.block_tables, kc, vc,
+                               batch.scale, tokens=list(toks))
+        return time.perf_counter() - t1
+
+    if mixed:
+        probe_stride = max(1, T // 32)
+        t_probe = attend(range(0, T, probe_stride))
+        per_token = t_probe / len(range(0, T, probe_stride))
+        stride = max(1, int(np.ceil(T * per_token / budget_s)))
+        toks = range(stride // 2, T, stride)
+        t_attn = attend(toks)
+        n = len(toks)
+        t_step = t_attn + t_write * n / T
+        return {
+            "value": round(n / t_step, 1), "unit": "tokens/s", "cores": info["cores"],
+            "kind": "oracle",
+            "sample": (f"numpy float64 oracle: slot mapping + cache write of all {T} tokens "
+                       f"({t_write:.1f} s, counted pro rata) and attention of every {stride}-th "
+                       f"packed token ({n} of {T}, {t_attn:.1f} s)"),
+            "seconds": round(t_attn + t_write + t_probe, 2),
+            "cpu_model": info["cpu_model"], "blas": info["blas"],
+        }
     t_attn = 0.0
     kv_bytes = 0
     s = 0
     while s < batch.num_seqs and t_attn < budget_s:
-        hi = min(batch.num_seqs, s + 16)
-        toks = list(range(int(cu[s]), int(cu[hi])))
-        t1 = time.perf_counter()
-        oracle.paged_attention(batch.q, cu, batch.kv_lens, batch.block_tables, kc, vc,
-                               batch.scale, tokens=toks)
-        t_attn += time.perf_counter() - t1
+        hi = min(batch.num_seqs, s + (16 if batch.num_seqs > 64 else 1))
+        t_attn += attend(range(int(cu[s]), int(cu[hi])))
         kv_bytes += int(batch.kv_lens[s:hi].astype(np.int64).sum()) * 2 * Hkv * D * 2
-        done_tokens += toks
         s = hi
     frac_seqs = s / batch.num_seqs
     # whole-step rate: attention over the sampled sequences, plus the write over the batch
@@ -195,13 +241,51 @@ def cpu_baseline(batch, budget_s=20.0):
     return {
         "value": round(kv_bytes / t_step / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(cores),
+        "cores": info["cores"],
         "kind": "oracle",
-        "sample": (f"numpy float64 oracle: slot mapping + cache write of all {batch.num_tokens} "
+        "sample": (f"numpy float64 oracle: slot mapping + cache write of all {T} "
                    f"tokens ({t_write:.1f} s, counted pro rata) and attention of the first {s} of "
                    f"{batch.num_seqs} sequences ({t_attn:.1f} s, {kv_bytes / 1e9:.3f} GB of KV)"),
         "seconds": round(t_attn + t_write, 2),
+        "cpu_model": info["cpu_model"], "blas": info["blas"],
     }
+
+
+def unique_kv_bytes(b):
+    """KV bytes of the distinct cache slots the batch reads (a block shared by several tables
+    counts once)."""
+    import numpy as np
+    bs = b.block_size
+    slots = []
+    for s in range(b.num_seqs):
+        p = np.arange(int(b.kv_lens[s]), dtype=np.int64)
+        slots.append(b.block_tables[s][p // bs].astype(np.int64) * bs + p % bs)
+    return int(np.unique(np.concatenate(slots)).size) * 2 * b.num_kv_heads * b.head_dim * 2
+
+
+STREAM_BYTES = 2 << 30
+
+
+def stream_ceiling(reps=10):
+    """Measured streaming-read rate: a plain non-temporal 16-byte read of 2 GiB (cb_stream_read),
+    median of `reps` launches, GB/s."""
+    import torch
+    import ragged_paged_kv_amd as cb
+    buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    cb.cb_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cb.cb_stream_read(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    med = pct(ms, 0.5)
+    return {"gbs": round(STREAM_BYTES / (med / 1e3) / 1e9, 1), "bytes": STREAM_BYTES,
+            "ms_median": round(med, 5), "kernel": "cb_stream_read (non-temporal 16-byte loads)"}
 
 
 def pct(xs, q):
@@ -360,24 +444,59 @@ def measure(args, config, steps, warmup):
     return r
 
 
-def roofline_of(r):
+def roofline_of(r, stream_gbs=None):
     import ragged_paged_kv_amd as cb
     w, b = r["work"], r["batch"]
     sec = r["kernel_ms"] / 1e3
     if r["kernel"] == cb.CB_KERNEL_DECODE:
         achieved = w["decode_kernel_bytes"] / sec / 1e9
+        extra = {}
+        if stream_gbs:  # against the measured streaming-read ceiling of this GPU
+            extra = {"stream_ceiling_gbs": stream_gbs, "frac_of_stream_ceiling": round(achieved / stream_gbs, 4)}
         return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(b.name), "kernel": "decode_kernel",
                 "kernel_ms": round(r["kernel_ms"], 5), "bytes_per_launch": w["decode_kernel_bytes"],
-                **timing_of(r)}
+                **extra, **timing_of(r)}
     achieved = w["prefill_flops"] / sec / 1e12
+    in_step = w["prefill_flops"] / (r["step_kernel_ms"] / 1e3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_from_profile(b.name), "kernel": "prefill_kernel",
             "kernel_ms": round(r["kernel_ms"], 5), "flops_per_launch": w["prefill_flops"],
             "timed_on": "the batch's prefill chunks alone",
-            "kernel_ms_in_step": round(r["step_kernel_ms"], 5), **timing_of(r)}
+            "kernel_ms_in_step": round(r["step_kernel_ms"], 5),
+            # the same kernel inside the whole step, where the decode kernel shares the GPU
+            "frac_in_step": round(in_step / BF16_PEAK_TFLOPS, 4), **timing_of(r)}
+
+
+def sub_result(args, config, stream_gbs, cpu_budget_s):
+    """One further workload of the default run, as a sub-object of the JSON line: step time, the
+    workload's metric, its dominant kernel's roofline and the oracle's rate on a sample."""
+    m = measure(args, config, max(5, args.steps // 2), max(2, args.warmup // 2))
+    b, w = m["batch"], m["work"]
+    step_s = m["ms_per_step"] / 1e3
+    mixed = config not in DECODE_CONFIGS
+    out = {
+        "workload": b.name, "num_tokens": b.num_tokens, "num_seqs": b.num_seqs,
+        "kv_tokens": int(b.kv_lens.sum()), "kv_split_tokens": int(m["split"]), "seed": b.seed,
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "tokens_per_s": round(w["T"] / step_s, 1),
+        "step_gbs": round(w["step_bytes"] / step_s / 1e9, 3),
+        "hbm_frac": round(w["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roofline_of(m, stream_gbs),
+    }
+    if mixed:
+        out["prefill_flops"] = w["prefill_flops"]
+    uniq = unique_kv_bytes(b)
+    if uniq < w["kv_bytes"]:  # blocks shared by several sequences: bytes of distinct slots
+        out["kv_bytes_logical"] = w["kv_bytes"]
+        out["kv_bytes_unique"] = uniq
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the oracle on the host cores ({b.name}) ...")
+        out["cpu_baseline"] = cpu_baseline(b, cpu_budget_s, mixed=mixed)
+        log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+    return out
 
 
 def timing_of(r):
@@ -886,7 +1005,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--split", type=int, default=0, help="KV partition tokens (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-batch measurement")
+    ap.add_argument("--no-mixed", action="store_true",
+                    help="measure only --config (skip the other workloads of the default run)")
     ap.add_argument("--separate", action="store_true",
                     help="time the step as cb_slot_mapping + cb_cache_write + cb_paged_attention "
                          "(default: cb_paged_attention_write, the same work in one call)")
@@ -927,6 +1047,8 @@ def main():
         bench_async(args)
         return
 
+    stream = stream_ceiling()
+    log(f"[bench] streaming-read ceiling: {stream['gbs']} GB/s ({stream['bytes']} bytes, median of 10)")
     r = measure(args, args.config, args.steps, args.warmup)
     b, w = r["batch"], r["work"]
     step_s = r["ms_per_step"] / 1e3
@@ -960,24 +1082,21 @@ def main():
         "attention_ms": round(r["attn_ms"], 5),
         "step_bytes": w["step_bytes"],
         "attention_bytes": w["attn_bytes"],
-        "roofline": roofline_of(r),
+        "roofline": roofline_of(r, stream["gbs"]),
         "cpu_baseline": None,
+        "stream_read": stream,
     }
     if w["prefill_flops"]:
         res["prefill_flops"] = w["prefill_flops"]
-    if args.config in DECODE_CONFIGS and not args.no_mixed:
-        m = measure(args, 3, max(5, args.steps // 2), max(2, args.warmup // 2))
-        mb = m["batch"]
-        res["mixed_batch"] = {
-            "workload": mb.name, "num_tokens": mb.num_tokens, "num_seqs": mb.num_seqs,
-            "tokens_per_s": round(m["work"]["T"] / (m["ms_per_step"] / 1e3), 1),
-            "ms_per_step": round(m["ms_per_step"], 5),
-            "roofline": roofline_of(m),
-        }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores ...")
-        res["cpu_baseline"] = cpu_baseline(b)
+        res["cpu_baseline"] = cpu_baseline(b, mixed=args.config not in DECODE_CONFIGS)
         log(f"[bench] cpu baseline: {res['cpu_baseline']}")
+    if args.config == 2 and not args.no_mixed:
+        # the other full-size workloads of the metric, each as its own sub-object
+        res["mixed_batch"] = sub_result(args, 3, stream["gbs"], 8.0)
+        res["long_context_decode"] = sub_result(args, 4, stream["gbs"], 8.0)
+        res["mixed_batch_70b"] = sub_result(args, 5, stream["gbs"], 8.0)
     print(json.dumps(res), flush=True)
 
 

@@ -253,6 +253,20 @@ int cb_validate_batch(const int32_t* cu_seqlens_q, const int32_t* kv_lens,
 enum { CB_KERNEL_DECODE = 1, CB_KERNEL_PREFILL = 2 };
 int cb_time_next_kernel(int32_t which, void* start_event, void* stop_event);
 
+/*
+ * cb_stream_read — measurement aid: read `bytes` of device memory at `buf` once, with 16-byte
+ * non-temporal loads, as fast as the GPU streams HBM. Not an operation of the method: its rate
+ * is the measured streaming-read ceiling that the bandwidth-bound kernels are reported against
+ * beside the 8 TB/s specification.
+ *   buf: device memory, 16-byte aligned; bytes a multiple of 16 (0: nothing is launched).
+ *   sink: device memory of sink_words >= 256 uint32 words, caller-owned; each thread of the
+ *         launch (at most 1024 workgroups of 256, and at most sink_words threads, rounded down
+ *         to 256) writes one word.
+ * Errors: CB_ERR_INVALID_ARG for NULL pointers, misalignment or a sink under 256 words;
+ * CB_ERR_HIP if the launch fails. Enqueued on `stream`; nothing else is read or written.
+ */
+int cb_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

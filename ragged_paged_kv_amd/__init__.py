@@ -26,7 +26,7 @@ __all__ = [
     "cb_cache_write", "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens",
     "cb_paged_attention", "cb_paged_attention_write", "cb_paged_attention_write_noalloc",
     "CB_NOALLOC_SCRATCH_BYTES", "cb_split_kv_reduce", "cb_validate_batch",
-    "cb_time_next_kernel", "alloc_workspace", "EXPORTED_SYMBOLS", "CB_KERNEL_DECODE", "CB_KERNEL_PREFILL",
+    "cb_time_next_kernel", "cb_stream_read", "alloc_workspace", "EXPORTED_SYMBOLS", "CB_KERNEL_DECODE", "CB_KERNEL_PREFILL",
     "cb_copy_blocks", "BlockManager", "CB_ERR_OUT_OF_BLOCKS", "StepGraphs",
     "cb_swap_out_blocks", "cb_swap_in_blocks", "cb_carry_over", "AsyncSteps",
 ]
@@ -35,7 +35,7 @@ EXPORTED_SYMBOLS = (
     "cb_status_string", "cb_last_error", "cb_slot_mapping", "cb_cache_write",
     "cb_paged_attention_workspace_size", "cb_paged_attention_split_tokens", "cb_paged_attention",
     "cb_paged_attention_write", "cb_paged_attention_write_noalloc", "cb_split_kv_reduce",
-    "cb_validate_batch", "cb_time_next_kernel",
+    "cb_validate_batch", "cb_time_next_kernel", "cb_stream_read",
     # include/cbblocks.h
     "cb_bm_create", "cb_bm_destroy", "cb_bm_add_sequence", "cb_bm_append_tokens",
     "cb_bm_append_batch", "cb_bm_fork",
@@ -92,6 +92,7 @@ _sig = {
     "cb_split_kv_reduce": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "cb_validate_batch": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _i32]),
     "cb_time_next_kernel": (ctypes.c_int, [_i32, _p, _p]),
+    "cb_stream_read": (ctypes.c_int, [_p, _sz, _p, _i32, _p]),
     "cb_bm_create": (ctypes.c_int, [_i64, _i32, _p]),
     "cb_bm_destroy": (None, [_p]),
     "cb_bm_add_sequence": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
@@ -323,6 +324,17 @@ def cb_split_kv_reduce(o_part, lse_part, num_splits, out, stream=None):
                                   _dev(out, "out", torch.bfloat16, 3), T, Hq, D, ms,
                                   _stream(stream)),
            "cb_split_kv_reduce")
+
+
+def cb_stream_read(buf, sink, stream=None):
+    """Read every byte of the device tensor ``buf`` once (measurement aid: the streaming-read
+    ceiling); ``sink`` is an int32 device tensor of at least 256 elements."""
+    torch = _torch()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("cb_stream_read: buf must be a contiguous device tensor")
+    _check(lib.cb_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                              _dev(sink, "sink", torch.int32, 1), sink.numel(), _stream(stream)),
+           "cb_stream_read")
 
 
 def _event_handle(ev, stream):

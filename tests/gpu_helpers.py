@@ -101,8 +101,11 @@ def oracle_step(batch: synth.Batch, tokens=None):
 
 
 def assert_close(got, ref, where=""):
+    """The attention bound: |d| <= 2e-2 + 1e-2 |ref| elementwise, and max |d| <= 2e-2 on its own
+    (the max-abs half of the bound, without the relative allowance)."""
     ok, rep = oracle.within_tolerance(got, ref)
     assert ok, f"{where}: outside |d| <= 2e-2 + 1e-2|ref|: {rep}"
+    assert rep["max_abs"] <= oracle.ATOL, f"{where}: max |d| above 2e-2: {rep}"
     return rep
 
 

@@ -160,3 +160,87 @@ def test_async_loop_matches_sync_loop(use_graphs):
     assert np.array_equal(sync_out, async_out)
     say(f"async == sync over {STEPS} steps; last tokens {async_tokens[-1][:6]}")
     assert len({t.tobytes() for t in sync_tokens[1:]}) > 1   # the tokens do change step to step
+
+
+class ScriptedModel(Model):
+    """The stand-in model with a scripted sampler: the token that step n samples for packed row r
+    is fixed in advance (a host table), so every step's inputs are known on the host and the
+    oracle can replay the loop. Each step's attention output is kept for the comparison."""
+
+    def __init__(self, rng, T, script):
+        super().__init__(rng, T)
+        self.script = torch.from_numpy(script).cuda()   # [STEPS, T] int32
+        self.kept = []
+        self.step = 0
+
+    def sample(self, out_ids, T):
+        self.kept.append(self.out[:T].clone())
+        out_ids[:T].copy_(self.script[self.step, :T])
+        self.step += 1
+
+
+@pytest.mark.parametrize("use_graphs", [False, True])
+def test_async_loop_against_oracle(use_graphs):
+    """Every step of an async loop (placeholders, carry-over, A/B slots, three streams) against
+    the oracle replaying the same steps on the host: slot mapping, cache write and attention of
+    each step from host-known inputs. The tokens each step samples are scripted, so the inputs of
+    step n + 1 (carried into its placeholders on the GPU) are known without reading the GPU."""
+    import oracle
+    rng = np.random.default_rng(15)
+    prompts, tables, MB = schedule(rng)
+    T0 = sum(len(p) for p in prompts)
+    T = ((T0 + 15) // 16) * 16
+    NB = S * MB
+    kc0, vc0 = rand_bf16(rng, (NB, BS, HKV, D)), rand_bf16(rng, (NB, BS, HKV, D))
+    script = rng.integers(0, V, (STEPS, T)).astype(np.int32)
+    m = ScriptedModel(np.random.default_rng(9), T, script)
+    eq, ek, ev = (host_u16(x) for x in (m.eq, m.ek, m.ev))
+    scale = 1.0 / np.sqrt(D)
+    kc, vc = dev_bf16(kc0, "cuda"), dev_bf16(vc0, "cuda")
+    a = cb.AsyncSteps(m.q, m.k, m.v, m.out, kc, vc, scale, max_seqs=S + 8, max_kv_len=MB * BS,
+                      max_blocks_per_seq=MB, use_graphs=use_graphs)
+    prev_cu = None
+    for step in range(STEPS):
+        cu, kv = metadata(prompts, step)
+        n = int(cu[-1])
+        slot = a.slot()
+        if step == 0:
+            a.in_ids_host[slot][:n].copy_(torch.from_numpy(np.concatenate(prompts)))
+            carried = 0
+        else:
+            a.in_ids_host[slot][:n].zero_()
+            dest = np.full(int(prev_cu[-1]), -1, np.int32)
+            dest[prev_cu[1:] - 1] = np.arange(S)
+            a.carry_dest_host[slot][:dest.size].copy_(torch.from_numpy(dest))
+            carried = dest.size
+        st = a.begin(cu, kv, tables, carried)
+        with torch.cuda.stream(st):
+            m.pre(a.in_ids[slot], n)
+        a.attention()
+        with torch.cuda.stream(st):
+            m.sample(a.out_ids[slot], n)
+        a.end(n)
+        if step > 0:
+            a.wait(1 - slot)
+        prev_cu = cu
+    a.wait(a.slot() ^ 1)
+    torch.cuda.synchronize()
+    got = [host_u16(o) for o in m.kept]
+    a.close()
+
+    # the oracle replays the loop: step 0 reads the prompts, step n > 0 the token that step n - 1
+    # sampled for each sequence's last row
+    kch, vch = kc0.copy(), vc0.copy()
+    prev_cu = None
+    worst = 0.0
+    for step in range(STEPS):
+        cu, kv = metadata(prompts, step)
+        ids = (np.concatenate(prompts) if step == 0 else script[step - 1][prev_cu[1:] - 1])
+        sl = oracle.slot_mapping(cu, kv, tables, BS)
+        kch, vch = oracle.cache_write(kch, vch, ek[ids], ev[ids], sl)
+        ref, _ = oracle.paged_attention(eq[ids], cu, kv, tables, kch, vch, np.float32(scale))
+        ok, rep = oracle.within_tolerance(oracle.bf16_to_f64(got[step]), ref)
+        assert ok and rep["max_abs"] <= oracle.ATOL, f"step {step}: {rep}"
+        worst = max(worst, rep["max_abs"])
+        prev_cu = cu
+    say(f"async loop == oracle at all {STEPS} steps (graphs {use_graphs}), max_abs {worst:.3g}")

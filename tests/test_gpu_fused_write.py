@@ -54,16 +54,50 @@ def test_edge_cases(name):
     same_as_separate(b)
 
 
-@pytest.mark.parametrize("n", [2, 3])
+def same_as_separate_on_gpu(b):
+    """As same_as_separate, with the caches compared on the GPU (bit patterns as int16): the
+    long-context and 70B-shaped caches are several GB each."""
+    step = Step(b).run()
+    kc, vc, out = fused(step, b)
+    i16 = lambda t: t.view(torch.int16)  # noqa: E731
+    assert torch.equal(i16(kc), i16(step.k_cache)), "k caches differ"
+    assert torch.equal(i16(vc), i16(step.v_cache)), "v caches differ"
+    assert torch.equal(i16(out), i16(step.out)), "outputs differ"
+    return out
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
 def test_full_size(n):
+    """The fused entry point (the step the benchmark times) bit-identical to the three separate
+    ones at every full size, and against the oracle on every decode token and sampled prefill
+    rows (every row of the mixed 2048-token batch: test_full_size_every_element)."""
     b = synth.make_config(n)
     say(f"[fused] full config {n} ({b.name})")
-    out = same_as_separate(b)
-    if n == 2:
+    out = same_as_separate(b) if n in (2, 3) else same_as_separate_on_gpu(b)
+    if n != 3:
         toks = _sample_tokens(b)
         _, _, ref, _ = oracle_step(b, tokens=toks)
         got = out.float().cpu().numpy().astype(np.float64)
-        assert_close(got[toks], ref[toks], b.name)
+        rep = assert_close(got[toks], ref[toks], b.name)
+        say(f"[fused] full config {n}: {len(toks)} tokens against the oracle: {rep}")
+
+
+def test_full_size_every_element():
+    """The mixed 2048-token batch at full size through the fused entry point: every output element
+    of every token (decodes, the 1024-token chunk split along its keys, three prompts) against
+    the oracle, and the caches bit-exact."""
+    b = synth.make_config(3)
+    step = Step(b)
+    kc, vc = dev_bf16(b.k_cache, "cuda"), dev_bf16(b.v_cache, "cuda")
+    out = torch.full_like(step.out, float("nan"))
+    cb.cb_paged_attention_write(step.q, step.k, step.v, step.cu, step.kv_lens, step.tables, kc, vc,
+                                out, b.scale, step.max_q_len, step.max_kv_len, step.ws)
+    torch.cuda.synchronize()
+    _, (kref, vref), ref, _ = oracle_step(b)
+    assert np.array_equal(host_u16(kc), kref) and np.array_equal(host_u16(vc), vref)
+    got = out.float().cpu().numpy().astype(np.float64)
+    rep = assert_close(got, ref, b.name)
+    say(f"[fused] {b.name}: all {b.num_tokens} tokens against the oracle: {rep}")
 
 
 @pytest.mark.parametrize("split", [0, 64])
