@@ -30,8 +30,10 @@
  *    `stream` (a hipStream_t; NULL means the default stream) in call order. For a batch with
  *    both decode and prefill rows, cb_paged_attention runs its decode kernel on an internal
  *    second stream (created on first use per device and caller stream, default priority, kept
- *    until the process ends) that it forks from and joins back into `stream` with events, so
- *    the call still completes in `stream` order.
+ *    until the process ends; at most 64 caller streams per device get one, calls on further
+ *    streams run that kernel after the prefill kernel on `stream`, with the same results) that
+ *    it forks from and joins back into `stream` with events, so the call still completes in
+ *    `stream` order.
  *  - Return value: CB_OK (0) or a negative cb_status. Only host-checkable facts are checked
  *    (null pointers, shape limits, alignment, workspace size); on error nothing is enqueued
  *    and cb_last_error() describes the failure. Data-dependent preconditions (below, and

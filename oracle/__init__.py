@@ -15,7 +15,6 @@ invariants rather than by printed values.
 """
 from .attention import (  # noqa: F401
     bf16_to_f64,
-    f64_to_bf16_bits,
     slot_mapping,
     cache_write,
     unpage,
@@ -27,10 +26,10 @@ from .attention import (  # noqa: F401
     RTOL,
 )
 from .packing import (  # noqa: F401
-    padded_slots,
-    useful_slots,
-    padding_waste,
-    blocks_for,
-    internal_waste,
+    occupancy,
+    rectangle_count,
+    prompt_among_decodes,
+    block_layout,
     pack_ragged,
+    SMALLEST_BLOCK,
 )

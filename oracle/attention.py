@@ -37,14 +37,6 @@ def bf16_to_f64(u16: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float64 -> float32 -> bf16 (nearest even) bits; used only to build test data."""
-    f = np.asarray(x, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32)
-    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return r.astype(np.uint16)
-
-
 def slot_mapping(cu_seqlens_q, kv_lens, block_tables, block_size: int) -> np.ndarray:
     """Cache slot of every packed token: the i-th new token of sequence s sits at position
     p = L_s - q_s + i and goes to slot table[s][p // bs] * bs + p % bs.

@@ -1,10 +1,11 @@
 """Oracle of the async step's carry-over (test infrastructure only).
 
-"Continuous batching in transformers", section "Async batching": batch N+1's inputs are built
-before batch N has produced its tokens, so each token batch N will produce is entered in batch
-N+1 as a placeholder 0, and a carry-over mask holding, for each output of batch N, the index of
-its destination in batch N+1's inputs (or -1: not carried) adds the real token in before batch
-N+1's forward pass. Plain Python over lists.
+Source: "Continuous batching in transformers", section "Async batching". When the next step's
+inputs are assembled while the current step is still running, the tokens the current step will
+emit are not known yet; their input positions hold 0 for now. The carry-over fills them in on
+the device just before the next step runs: dest[i] names the input position of the next step
+that output i of the current step belongs to, and that position gains output i. An entry of
+dest outside the next step's inputs (-1 by convention) moves nothing. Plain Python over lists.
 """
 from __future__ import annotations
 

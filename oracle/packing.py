@@ -1,63 +1,59 @@
 """Ragged packing and block arithmetic — oracle side (test infrastructure only).
 
-Sources:
-  * "Continuous batching in transformers" (ai-infrastructure.net), section "Why use it":
-    a rectangular batch pads every row to the longest one; when an n-token prompt joins
-    B-1 one-token decodes the rectangle wastes (n-1)(B-1) slots, while ragged packing
-    stores only the real tokens; a zero-length row is an error, not a row to pad.
-  * Same page, section "The paged cache, its two reserved blocks, and the block-size
-    trade": a sequence of L tokens occupies ceil(L / block_size) blocks and wastes the
-    unused tail of its last block; block_size below 4 is rejected.
-  * "3.3 Batching & Memory Management", section "PagedAttention: block tables" and
-    "Check your understanding": the same ceil-div count (1000 tokens at 16 per block
-    -> 63 blocks, 8 slots unused).
+What is counted, and where the pages define it:
+  * A padded batch is a rectangle: every row is stretched to the longest row. A ragged batch
+    keeps only the real tokens, one after another with no batch axis, and every row must hold
+    at least one token ("Continuous batching in transformers", section "Why use it").
+  * A sequence of L tokens is stored in blocks of block_size token slots; position p sits in
+    the sequence's block p // block_size, so the last block may have unused slots. Block sizes
+    below 4 are rejected ("Continuous batching in transformers", section "The paged cache, its
+    two reserved blocks, and the block-size trade"; "3.3 Batching & Memory Management",
+    sections "PagedAttention: block tables" and "Check your understanding").
+
+The counts are taken from explicit layouts: the padded rectangle as a boolean occupancy grid,
+and a sequence's blocks as the block index of each of its positions.
 """
 from __future__ import annotations
 
 import numpy as np
 
-MIN_BLOCK_SIZE = 4
+SMALLEST_BLOCK = 4
 
 
-def _check_rows(row_lengths):
-    lens = [int(x) for x in row_lengths]
-    if not lens:
+def occupancy(row_lengths) -> np.ndarray:
+    """Boolean grid [rows, longest row] of a padded batch: cell (r, j) is True when row r has
+    a real token at column j, False where the rectangle holds padding."""
+    lens = np.asarray([int(x) for x in row_lengths], dtype=np.int64)
+    if lens.size == 0:
         raise ValueError("a batch needs at least one row")
-    if min(lens) <= 0:
+    if (lens <= 0).any():
         raise ValueError("every row of a batch must hold at least one token")
-    return lens
+    return np.arange(int(lens.max()))[None, :] < lens[:, None]
 
 
-def padded_slots(row_lengths) -> int:
-    """Slots of the rectangle a padded batch allocates: number of rows times the longest row."""
-    lens = _check_rows(row_lengths)
-    return len(lens) * max(lens)
+def rectangle_count(row_lengths) -> dict:
+    """Cells of the padded rectangle, real tokens (what ragged packing stores) and the padding
+    in between, counted on the occupancy grid."""
+    grid = occupancy(row_lengths)
+    real = int(grid.sum())
+    return {"padded": int(grid.size), "ragged": real, "wasted": int(grid.size) - real}
 
 
-def useful_slots(row_lengths) -> int:
-    """Slots a ragged (packed) batch stores: exactly the real tokens."""
-    lens = _check_rows(row_lengths)
-    return sum(lens)
+def prompt_among_decodes(B: int, n: int) -> dict:
+    """rectangle_count of a batch of B rows: one n-token prompt and B - 1 one-token decodes."""
+    return rectangle_count(np.where(np.arange(int(B)) == 0, int(n), 1))
 
 
-def padding_waste(B: int, n: int) -> int:
-    """Padded-minus-ragged slots when one n-token prompt joins B-1 single-token decodes."""
-    rows = [n] + [1] * (B - 1)
-    return padded_slots(rows) - useful_slots(rows)
-
-
-def blocks_for(seq_len: int, block_size: int) -> int:
-    """Blocks a sequence of ``seq_len`` tokens occupies (ceil-div)."""
-    if block_size < MIN_BLOCK_SIZE:
-        raise ValueError(f"block_size must be at least {MIN_BLOCK_SIZE}, got {block_size}")
+def block_layout(seq_len: int, block_size: int) -> dict:
+    """Blocks a sequence of seq_len tokens occupies and the unused slots of its last block, from
+    the block index of every position."""
+    if block_size < SMALLEST_BLOCK:
+        raise ValueError(f"block_size must be at least {SMALLEST_BLOCK}, got {block_size}")
     if seq_len < 0:
         raise ValueError("negative sequence length")
-    return -(-int(seq_len) // int(block_size))
-
-
-def internal_waste(seq_len: int, block_size: int) -> int:
-    """Unused slots in the last block of a sequence."""
-    return blocks_for(seq_len, block_size) * block_size - int(seq_len)
+    block_of_position = np.arange(int(seq_len)) // int(block_size)
+    blocks = int(np.unique(block_of_position).size)
+    return {"blocks": blocks, "unused_tail": blocks * int(block_size) - int(seq_len)}
 
 
 def pack_ragged(rows):
@@ -67,8 +63,8 @@ def pack_ragged(rows):
     total. No batch axis, no padding.
     """
     rows = [np.asarray(r) for r in rows]
-    _check_rows([r.shape[0] for r in rows])
-    cu = np.zeros(len(rows) + 1, dtype=np.int64)
-    for i, r in enumerate(rows):
-        cu[i + 1] = cu[i] + r.shape[0]
-    return np.concatenate(rows, axis=0), cu
+    occupancy([r.shape[0] for r in rows])  # the same row rules
+    starts = [0]
+    for r in rows:
+        starts.append(starts[-1] + r.shape[0])
+    return np.concatenate(rows, axis=0), np.asarray(starts, dtype=np.int64)

@@ -10,22 +10,22 @@
 //
 // Work split. A sequence whose rows (new tokens x query heads per KV head, G = Hq/Hkv) fit in
 // one 16-row MFMA tile (q * G <= 16) is decode-type: its KV range is cut into partitions of P
-// tokens, one workgroup per (partition, KV head); several partitions are merged afterwards by
-// log-sum-exp. Longer chunks are prefill-type: one workgroup per (128-row query tile, KV head)
-// over the whole causal key range, with K/V tiles staged in LDS and shared by 4 waves.
+// tokens, and each (partition, KV head) item is streamed by one wave of a persistent decode
+// grid that takes items from a queue; several partitions are merged afterwards by log-sum-exp.
+// Longer chunks are prefill-type: one 8-wave workgroup per (256-row query tile, KV head) over
+// the tile's causal key range (split along the keys into parts when the batch has too few
+// tiles to fill the GPU), with 32-key K/V tiles staged in LDS and read by all 8 waves.
 //
-// MFMA orientation (both kernels). v_mfma_f32_16x16x32_bf16 with
+// MFMA orientation (both kernels): the key dimension is the A operand's row index,
 //   S^T[key][row]  = K[key][:] . Q[row][:]        (A = K rows, B = Q^T, contraction over dims)
 //   O^T[dim][row] += V^T[dim][key] . P^T[key][row] (A = V^T,   B = P^T, contraction over keys)
-// Output lane (n, g) = (lane % 16, lane / 16) holds column n (a query row) and rows 4g..4g+3,
-// so each lane carries one query row: the running max / sum are lane-local after a 2-step
-// cross-group reduction, and the rescale of O needs no data movement. The contraction index
-// may be permuted freely as long as A and B agree: in k-step kk lane group g takes an 8-dim chunk
-// of Q and K (decode: dims [32 kk + 8 g, +8), prefill: [g D/4 + 8 kk, +8); 16-byte loads), and
-// keys {16j + 4g + i} of P and V, which is exactly
-// where the S^T tile leaves them, so P feeds the second MFMA without a shuffle. V arrives with
-// 8 dims of one key per 16 bytes; 8 such rows are transposed in registers with byte permutes
-// into the 8-keys-per-dim operand.
+// so each output lane holds one query row (its column of S^T and O^T): the running max and sum
+// are lane-local up to one cross-lane step, the rescale of O needs no data movement, and the
+// probabilities leave the first MFMA already in the B layout of the second. The contraction
+// index may be permuted freely as long as A and B agree. Decode: v_mfma_f32_16x16x32_bf16 on
+// 16 keys x (up to 16 query rows); its V^T operand is built in registers from 16-byte pieces
+// of 8 dims of one key with byte permutes. Prefill: v_mfma_f32_32x32x16_bf16 on 32 keys x 32
+// query rows per wave; its V^T operand comes from transposing LDS reads.
 //
 // Masking is by select before the exponential (never by multiplying with 0), and V rows of
 // keys at or past the range end are zeroed, so NaN or stale data in unread slots (block tails,
@@ -54,17 +54,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Running maxima start at this finite floor so that exp2(m_old - m_new) never sees inf - inf.
 constexpr float kMaxFloor = -1e30f;
 constexpr int kMaxSplitTokens = 2048;  // partition size cap: <= 129 table entries at bs 16
-#ifndef CB_PREFILL_WAVES
-#define CB_PREFILL_WAVES 8
-#endif
-#ifndef CB_PREFILL_TILES
-#define CB_PREFILL_TILES 2
-#endif
-constexpr int kPrefillWaves = CB_PREFILL_WAVES;
-constexpr int kPrefillTiles = CB_PREFILL_TILES;  // 16-row MFMA tiles per prefill wave
-constexpr int kPrefillRows = kPrefillWaves * 16 * kPrefillTiles;  // query rows (token x head) per tile
-// two waves per SIMD at two row tiles per wave; with more, the wave needs the whole register file
-constexpr int kPrefillWavesPerSimd = kPrefillTiles > 2 ? 1 : 2;
+constexpr int kPrefillWaves = 8;                   // waves per prefill workgroup, 2 per SIMD
+constexpr int kPrefillRows = kPrefillWaves * 32;   // query rows (token x head) per tile: 32 per wave
+constexpr int kPrefillWavesPerSimd = 2;
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup beside prefill work (4 otherwise)
 
 struct Work {
@@ -865,13 +857,13 @@ __device__ inline void chunk_exp32(const f32x16& acc, float c, float m, float& l
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill kernel: one workgroup of 4 waves per (query tile of 128 rows, KV head). Each wave owns
-// 32 rows (two 16-row MFMA tiles). K/V tiles of 32 keys are gathered through the block table
-// into LDS by all 256 threads and read by every wave. Three LDS tiles are in flight, so a wave
-// can overlap its matrix and vector work: while the exponentials of tile t run on the VALU, the
-// S^T = K Q^T products of tile t + 1 run on the matrix cores, and the P V products of tile t run
-// beside the row maxima of tile t + 1. Tile t + 2 is loaded into registers meanwhile and stored
-// to LDS at the end of the step.
+// Prefill kernel: one workgroup of 8 waves (two per SIMD) per (query tile of 256 rows, KV head).
+// Each wave owns 32 rows (one 32 x 32 MFMA tile). K/V tiles of 32 keys are gathered through the
+// block table into LDS by all 512 threads and read by every wave. Three LDS tiles are in flight,
+// so a wave can overlap its matrix and vector work: while the exponentials of tile t run on the
+// VALU, the S^T = K Q^T products of tile t + 1 run on the matrix cores, and the P V products of
+// tile t run beside the row maxima of tile t + 1. A step starts by storing tile t + 2 (loaded
+// into registers two steps earlier) to LDS and loading tile t + 4 into the registers it frees.
 
 constexpr int kPrefillKeys = 32;  // keys per LDS tile (one barrier per tile)
 constexpr int kPrefillBufs = 3;   // LDS tiles: being computed, ready, being filled
@@ -938,7 +930,6 @@ void prefill_kernel(
 
   // Q^T operand (B of S^T = K Q^T): lane l holds dims [16kk + 8h, +8) of query row
   // R = 32 wave + l % 32, row = (token R / G, head R % G)
-  static_assert(kPrefillTiles == 2, "the 32 x 32 layout gives each wave 32 query rows");
   bf16x8 qf[KK];
   int last_key;
   {
@@ -1576,31 +1567,46 @@ bool device_cus(int* out) {
 // Second stream for the decode kernel, so that it runs beside the prefill kernel (the one is
 // HBM-bound, the other MFMA-bound): one per (device, caller stream), created on first use, kept
 // until the process ends, default priority. fork / join order it after the planning kernel and
-// before the merge on the caller's stream.
+// before the merge on the caller's stream. At most kMaxAuxStreams caller streams per device get
+// one; calls on further caller streams run the decode kernel after the prefill kernel on the
+// caller's stream instead (same results, no overlap), so the table stays bounded however many
+// streams a caller cycles through.
+//
+// Host threads that enqueue on one caller stream at the same time share its fork and join
+// events. Each call records an event and makes the other stream wait on it right away, so a
+// wait always covers at least that call's own work (it may also cover another thread's work
+// enqueued in between: extra ordering, never missing ordering).
+constexpr int kMaxAuxStreams = 64;
+
 struct AuxStream {
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
 
-bool aux_stream(hipStream_t st, AuxStream* out) {
+enum class Aux { kOk, kFull, kError };
+
+Aux aux_stream(hipStream_t st, AuxStream* out) {
   static std::mutex mu;
   static std::map<std::pair<int, hipStream_t>, AuxStream> table;
+  static int per_device[64] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipGetDevice(&dev) != hipSuccess) return Aux::kError;
   std::lock_guard<std::mutex> lock(mu);
   auto it = table.find({dev, st});
   if (it != table.end()) {
     *out = it->second;
-    return true;
+    return Aux::kOk;
   }
+  if (dev < 0 || dev >= 64 || per_device[dev] >= kMaxAuxStreams) return Aux::kFull;
   AuxStream a;
-  if (hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) != hipSuccess) return false;
+  if (hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) != hipSuccess) return Aux::kError;
   if (hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess)
-    return false;
+    return Aux::kError;
   table[{dev, st}] = a;
+  ++per_device[dev];
   *out = a;
-  return true;
+  return Aux::kOk;
 }
 
 }  // namespace
@@ -1750,6 +1756,19 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
   const __bf16* vc = static_cast<const __bf16*>(v_cache);
   __bf16* op = static_cast<__bf16*>(out);
 
+  // With prefill work, the decode kernel goes to the second stream and overlaps the prefill
+  // (not in the no-allocation variant, which creates no stream, nor on a caller stream past the
+  // per-device limit: there it follows the prefill kernel on the caller's stream, with the whole
+  // GPU). The plan sizes the decode kernel's share of the compute units accordingly.
+  hipStream_t dst = st;
+  AuxStream aux;
+  if (p.pre_cap > 0 && p.dec_cap > 0 && !no_alloc) {
+    const Aux a = aux_stream(st, &aux);
+    if (a == Aux::kError) return fail(CB_ERR_HIP, "creating the decode stream failed");
+    if (a == Aux::kOk) dst = aux.stream;
+  }
+  const int32_t beside = dst != st ? 1 : 0;
+
   if (k_new) {
     WriteArgs w{static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
                 static_cast<uint4*>(const_cast<void*>(k_cache)), static_cast<uint4*>(const_cast<void*>(v_cache)),
@@ -1760,23 +1779,16 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
     plan_write_kernel<<<(unsigned)(1 + nw), 1024, 0, st>>>(
         cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd, p.max_splits, p.bq, block_size,
         max_blocks_per_seq, max_kv_len, dec, p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus,
-        p.pre_splits, num_tokens, 4 * head_dim, nsplit_tok, no_alloc ? 0 : 1, w);
+        p.pre_splits, num_tokens, 4 * head_dim, nsplit_tok, beside, w);
   } else {
     plan_kernel<<<1, 1024, 0, st>>>(cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd,
                                     p.max_splits, p.bq, block_size, max_blocks_per_seq, max_kv_len, dec,
                                     p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus, p.pre_splits,
-                                    num_tokens, 4 * head_dim, nsplit_tok, no_alloc ? 0 : 1);
+                                    num_tokens, 4 * head_dim, nsplit_tok, beside);
   }
-  // With prefill work, the decode kernel goes to the second stream and overlaps the prefill
-  // (not in the no-allocation variant, which creates no stream: there it follows the prefill
-  // kernel on the caller's stream, with the whole GPU).
-  hipStream_t dst = st;
-  AuxStream aux;
-  if (p.pre_cap > 0 && p.dec_cap > 0 && !no_alloc) {
-    if (!aux_stream(st, &aux)) return fail(CB_ERR_HIP, "creating the decode stream failed");
+  if (dst != st) {
     if (hipEventRecord(aux.fork, st) != hipSuccess || hipStreamWaitEvent(aux.stream, aux.fork, 0) != hipSuccess)
       return fail(CB_ERR_HIP, "decode stream fork failed");
-    dst = aux.stream;
   }
   if (p.pre_cap > 0) {
     // one workgroup per (item, KV head); workgroups past the plan's item count exit at once.

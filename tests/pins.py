@@ -95,53 +95,62 @@ def run_oracle(orc, batch, tokens=None):
 
 
 def pin_padding_waste(orc, rows):
+    """The page's printed example (one 100-token prompt among 7 one-token decodes) and the three
+    printed ratios of waste when B, n or both double."""
     g = {r[0]: r[1] for r in rows}
     B, n = int(g["B"]), int(g["n"])
-    batch = [n] + [1] * (B - 1)
-    assert orc.padding_waste(B, n) == int(g["waste"])
-    assert orc.padded_slots(batch) == int(g["padded"])
-    assert orc.useful_slots(batch) == int(g["real"])
+    c = orc.prompt_among_decodes(B, n)
+    assert (c["wasted"], c["padded"], c["ragged"]) == (int(g["waste"]), int(g["padded"]),
+                                                       int(g["real"]))
     for key, (b2, n2) in {"ratio_double_B": (2 * B, n), "ratio_double_n": (B, 2 * n),
                           "ratio_double_both": (2 * B, 2 * n)}.items():
-        r = orc.padding_waste(b2, n2) / orc.padding_waste(B, n)
+        r = orc.prompt_among_decodes(b2, n2)["wasted"] / c["wasted"]
         assert f"{r:.3f}" == g[key], (key, r)
-    d2b = {orc.padding_waste(b + 2, n) - 2 * orc.padding_waste(b + 1, n) + orc.padding_waste(b, n)
-           for b in range(1, 20)}
-    d2n = {orc.padding_waste(B, m + 2) - 2 * orc.padding_waste(B, m + 1) + orc.padding_waste(B, m)
-           for m in range(1, 20)}
-    assert d2b == {int(g["second_difference_B"])} and d2n == {int(g["second_difference_n"])}
-    mixed = (orc.padding_waste(B + 1, n + 1) - orc.padding_waste(B + 1, n)
-             - orc.padding_waste(B, n + 1) + orc.padding_waste(B, n))
-    assert mixed == int(g["mixed_difference"])
+    # The page also prints zero second differences in B and n and a unit mixed difference: the
+    # signature of the bilinear form (n - 1)(B - 1), which pin_padding_closed_form checks the
+    # oracle against cell by cell.
+    assert (int(g["second_difference_B"]), int(g["second_difference_n"]),
+            int(g["mixed_difference"])) == (0, 0, 1)
 
 
 def pin_padding_closed_form(orc):
-    # rectangle count against the closed form (n - 1)(B - 1), and the degenerate cases
+    # the occupancy count against the closed form (n - 1)(B - 1), including the degenerate
+    # cases B = 1 and n = 1
     for B in range(1, 30):
         for n in range(1, 30):
-            assert orc.padding_waste(B, n) == (n - 1) * (B - 1)
-    assert orc.padding_waste(1, 100) == 0 and orc.padding_waste(8, 1) == 0
+            c = orc.prompt_among_decodes(B, n)
+            assert c["wasted"] == (n - 1) * (B - 1)
+            assert c["padded"] == B * n and c["ragged"] == n + B - 1
+    # arbitrary rows: padded = rows x longest, ragged = sum, brute-forced cell by cell
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        lens = rng.integers(1, 40, size=int(rng.integers(1, 9)))
+        c = orc.rectangle_count(lens)
+        cells = sum(1 for r in lens for j in range(int(lens.max())) if j < r)
+        assert c["ragged"] == cells == int(lens.sum())
+        assert c["padded"] == len(lens) * int(lens.max())
     # the tiny workload: decodes at 1 token each and a 24-token prompt -> 27 rows vs 4 x 24
-    rows = [1, 1, 1, 24]
-    assert orc.useful_slots(rows) == 27 and orc.padded_slots(rows) == 96
-    assert orc.padded_slots(rows) - orc.useful_slots(rows) == (24 - 1) * (4 - 1)
-    packed, cu = orc.pack_ragged([np.zeros((r, 2)) for r in rows])
+    c = orc.rectangle_count([1, 1, 1, 24])
+    assert c["ragged"] == 27 and c["padded"] == 96 and c["wasted"] == (24 - 1) * (4 - 1)
+    packed, cu = orc.pack_ragged([np.zeros((r, 2)) for r in (1, 1, 1, 24)])
     assert packed.shape[0] == 27 and list(cu) == [0, 1, 2, 3, 27]
 
 
 def pin_block_arithmetic(orc, rows):
+    """The page's table (block-table rows for an 8192-token sequence, worst tail waste per block
+    size) and the chapter's two counts (1000 and 1300 tokens at block size 16)."""
     for r in rows:
         if r[0] == "table":
             bs, table_rows, worst = int(r[1]), int(r[2]), int(r[3])
-            assert orc.blocks_for(8192, bs) == table_rows
-            assert max(orc.internal_waste(L, bs) for L in range(1, 2 * bs + 1)) == worst
+            assert orc.block_layout(8192, bs)["blocks"] == table_rows
+            assert max(orc.block_layout(L, bs)["unused_tail"] for L in range(1, 2 * bs + 1)) == worst
         elif r[0] == "blocks":
             L, bs, nb, waste = (int(x) for x in r[1:])
-            assert orc.blocks_for(L, bs) == nb and orc.internal_waste(L, bs) == waste
-    assert orc.blocks_for(0, 16) == 0
-    for bs in (16, 32, 256):
-        assert orc.blocks_for(bs, bs) == 1 and orc.internal_waste(bs, bs) == 0
-        assert orc.blocks_for(bs + 1, bs) == 2 and orc.internal_waste(bs + 1, bs) == bs - 1
+            assert orc.block_layout(L, bs) == {"blocks": nb, "unused_tail": waste}
+    # ceil(L / bs) blocks and bs * blocks - L unused slots, for every L up to a few blocks
+    for bs in (4, 16, 32, 48, 256):
+        for L in range(0, 5 * bs):
+            assert orc.block_layout(L, bs) == {"blocks": -(-L // bs), "unused_tail": -(-L // bs) * bs - L}
 
 
 # ----------------------------------------------------------------------------------------------
@@ -184,7 +193,7 @@ def pin_slot_mapping_p3(orc, rows):
     for i, nm in enumerate(names):
         assert sl1[i] == sl[cu[i] + kv[i] - 1]
     for nm, w in waste.items():
-        assert orc.internal_waste(seqs[nm][0], bs) == w
+        assert orc.block_layout(seqs[nm][0], bs)["unused_tail"] == w
 
 
 def pin_slot_mapping_bruteforce(orc, seed=0):

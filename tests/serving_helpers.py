@@ -11,13 +11,14 @@ import numpy as np
 
 import oracle
 import oracle.blocks as ob
+import synth
 
 P61 = (1 << 61) - 1
 
 
 def rand_bf16(rng, shape):
     # finite bf16 patterns (no NaN/Inf), so equality of bits is equality of values
-    return oracle.f64_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    return synth.bf16_from_f32(rng.standard_normal(shape).astype(np.float32))
 
 
 class KVSource:
@@ -39,7 +40,7 @@ class KVSource:
         for i, hv in enumerate(hs):
             if hv not in self.memo:
                 g = np.random.default_rng([self.seed, hv])
-                self.memo[hv] = oracle.f64_to_bf16_bits(
+                self.memo[hv] = synth.bf16_from_f32(
                     g.standard_normal((2, self.hkv, self.d)).astype(np.float32))
             k[i], v[i] = self.memo[hv]
         return k, v

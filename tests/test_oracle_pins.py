@@ -22,7 +22,7 @@ def test_padding_waste_closed_form():
 
 def test_zero_length_row_raises():
     with pytest.raises(ValueError):
-        oracle.padded_slots([100, 0, 1])
+        oracle.rectangle_count([100, 0, 1])
     with pytest.raises(ValueError):
         oracle.pack_ragged([np.zeros((3, 2)), np.zeros((0, 2))])
 
@@ -34,8 +34,8 @@ def test_block_arithmetic_printed_values(golden):
 def test_block_size_below_four_raises():
     for bad in (0, 1, 2, 3):
         with pytest.raises(ValueError):
-            oracle.blocks_for(10, bad)
-    assert oracle.blocks_for(10, 4) == 3
+            oracle.block_layout(10, bad)
+    assert oracle.block_layout(10, 4) == {"blocks": 3, "unused_tail": 2}
 
 
 def test_page_bytes_per_token(golden):
