@@ -184,6 +184,19 @@ def host_info():
             "cores": threads or len(os.sched_getaffinity(0))}
 
 
+def clock_from_profile(workload):
+    """The prefill kernel's clock (GHz) and MFMA-busy fraction under its own load on this
+    workload, from the committed SQ / GRBM counter run, if it was taken on the current kernel
+    code; else None."""
+    path = os.path.join(ROOT, "profiles", "prefill_kernel_mfma_busy.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("code_sha256") != code_sha256(rec.get("source", "attention.hip")):
+        return None
+    return rec.get("workloads", {}).get(workload)
+
+
 def cpu_baseline(batch, budget_s=20.0, mixed=False):
     """The oracle (numpy float64, test infrastructure) on this host's cores over a bounded sample
     of the same workload: slot mapping + cache write over the whole batch, attention over a
@@ -467,7 +480,9 @@ def roofline_of(r, stream_gbs=None):
             "timed_on": "the batch's prefill chunks alone",
             "kernel_ms_in_step": round(r["step_kernel_ms"], 5),
             # the same kernel inside the whole step, where the decode kernel shares the GPU
-            "frac_in_step": round(in_step / BF16_PEAK_TFLOPS, 4), **timing_of(r)}
+            "frac_in_step": round(in_step / BF16_PEAK_TFLOPS, 4),
+            # measured clock and MFMA-busy fraction under this load (committed counter run)
+            "counters": clock_from_profile(b.name), **timing_of(r)}
 
 
 def sub_result(args, config, stream_gbs, cpu_budget_s):

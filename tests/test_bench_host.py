@@ -63,3 +63,15 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in r.stderr and not r.stdout.strip()
+
+
+def test_clock_record(bench):
+    """The prefill kernel's counter record: MFMA busy is a fraction, the clock sits below the
+    2.4 GHz the dense-peak figure assumes, and the bench returns it only on the current code."""
+    path = os.path.join(ROOT, "profiles", "prefill_kernel_mfma_busy.json")
+    r = json.load(open(path))
+    assert r["workloads"]
+    for w, v in r["workloads"].items():
+        assert 0 < v["mfma_busy"] < 1 and 1.0 < v["clock_ghz"] <= 2.45, (w, v)
+        got = bench.clock_from_profile(w)
+        assert got == (v if r["code_sha256"] == bench.code_sha256(r["source"]) else None)
