@@ -254,3 +254,14 @@ def test_noalloc_scratch_size_matches_header():
     text = open(os.path.join(ROOT, "include", "cbattn.h")).read()
     m = re.search(r"#define CB_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == cb.CB_NOALLOC_SCRATCH_BYTES
+
+
+def test_stream_read_host_checks():
+    f = cb.lib.cb_stream_read
+    sink = ctypes.c_void_p(0x20000)
+    assert f(FAKE, 0, N, 0, N) == 0                                 # nothing to read: no launch
+    assert f(N, 1024, sink, 256, N) == -1                           # NULL buffer
+    assert f(FAKE, 1024, N, 256, N) == -1                           # NULL sink
+    assert f(ctypes.c_void_p(0x10008), 1024, sink, 256, N) == -1    # misaligned
+    assert f(FAKE, 1000, sink, 256, N) == -1                        # not a multiple of 16 bytes
+    assert f(FAKE, 1024, sink, 255, N) == -1                        # sink below 256 words

@@ -109,7 +109,6 @@ def test_unread_slots_do_not_matter(torch_cuda, poison):
     b = synth.make_config(5, small=True)
     ref = Step(b).run().out_u16()
     m = readable_mask(b)
-    import copy
     b2 = copy.copy(b)
     rng = np.random.default_rng(1)
     for name in ("k_cache", "v_cache"):
@@ -236,7 +235,6 @@ def test_loose_upper_bounds(torch_cuda):
     # host bounds larger than the real maxima only size grids and the workspace
     b = synth.make_config(3, small=True)
     # the table must be able to address max_kv_len
-    import copy
     b2 = copy.copy(b)
     need = -(-(b.max_kv_len * 2 + 5) // b.block_size)
     b2.block_tables = np.concatenate(
@@ -311,3 +309,32 @@ def test_kernel_timing_hook(torch_cuda, which):
     st.attention()
     torch.cuda.synchronize()
     assert np.array_equal(st.out_u16(), ref)
+
+
+def test_planned_decode_share_and_prefill_split(torch_cuda):
+    """The planner's two measured rates (about 1.0 us per 32-key prefill step of a workgroup and
+    5.5 GB/ms of decode streaming, both taken on MI355X) decide whether prefill tiles are split
+    along their keys (only when the longest tile would outlast the decode work) and how many
+    compute units the decode kernel takes beside the prefill kernel (its share of the estimated
+    time, at least half). Their effect, read back from the caller's workspace (counts: decode
+    items, prefill items, queue head, split flag, decode workgroups allowed):
+      - the 8B mixed batch: 1.1 GB of decode (~200 us) outlasts its longest tile (96 steps): no
+        split, decode takes most of the CUs;
+      - its prefill chunks alone (no decode work): the tiles are split;
+      - the 70B-shaped batch: prefill (~1 ms spread over the CUs) outweighs decode: no split
+        (the partials would not fit the workspace budget either), decode at the floor of half."""
+    torch = torch_cuda
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    b3 = synth.make_config(3)
+    rng = np.random.default_rng(3)
+    chunks = synth.build_batch("mixed-2048-chunks", 3, rng,
+                               [synth.SeqSpec(1024, 3072)] + [synth.SeqSpec(320, 320)] * 3,
+                               num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16)
+    for name, b, split, lo, hi in (("8B mixed", b3, 0, cus // 2 + 1, cus),
+                                   ("8B chunks alone", chunks, 1, cus + 1, 1 << 30),
+                                   ("70B-shaped", synth.make_config(5), 0, cus // 2, cus // 2)):
+        step = Step(b).run()
+        counts = step.ws[:32].view(torch.int32).cpu().numpy()
+        say(f"[plan] {name}: split {counts[3]}, decode workgroups allowed {counts[4]} ({cus} CUs)")
+        assert counts[3] == split, (name, counts)
+        assert lo <= counts[4] <= hi, (name, counts)
