@@ -5,6 +5,7 @@ Slot mapping and the cache write must be bit-exact; attention outputs must satis
 the five workloads are compared on every output element; the full-size workloads (in the launch
 configuration the benchmark times) on every decode token and a sample of prefill tokens.
 """
+import copy
 import zlib
 
 import numpy as np
