@@ -309,6 +309,10 @@ def pct(xs, q):
 
 FLUSH_BYTES = 1 << 30  # larger than the 256 MB Infinity Cache and the L2s together
 FLUSH_LAUNCHES = 8
+# Untimed launches of the prefill chunks alone before their timed ones (seconds of GPU time):
+# on MI355X the 70B-shaped chunks take 1.23 ms over the first 10 launches after idle and settle
+# at 1.045 ms after about 30 ms of back-to-back launches.
+PREFILL_WARM_S = 0.15
 
 
 def measure(args, config, steps, warmup):
@@ -427,16 +431,29 @@ def measure(args, config, steps, warmup):
         mq, mkv = int(ql.max()), int(b.kv_lens[pre].max())
         wss = cb.alloc_workspace(len(pre), len(rows), b.num_q_heads, b.num_kv_heads, b.head_dim,
                                  b.block_size, mq, mkv, 0, device=dev)
-        iso = []
-        for i in range(warmup + steps):
+        def timed_alone():
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             cb.cb_time_next_kernel(kernel, e0, e1, stream=stream)
             cb.cb_paged_attention(qs, cus, kvs, bts, kc, vc, outs, b.scale, mq, mkv, wss,
                                   stream=stream)
-            if i >= warmup:
-                iso.append((e0, e1))
+            return e0, e1
+
+        # The GPU's clocks ramp up over the first tens of milliseconds of sustained load: the
+        # first launches after the host-side set-up are timed on their own ("cold"), then the
+        # same launches run untimed for PREFILL_WARM_S before the timed ones, so that the
+        # roofline is taken in the steady state that back-to-back serving steps run in.
+        cold = [timed_alone() for _ in range(max(1, warmup))]
+        torch.cuda.synchronize()
+        cold_ms = [e0.elapsed_time(e1) for e0, e1 in cold]
+        n_warm = min(20000, int(PREFILL_WARM_S * 1e3 / max(min(cold_ms), 1e-3)))
+        for _ in range(n_warm):
+            cb.cb_paged_attention(qs, cus, kvs, bts, kc, vc, outs, b.scale, mq, mkv, wss,
+                                  stream=stream)
+        iso = [timed_alone() for _ in range(steps)]
         torch.cuda.synchronize()
         iso_ms = [e0.elapsed_time(e1) for e0, e1 in iso]
+        r["kernel_ms_cold"] = pct(cold_ms, 0.5)
+        r["warm_launches"] = n_warm
         r["step_kernel_ms"] = r["kernel_ms"]
         r["kernel_ms"] = sum(iso_ms) / len(iso_ms)
         r["kernel_ms_median"] = pct(iso_ms, 0.5)
@@ -449,7 +466,9 @@ def measure(args, config, steps, warmup):
 
         r["kernel_ms_flushed"] = flushed(alone)
         log(f"[bench] {b.name} prefill chunks alone ({len(pre)} sequences, {len(rows)} tokens): "
-            f"prefill kernel avg {r['kernel_ms']:.4f} ms (min {min(iso_ms):.4f}, max {max(iso_ms):.4f})")
+            f"prefill kernel avg {r['kernel_ms']:.4f} ms (min {min(iso_ms):.4f}, max {max(iso_ms):.4f}) "
+            f"after {n_warm} untimed launches; the first {len(cold_ms)} after set-up: median "
+            f"{r['kernel_ms_cold']:.4f} ms")
     log(f"[bench] {b.name} {'decode' if kernel == cb.CB_KERNEL_DECODE else 'prefill'} kernel "
         f"p10 / median / p90 {r['kernel_ms_p10']:.4f} / {r['kernel_ms_median']:.4f} / "
         f"{r['kernel_ms_p90']:.4f} ms; after reading {FLUSH_BYTES >> 20} MiB to flush the caches (median of "
@@ -477,7 +496,11 @@ def roofline_of(r, stream_gbs=None):
             "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_from_profile(b.name), "kernel": "prefill_kernel",
             "kernel_ms": round(r["kernel_ms"], 5), "flops_per_launch": w["prefill_flops"],
-            "timed_on": "the batch's prefill chunks alone",
+            "timed_on": "the batch's prefill chunks alone, in steady state after "
+                        f"{r['warm_launches']} untimed launches",
+            # the first launches after the set-up, before the clocks have ramped up
+            "kernel_ms_cold": round(r["kernel_ms_cold"], 5),
+            "frac_cold": round(w["prefill_flops"] / (r["kernel_ms_cold"] / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "kernel_ms_in_step": round(r["step_kernel_ms"], 5),
             # the same kernel inside the whole step, where the decode kernel shares the GPU
             "frac_in_step": round(in_step / BF16_PEAK_TFLOPS, 4),
