@@ -834,29 +834,6 @@ __device__ inline void rescale_lazy32(float m_lane, float& m, float& l, f32x16 (
   }
 }
 
-// The prefill kernel's scores come out of the MFMAs already scaled and shifted by the row's
-// reference max (acc = c s - m, Q pre-scaled by c, the score MFMAs started from -m), so its lazy
-// rescale works on the chunk maximum relative to m.
-// On a rescale the reference moves up by delta >= 0; the accumulated output and sum shrink by
-// 2^-delta, the pending scores and the MFMA's initial value (-m) move down by delta.
-template <int NDT>
-__device__ inline void rescale_rel32(float mx, float& m, float& l, f32x16 (&o)[NDT], f32x16& acc,
-                                     f32x16& nm) {
-  if (__builtin_amdgcn_ballot_w64(mx > kRescaleSlack) != 0) {  // wave-uniform
-    const float delta = fmaxf(0.f, pair_max(mx));
-    const float alpha = __builtin_amdgcn_exp2f(-delta);
-    l *= alpha;
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) o[t] *= alpha;
-    m += delta;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acc[i] -= delta;
-      nm[i] = -m;
-    }
-  }
-}
-
 // P^T operands of the chunk's two 16-key halves: slot e of half ks is key
 // k0 + 16ks + 8(e / 4) + 4h + e % 4, i.e. accumulator 8ks + e.
 // Adds a pair of bf16 probabilities to a row sum (one dot-product instruction against (1, 1)).
@@ -887,9 +864,10 @@ __device__ inline void chunk_exp32(const f32x16& acc, float c, float m, float& l
 // VALU, the S^T = K Q^T products of tile t + 1 run on the matrix cores, and the P V products of
 // tile t run beside the row maxima of tile t + 1. A step starts by storing tile t + 2 (loaded
 // into registers two steps earlier) to LDS and loading tile t + 4 into the registers it frees.
-// Q is scaled by c = scale * log2(e) when it is loaded and each tile's score MFMAs start from
-// -m (the row's reference max), so the scores arrive as the exponents themselves: the
-// exponentials take them with no multiply-add, 16 fewer vector instructions per step.
+// The scale stays in fp32, applied to each score beside its exponential: scaling Q before the
+// MFMAs would round c q to bf16, a relative error of 2^-9 on every product q_i k_i, which for
+// keys of large magnitude moves the logits by hundredths of a log2 unit (measured: outputs off
+// by up to 0.06 on keys growing to 11x, against 0.015 with the scale in fp32).
 
 constexpr int kPrefillKeys = 32;  // keys per LDS tile (one barrier per tile)
 constexpr int kPrefillBufs = 3;   // LDS tiles: being computed, ready, being filled
@@ -967,13 +945,7 @@ void prefill_kernel(
     if (qi < tok_end) {
       const __bf16* p = q + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + 8 * h;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        // scaled by c = scale * log2(e) once here (rounded to bf16), so that the score MFMAs
-        // give log2-domain logits and the exponentials need no multiply
-        const bf16x8 raw = *reinterpret_cast<const bf16x8*>(p + 16 * kk);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)((float)raw[e] * scale_log2);
-      }
+      for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(p + 16 * kk);
       last_key = L - qn + qi;
     } else {
 #pragma unroll
@@ -1133,16 +1105,10 @@ void prefill_kernel(
   f32x16 accA, accB;
   qk(0, accA);
   {
-    const float mc = n_open > 0 ? chunk_max32<false>(accA, kb, kend, last_key, 1.f, h)
-                                : chunk_max32<true>(accA, kb, kend, last_key, 1.f, h);
+    const float mc = n_open > 0 ? chunk_max32<false>(accA, kb, kend, last_key, scale_log2, h)
+                                : chunk_max32<true>(accA, kb, kend, last_key, scale_log2, h);
     rescale_lazy32<NDT>(mc, m, l, o);
   }
-  // tile 0's scores relative to its reference max, like those of every later tile
-#pragma unroll
-  for (int i = 0; i < 16; ++i) accA[i] -= m;
-  f32x16 nm;  // -m in every slot: the initial value of each tile's score MFMAs
-#pragma unroll
-  for (int i = 0; i < 16; ++i) nm[i] = -m;
 
   // step st < nsteps - 1: tile st is in LDS buffer cur with its scores (masked) in accA / accB
   // by the parity P = st % 2 and its reference max settled; tile st + 1 is in buffer nxt; buffer
@@ -1180,13 +1146,13 @@ void prefill_kernel(
     const int r = lane & 15;
     const __bf16* vb = &sm.v[cur][4 * h + (r >> 2)][16 * ((lane >> 4) & 1) + 4 * (r & 3)];
     float rs = 0.f;
-    acc_n = nm;
+    acc_n = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int e = 0; e < EPP; ++e) {
         const int i = kk * EPP + e;
-        pb[i / 8][i % 8] = (__bf16)__builtin_amdgcn_exp2f(acc[i]);
+        pb[i / 8][i % 8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m));
         if (e & 1) rs = add_pair(rs, pb[i / 8][i % 8 - 1], pb[i / 8][i % 8]);
       }
 #pragma unroll
@@ -1227,7 +1193,8 @@ void prefill_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    rescale_rel32<NDT>(mx, m, l, o, acc_n, nm);
+    const float mc = mx * scale_log2;
+    rescale_lazy32<NDT>(mc, m, l, o);
     const int t = cur;
     cur = nxt;
     nxt = fil;
@@ -1255,7 +1222,7 @@ void prefill_kernel(
   {
     const f32x16 acc_last = (nsteps - 1) & 1 ? accB : accA;
     bf16x8 pb[2];
-    chunk_exp32(acc_last, 1.f, 0.f, l, pb);
+    chunk_exp32(acc_last, scale_log2, m, l, pb);
     pv(cur, pb);
   }
 

@@ -15,7 +15,7 @@ import oracle
 import synth
 from gpu_helpers import (Step, assert_close, dev_bf16, dev_i32, host_u16, oracle_step,
                          readable_mask, say)
-from pins import permute_blocks, tiny_batch
+from pins import permute_blocks, table_slots, tiny_batch, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +121,80 @@ def test_unread_slots_do_not_matter(torch_cuda, poison):
     # the new tokens' slots are unread before the write as well
     got = Step(b2).run().out_u16()
     assert np.array_equal(got, ref)
+
+
+def _growing_keys(batch, rate):
+    """The batch with every key row (cached and new) of every sequence scaled by 2^(p / rate) at
+    position p: the scores grow along each sequence, so the online softmax's running reference
+    maximum has to move again and again."""
+    b = copy.copy(batch)
+    Hkv, D, bs = b.num_kv_heads, b.head_dim, b.block_size
+    kc = b.k_cache.copy().reshape(-1, Hkv, D)
+    k = b.k.copy()
+    cu = b.cu_seqlens_q
+    for s in range(b.num_seqs):
+        L, q0, q1 = int(b.kv_lens[s]), int(cu[s]), int(cu[s + 1])
+        f = 2.0 ** (np.arange(L) / rate)
+        slots = table_slots(b.block_tables[s], L, bs)
+        for p in range(L - (q1 - q0)):
+            kc[slots[p]] = synth.bf16_from_f32((widen(kc[slots[p]]) * f[p]).astype(np.float32))
+        k[q0:q1] = synth.bf16_from_f32((widen(k[q0:q1]) * f[L - (q1 - q0):, None, None]).astype(np.float32))
+    b.k_cache = kc.reshape(b.k_cache.shape)
+    b.k = k
+    return b
+
+
+def _reference_moves(b):
+    """Most moves of a lazily kept reference maximum over one query row and head of the batch
+    (float64 scores in log2 units, 32-key tiles from key 0): the reference starts at the first
+    tile's maximum and moves to a tile's maximum when that exceeds it by more than 8."""
+    Hq, Hkv, D, bs = b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size
+    G = Hq // Hkv
+    kc = b.k_cache.reshape(-1, Hkv, D)
+    c = b.scale / np.log(2.0)
+    most = 0
+    for s in range(b.num_seqs):
+        L, q0, q1 = int(b.kv_lens[s]), int(b.cu_seqlens_q[s]), int(b.cu_seqlens_q[s + 1])
+        qn = q1 - q0
+        slots = table_slots(b.block_tables[s], L, bs)
+        keys = np.concatenate([widen(kc[slots[: L - qn]]), widen(b.k[q0:q1])])  # [L, Hkv, D]
+        q = widen(b.q[q0:q1])  # [qn, Hq, D]
+        for hh in range(Hq):
+            sc = c * (q[:, hh] @ keys[:, hh // G].T)  # [qn, L]
+            for i in range(qn):
+                row = sc[i, : L - qn + i + 1]
+                m, moves = row[:32].max(), 0
+                for t in range(32, len(row), 32):
+                    if row[t:t + 32].max() > m + 8:
+                        m, moves = row[t:t + 32].max(), moves + 1
+                most = max(most, moves)
+    return most
+
+
+RESCALE = {
+    # (specs, Hq, Hkv, D, bs, kv_split_tokens, positions per doubling of the key scale): the
+    # scale ends near 2^3.5, so scaled scores reach a few tens of log2 units
+    "decode": ([synth.SeqSpec(1, 700), synth.SeqSpec(1, 333), synth.SeqSpec(2, 520)], 32, 8, 128, 16, 0, 200.0),
+    "decode-partitions": ([synth.SeqSpec(1, 700), synth.SeqSpec(1, 333), synth.SeqSpec(2, 520)], 32, 8, 128, 16, 64, 200.0),
+    "prefill-split": ([synth.SeqSpec(64, 2000), synth.SeqSpec(130, 130)], 32, 8, 128, 16, 0, 570.0),
+    "mixed-d64": ([synth.SeqSpec(1, 600), synth.SeqSpec(40, 700)], 16, 2, 64, 16, 0, 200.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RESCALE))
+def test_growing_scores_move_the_reference_max(torch_cuda, name):
+    """Scores that keep growing along the sequence: the lazy rescale of both kernels (and the
+    merge of partitions with different maxima) runs many times, and every output element still
+    matches the oracle. The batch is checked first to make the path certain: a reference max kept
+    the kernels' way (moved when a tile exceeds it by more than 8) moves several times in a row."""
+    specs, Hq, Hkv, D, bs, split, rate = RESCALE[name]
+    b = _growing_keys(tiny_batch(list(specs), Hq, Hkv, D, bs, seed=zlib.crc32(name.encode()) % 1000), rate)
+    moves = _reference_moves(b)
+    say(f"[rescale] {name}: a lazily kept reference max moves up to {moves} times in one row")
+    assert moves >= 3
+    step = Step(b, kv_split_tokens=split).run()
+    rep = check_full(b, step)
+    say(f"[rescale] {name}: {rep}")
 
 
 def test_split_kv_reduce_entry(torch_cuda):
