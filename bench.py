@@ -14,7 +14,10 @@ prefill-chunk tokens), "long_context_decode" (16 sequences of 32K-128K keys, spl
 and the log-sum-exp merge) and "mixed_batch_70b" (64 q-heads / 8 KV heads, block 32, 8192 tokens:
 128 decodes + chunked prefills, a 2048-token prefix shared by a quarter of the sequences).
 "stream_read" is the measured streaming-read rate of this GPU (cb_stream_read over 2 GiB), which
-the decode rooflines are also reported against.
+the decode rooflines are also reported against. The headline step runs the given W warm-up and
+K timed steps; the further workloads, and the prefill roofline's chunks-alone launches, are timed
+after 0.15 s of untimed launches, in the steady state of the GPU's clocks under sustained load
+(the first launches after idle run up to 18% slower), with the first launches reported beside.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
 
@@ -313,11 +316,17 @@ FLUSH_LAUNCHES = 8
 # on MI355X the 70B-shaped chunks take 1.23 ms over the first 10 launches after idle and settle
 # at 1.045 ms after about 30 ms of back-to-back launches.
 PREFILL_WARM_S = 0.15
+# Untimed steps (seconds of wall time) before the timed steps of the further workloads of the
+# default run: the 70B-shaped mixed step takes 1.76-1.82 ms over its first steps and 1.64 ms in
+# steady state.
+SUB_WARM_S = 0.15
 
 
-def measure(args, config, steps, warmup):
+def measure(args, config, steps, warmup, warm_s=0.0):
     """Generate workload `config`, run warmup + timed steps; returns the batch, its work and the
-    timings (step wall time, dominant kernel times from the library's events)."""
+    timings (step wall time, dominant kernel times from the library's events). warm_s > 0: after
+    the warmup steps, further untimed steps until that much wall time has passed, so that the
+    timed steps run at the clocks of sustained load."""
     import numpy as np
     import torch
 
@@ -370,6 +379,14 @@ def measure(args, config, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    warm_steps = 0
+    if warm_s > 0:
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < warm_s:
+            for _ in range(8):
+                step()
+            warm_steps += 8
+            torch.cuda.synchronize()
     # the K timed steps, with nothing but the step enqueued
     t_start = time.perf_counter()
     for i in range(steps):
@@ -389,7 +406,7 @@ def measure(args, config, steps, warmup):
     kern_ms = [e[2].elapsed_time(e[3]) for e in events]
     r = {
         "batch": b, "work": w, "split": split, "kernel": kernel,
-        "ms_per_step": elapsed / steps * 1e3,
+        "ms_per_step": elapsed / steps * 1e3, "warm_steps": warm_steps,
         "attn_ms": sum(attn_ms) / len(attn_ms),
         "kernel_ms": sum(kern_ms) / len(kern_ms),
         "kernel_ms_median": pct(kern_ms, 0.5),
@@ -511,7 +528,8 @@ def roofline_of(r, stream_gbs=None):
 def sub_result(args, config, stream_gbs, cpu_budget_s):
     """One further workload of the default run, as a sub-object of the JSON line: step time, the
     workload's metric, its dominant kernel's roofline and the oracle's rate on a sample."""
-    m = measure(args, config, max(5, args.steps // 2), max(2, args.warmup // 2))
+    # the further workloads are timed in steady state (the headline step keeps the given W and K)
+    m = measure(args, config, max(5, args.steps // 2), max(2, args.warmup // 2), warm_s=SUB_WARM_S)
     b, w = m["batch"], m["work"]
     step_s = m["ms_per_step"] / 1e3
     mixed = config not in DECODE_CONFIGS
@@ -519,6 +537,7 @@ def sub_result(args, config, stream_gbs, cpu_budget_s):
         "workload": b.name, "num_tokens": b.num_tokens, "num_seqs": b.num_seqs,
         "kv_tokens": int(b.kv_lens.sum()), "kv_split_tokens": int(m["split"]), "seed": b.seed,
         "ms_per_step": round(m["ms_per_step"], 5),
+        "untimed_steps_before": int(m["warm_steps"]) + max(2, args.warmup // 2),
         "tokens_per_s": round(w["T"] / step_s, 1),
         "step_gbs": round(w["step_bytes"] / step_s / 1e9, 3),
         "hbm_frac": round(w["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
