@@ -59,9 +59,10 @@ constexpr int kPrefillRows = kPrefillWaves * 32;   // query rows (token x head) 
 constexpr int kPrefillWavesPerSimd = 2;
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup beside prefill work (4 otherwise)
 
-struct Work {
-  int32_t seq;
-  int32_t idx;  // query tile (prefill)
+// A prefill item carries what its workgroup needs to start (one 32-byte scalar load): sequence,
+// query tile * kMaxPreSplits + key part, the sequence's first packed row, query rows, KV length.
+struct alignas(16) Work {
+  int32_t seq, idx, q0, qn, L, pad0, pad1, pad2;
 };
 // A decode item carries what its wave needs to start (one 32-byte scalar load): sequence, KV
 // partition, first query row, query rows, KV length.
@@ -393,9 +394,11 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
     seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull,
               rem, np);
     int nit = np, qn = 0, L = 0;
-    if (np > 0 && emax > 1) {  // few tiles (splitting is on): count the parts
+    if (np > 0) {
       qn = cu[s + 1] - cu[s];
       L = kv_lens[s];
+    }
+    if (np > 0 && emax > 1) {  // few tiles (splitting is on): count the parts
       nit = 0;
       for (int tl = 0; tl < np; ++tl) {
         int ns, chunk;
@@ -410,11 +413,11 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
         int ns, chunk;
         prefill_split(L - qn + min(qn, (tl + 1) * bq), emax, ns, chunk);
         for (int part = 0; part < ns; ++part, ++ep)
-          if (ep < pre_cap) pre[ep] = Work{s, tl * kMaxPreSplits + part};
+          if (ep < pre_cap) pre[ep] = Work{s, tl * kMaxPreSplits + part, cu[s], qn, L, 0, 0, 0};
       }
     } else {
       for (int k = 0; k < np; ++k)
-        if (ep + k < pre_cap) pre[ep + k] = Work{s, (np - 1 - k) * kMaxPreSplits};
+        if (ep + k < pre_cap) pre[ep + k] = Work{s, (np - 1 - k) * kMaxPreSplits, cu[s], qn, L, 0, 0, 0};
     }
     __syncthreads();
     if (tid == 1023) base[1] += incp;
@@ -914,13 +917,16 @@ void prefill_kernel(
 
   const int item = blockIdx.x / Hkv;
   const int kvh = blockIdx.x - item * Hkv;
-  if (item >= counts[1]) return;
+  // the item count and the item's record in one round trip (items has room for every workgroup
+  // of the grid); workgroups past the count leave
+  const int n_items = counts[1];
   const Work w = items[item];
+  if (item >= n_items) return;
   const int s = w.seq, qt = w.idx / kMaxPreSplits, part = w.idx - qt * kMaxPreSplits;
   const int G = Hq / Hkv;
-  const int q0 = cu[s];
-  const int qn = cu[s + 1] - q0;
-  const int L = kv_lens[s];
+  const int q0 = w.q0;
+  const int qn = w.qn;
+  const int L = w.L;
   const int tok0 = qt * bq;
   const int tok_end = min(qn, tok0 + bq);
   // keys [0, kend_tile) are visible to some row of the tile; this part covers [kb, kend)
