@@ -552,57 +552,67 @@ inline BlockDiv block_div(int32_t bs) {
 // ---------------------------------------------------------------------------------------------
 // Decode / split-KV kernel. Persistent waves, each working alone: a wave takes one
 // (KV partition, KV head) item at a time from a queue and streams its keys 32 at a time. K/V
-// fragments go straight from HBM into registers with 16-byte loads, one step ahead of the
-// MFMAs; the partition's block ids sit one per lane and are broadcast with readlane. No LDS and
-// no barriers, so a wave's start-up and write-out overlap with the other waves' streaming.
+// fragments go straight from HBM into registers with 16-byte loads, two steps ahead of the
+// MFMAs (each register set is refilled as soon as its MFMAs have read it); the partition's block
+// ids sit one per lane and are broadcast with readlane. No LDS and no barriers, so a wave's
+// start-up and write-out overlap with the other waves' streaming.
 
-// K/V are streamed once per call: non-temporal loads keep them from displacing reusable lines.
-__device__ inline u32x4 ld_stream16(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// K/V rows of one 16-key group are read through a buffer resource whose record count ends at the
+// range end: loads of keys at or past it return zeros and touch no memory, so a step's loads need
+// no branch and V rows past the end arrive zeroed (their slots may hold anything, NaN included).
+// The address and count are wave-uniform; readfirstlane puts them in scalar registers, where
+// the descriptor must be (from vector registers the compiler would loop over the lanes).
+__device__ inline __amdgpu_buffer_rsrc_t group_rsrc(const __bf16* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>((uint64_t)hi << 32 | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(nbytes),
+                                           0x00020000);
 }
-__device__ inline u32x2 ld_stream8(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-}
+constexpr int kLoadStream = 2;  // buffer-load cache policy: non-temporal (K/V are read once)
 
-// Issue the loads of one 32-key step into registers. K: lane (n, g) reads dims [32 kk + 8 g, +8)
-// of key 16 j + n, so one instruction covers 64 contiguous bytes of each of 16 key rows and the
-// next one completes each 128-byte line: ordinary cached loads. V: lane (c = n, g) reads chunk n
-// of key 16 (e / 4) + 4 g + e % 4, whole 256-byte rows per instruction: streaming loads.
-// base_j (wave-uniform) is the cache address of the first key of group j at this KV head; a
-// lane adds its fixed byte offsets: koff for K (key n, dims 8 g) and voff[i] for V (key 4 g + i,
-// chunk n).
+// The loads of one 32-key step into registers. K: lane (n, g) reads dims [32 kk + 8 g, +8) of key
+// 16 j + n, so one instruction covers 64 contiguous bytes of each of 16 key rows and the next one
+// completes each 128-byte line: ordinary cached loads. V: lane (c = n, g) reads chunk n of key
+// 16 (e / 4) + 4 g + e % 4, whole 256-byte rows per instruction: streaming loads. rk[j], rv[j]
+// cover group j from its first key's row at this KV head; a lane adds its fixed byte offsets:
+// koff for K (key n, dims 8 g) and voff[i] for V (key 4 g + i, chunk n).
 template <int D>
-__device__ inline void load_step(KVFrag<D>& f, const __bf16* __restrict__ kc,
-                                 const __bf16* __restrict__ vc, int64_t base0, int64_t base1,
-                                 uint32_t koff, const uint32_t (&voff)[4]) {
+__device__ inline void load_k(KVFrag<D>& f, const __amdgpu_buffer_rsrc_t (&rk)[2], uint32_t koff) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const char* p = reinterpret_cast<const char*>(kc + (j ? base1 : base0)) + koff;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int kk = 0; kk < KVFrag<D>::KSTEPS; ++kk)
-      f.k[j][kk] = *reinterpret_cast<const bf16x8*>(p + 64 * kk);
-  }
+      f.k[j][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk[j], koff + 64 * kk, 0, 0));
+}
+template <int D>
+__device__ inline void load_v(KVFrag<D>& f, const __amdgpu_buffer_rsrc_t (&rv)[2],
+                              const uint32_t (&voff)[4]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const char* p = reinterpret_cast<const char*>(vc + ((e >> 2) ? base1 : base0)) + voff[e & 3];
     if constexpr (D == 128) {
-      const u32x4 x = ld_stream16(p);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv[e >> 2], voff[e & 3], 0, kLoadStream);
       f.v[e][0] = x.x; f.v[e][1] = x.y; f.v[e][2] = x.z; f.v[e][3] = x.w;
     } else {
-      const u32x2 x = ld_stream8(p);
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rv[e >> 2], voff[e & 3], 0, kLoadStream);
       f.v[e][0] = x.x; f.v[e][1] = x.y;
     }
   }
 }
 
-// One 32-key step: S^T = K Q^T, online softmax, O^T += V^T P^T. Consumes the fragment: V words
-// of keys past the range end are zeroed in place (their slots may hold anything, NaN included).
+// One 32-key step: S^T = K Q^T, online softmax, O^T += V^T P^T. Two steps of loads stay in
+// flight: the K registers take the loads of the step after next as soon as the score MFMAs have
+// read them, the V registers as soon as the output MFMAs have (rk, rv: that step's groups).
 // first_last_key: the smallest last visible key over the rows written out (wave-uniform); steps
 // wholly below it and inside the range need no mask.
 template <int D>
 __device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], int k0, int kend,
                                     int last_key, int first_last_key, float scale_log2, int g,
-                                    float& m, float& l, f32x4 (&o)[D / 16]) {
+                                    float& m, float& l, f32x4 (&o)[D / 16],
+                                    const __amdgpu_buffer_rsrc_t (&rk)[2],
+                                    const __amdgpu_buffer_rsrc_t (&rv)[2], uint32_t koff,
+                                    const uint32_t (&voff)[4]) {
   constexpr int KSTEPS = D / 32;
   f32x4 acc[2];
 #pragma unroll
@@ -611,27 +621,27 @@ __device__ inline void compute_step(KVFrag<D>& f, const bf16x8 (&qf)[D / 32], in
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) acc[j] = mfma16x16x32(f.k[j][kk], qf[kk], acc[j]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  load_k<D>(f, rk, koff);
   const bool interior = k0 + 32 <= kend && k0 + 31 <= first_last_key;
   const bf16x8 pb =
       interior ? softmax_step<D / 16, false>(acc, k0, kend, last_key, scale_log2, g, m, l, o)
                : softmax_step<D / 16, true>(acc, k0, kend, last_key, scale_log2, g, m, l, o);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int key = k0 + 16 * (e >> 2) + 4 * g + (e & 3);
-    if (key >= kend) {
-#pragma unroll
-      for (int w = 0; w < D / 32; ++w) f.v[e][w] = 0u;
-    }
-  }
-#pragma unroll
   for (int jt = 0; jt < D / 16; ++jt) o[jt] = mfma16x16x32(vt_operand<D>(f.v, jt), pb, o[jt]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v<D>(f, rv, voff);
 }
 
 // Block id of key k (uniform) from the partition's table entries held one per lane in three
-// registers (entry jb0 + 64 r + lane in bt[r]).
+// registers (entry jb0 + 64 r + lane in bt[r]). Each register is read with its own readlane and
+// the result picked by a scalar select: indexing the array by jj would put it in memory.
 __device__ inline int block_of(const int (&bt)[3], int jj) {
-  const int v = jj < 64 ? bt[0] : (jj < 128 ? bt[1] : bt[2]);
-  return __builtin_amdgcn_readlane(v, jj & 63);
+  const int l = jj & 63;
+  const int b0 = __builtin_amdgcn_readlane(bt[0], l);
+  const int b1 = __builtin_amdgcn_readlane(bt[1], l);
+  const int b2 = __builtin_amdgcn_readlane(bt[2], l);
+  return jj < 64 ? b0 : (jj < 128 ? b1 : b2);
 }
 
 template <int D>
@@ -654,7 +664,7 @@ void decode_kernel(
   const int bs = bdiv.bs;
   // beside prefill work, only the first counts[4] workgroups (one per compute unit) take items
   if ((int)blockIdx.x >= counts[4]) return;
-  // per-lane byte offsets from a group's first cache row (see load_step)
+  // per-lane byte offsets from a group's first cache row (see load_k, load_v)
   const uint32_t row_bytes = (uint32_t)Hkv * D * (uint32_t)sizeof(__bf16);
   const uint32_t koff = n * row_bytes + 16 * g;
   uint32_t voff[4];
@@ -688,27 +698,26 @@ void decode_kernel(
     const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
     const int jb0 = bdiv.div(kb);
     const int nbt = bdiv.div(ke + bs - 1) - jb0;
+    // unconditional loads (indices clamped to the partition's last entry): no branch, no wait
+    // between them
     int bt[3];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-      const int j = 64 * r + lane;
-      bt[r] = j < nbt ? bt_row[jb0 + j] : 0;
-    }
+    for (int r = 0; r < 3; ++r) bt[r] = bt_row[jb0 + min(64 * r + lane, nbt - 1)];
 
     // Q^T operand: lane column n is query row n = (token n / G, head n % G)
+    // (loaded by every lane, from row 0 for the unused columns, then zeroed there: a branch
+    // around the loads would make the first K/V loads wait for them)
     bf16x8 qf[KSTEPS];
-    int last_key = -1;
-    if (n < rows) {
-      const int qi = n / G, hh = n - (n / G) * G;
+    const bool qrow = n < rows;
+    const int qi = qrow ? n / G : 0, hh = qrow ? n - (n / G) * G : 0;
+    const int last_key = qrow ? L - qn + qi : -1;
+    {
       const __bf16* pq = q + ((int64_t)(q0 + qi) * Hq + kvh * G + hh) * D + g * 8;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(pq + 32 * kk);
-      last_key = L - qn + qi;
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-        for (int x = 0; x < 8; ++x) qf[kk][x] = (__bf16)0.f;
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(pq + 32 * kk);
+        qf[kk] = __builtin_bit_cast(bf16x8, qrow ? x : u32x4{0u, 0u, 0u, 0u});
+      }
     }
 
     float m = kMaxFloor, l = 0.f;
@@ -717,29 +726,42 @@ void decode_kernel(
     for (int t = 0; t < NO; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int first_last_key = L - qn;  // last visible key of the item's first token
 
-    // element offset of the first key of the 16-key group starting at key k, at this KV head;
-    // groups wholly past the range end alias the first group (loaded, then masked)
-    auto group_row = [&](int k) -> int64_t {
-      const int kk = k < ke ? k : kb;
-      const int bi = bdiv.div(kk);
-      const int blk = block_of(bt, bi - jb0);
-      return ((int64_t)(uint32_t)(blk * bs + (kk - bi * bs)) * Hkv + kvh) * D;
+    // buffer resources of the two 16-key groups of the step starting at key k: the group's first
+    // row at this KV head, records up to the range end (none for groups wholly past it)
+    auto step_rsrc = [&](int k, __amdgpu_buffer_rsrc_t (&rk)[2], __amdgpu_buffer_rsrc_t (&rv)[2]) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int kg = k + 16 * j;
+        const int kk = kg < ke ? kg : kb;
+        const int bi = bdiv.div(kk);
+        const int blk = block_of(bt, bi - jb0);
+        const int64_t row = ((int64_t)(uint32_t)(blk * bs + (kk - bi * bs)) * Hkv + kvh) * D;
+        const uint32_t nb = (uint32_t)min(max(ke - kg, 0), 16) * row_bytes;
+        rk[j] = group_rsrc(k_cache + row, nb);
+        rv[j] = group_rsrc(v_cache + row, nb);
+      }
     };
 
     int k0 = kb;
     KVFrag<D> fa, fb;
-    load_step<D>(fa, k_cache, v_cache, group_row(k0), group_row(k0 + 16), koff, voff);
-    while (true) {
-      const int k1 = k0 + 32;
-      if (k1 < ke) load_step<D>(fb, k_cache, v_cache, group_row(k1), group_row(k1 + 16), koff, voff);
-      compute_step<D>(fa, qf, k0, ke, last_key, first_last_key, scale_log2, g, m, l, o);
-      if (k1 >= ke) break;
-      const int k2 = k1 + 32;
-      if (k2 < ke) load_step<D>(fa, k_cache, v_cache, group_row(k2), group_row(k2 + 16), koff, voff);
-      compute_step<D>(fb, qf, k1, ke, last_key, first_last_key, scale_log2, g, m, l, o);
-      if (k2 >= ke) break;
-      k0 = k2;
-    }
+    __amdgpu_buffer_rsrc_t rk[2], rv[2];
+    step_rsrc(k0, rk, rv);
+    load_k<D>(fa, rk, koff);
+    load_v<D>(fa, rv, voff);
+    step_rsrc(k0 + 32, rk, rv);
+    load_k<D>(fb, rk, koff);
+    load_v<D>(fb, rv, voff);
+    // Steps go in pairs with one exit test per pair: a pair's second step past the range end is
+    // fully masked (its loads read nothing and its probabilities are 0). An exit between the two
+    // steps would let the compiler sink the first step's V loads past it, and the merged paths
+    // make it wait for all loads at the top of the loop.
+    do {
+      step_rsrc(k0 + 64, rk, rv);
+      compute_step<D>(fa, qf, k0, ke, last_key, first_last_key, scale_log2, g, m, l, o, rk, rv, koff, voff);
+      step_rsrc(k0 + 96, rk, rv);
+      compute_step<D>(fb, qf, k0 + 32, ke, last_key, first_last_key, scale_log2, g, m, l, o, rk, rv, koff, voff);
+      k0 += 64;
+    } while (k0 < ke);
 
     l = group_sum(l);  // the row's sum (all lanes take part)
     // lane (n, g) holds row n, dims (4g + i) * NO + jt
