@@ -1520,8 +1520,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kNoAllocScratchBytes = CB_NOALLOC_SCRATCH_BYTES;
 constexpr size_t kNoAllocPrefillBudget = kNoAllocScratchBytes / 4;
 
-int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t requested,
-                     bool prefill) {
+int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t requested) {
   if (requested > 0) {
     int32_t p = (int32_t)cb::ceil_div(requested, 32) * 32;
     return p > kMaxSplitTokens ? kMaxSplitTokens : p;
@@ -1531,12 +1530,11 @@ int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t 
   // uniformly drawn lengths. Measured on decode-only batches (several draws each), this picked
   // the fastest size or one within 5% of it: 1536 at 256 sequences of up to 4K keys (a
   // power-of-two rule's 1024 was 4-8% slower), 768 at 64 of up to 8K, 2048 at 16 of up to 128K,
-  // and 2048 against 1536's 5% better at 128 of up to 16K (the 2048 cap). With prefill-type
-  // sequences in the batch the decode kernel runs beside the prefill kernel on part of the CUs,
-  // with fewer waves, and larger partitions pay: 2/3 of the items (in the 8B-shaped mixed
-  // 2048-token batch, 1280 against 768 took the call from 0.320-0.326 to 0.298-0.312 ms).
+  // and 2048 against 1536's 5% better at 128 of up to 16K (the 2048 cap). The same rule holds
+  // beside prefill work: over four draws of the 8B-shaped mixed 2048-token batch its 768 took
+  // the fused step 0.6-3% less time than partitions 1.5 times larger.
   const int64_t keys = (int64_t)max_kv_len * num_seqs * Hkv;
-  const int64_t p = (keys / (prefill ? 3641 : 5461) + 128) / 256 * 256;
+  const int64_t p = (keys / 5461 + 128) / 256 * 256;
   return (int32_t)std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(256, p));
 }
 
@@ -1546,7 +1544,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, in
   Plan p;
   p.G = Hq / Hkv;
   const int32_t dec_q = 16 / p.G;  // longest decode-type chunk
-  p.P = choose_split(num_seqs, Hkv, max_kv_len, kv_split_tokens, max_q_len > dec_q);
+  p.P = choose_split(num_seqs, Hkv, max_kv_len, kv_split_tokens);
   p.max_splits = (int32_t)cb::ceil_div(max_kv_len, p.P);
   p.qmaxd = max_q_len < dec_q ? max_q_len : dec_q;
   p.bq = kPrefillRows / p.G;
@@ -1653,8 +1651,9 @@ Aux aux_stream(hipStream_t st, AuxStream* out) {
 extern "C" int32_t cb_paged_attention_split_tokens(int32_t num_seqs, int32_t num_q_heads,
                                                    int32_t num_kv_heads, int32_t max_q_len,
                                                    int32_t max_kv_len, int32_t kv_split_tokens) {
-  const int32_t G = num_kv_heads > 0 && num_q_heads >= num_kv_heads ? num_q_heads / num_kv_heads : 1;
-  return choose_split(num_seqs, num_kv_heads, max_kv_len, kv_split_tokens, max_q_len > 16 / G);
+  (void)num_q_heads;
+  (void)max_q_len;
+  return choose_split(num_seqs, num_kv_heads, max_kv_len, kv_split_tokens);
 }
 
 extern "C" size_t cb_paged_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,

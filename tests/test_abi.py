@@ -130,8 +130,8 @@ def test_workspace_size_and_split_choice():
     for S, L in ((1, 100000), (300, 3000), (2048, 512), (7, 65536)):
         p = cb.cb_paged_attention_split_tokens(S, 32, 8, 1, L)
         assert p % 256 == 0 and 256 <= p <= 2048
-    # with prefill-type sequences possible (q > 16 / G), 1.5 times the decode-only size
-    assert cb.cb_paged_attention_split_tokens(68, 32, 8, 1024, 8192) == 1280
+    # the same rule with prefill-type sequences possible (q > 16 / G)
+    assert cb.cb_paged_attention_split_tokens(68, 32, 8, 1024, 8192) == 768
     assert cb.cb_paged_attention_split_tokens(68, 32, 8, 4, 8192) == 768      # q = 4: decode-type
     assert cb.cb_paged_attention_split_tokens(131, 64, 8, 4096, 16384) == 2048
     assert cb.cb_paged_attention_split_tokens(4, 4, 2, 1, 40, 100000) == 2048
