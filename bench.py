@@ -13,6 +13,8 @@ own roofline and oracle sample: "mixed_batch" (the same model shape, 64 decode t
 prefill-chunk tokens), "long_context_decode" (16 sequences of 32K-128K keys, split-KV partitions
 and the log-sum-exp merge) and "mixed_batch_70b" (64 q-heads / 8 KV heads, block 32, 8192 tokens:
 128 decodes + chunked prefills, a 2048-token prefix shared by a quarter of the sequences).
+The mixed workloads also carry "decode_sub_batch": the decode KV rate of their decode rows
+alone (same cache and tables), over the whole attention call and over the decode kernel.
 "stream_read" is the measured streaming-read rate of this GPU (cb_stream_read over 2 GiB), which
 the decode rooflines are also reported against. The headline step runs the given W warm-up and
 K timed steps; the further workloads, and the prefill roofline's chunks-alone launches, are timed
@@ -486,6 +488,43 @@ def measure(args, config, steps, warmup, warm_s=0.0):
             f"prefill kernel avg {r['kernel_ms']:.4f} ms (min {min(iso_ms):.4f}, max {max(iso_ms):.4f}) "
             f"after {n_warm} untimed launches; the first {len(cold_ms)} after set-up: median "
             f"{r['kernel_ms_cold']:.4f} ms")
+        # The batch's decode rows alone (same cache and tables): the decode KV rate of a mixed
+        # batch, timed over the whole attention call (the merge included) and on its kernel.
+        dec = np.nonzero((b.cu_seqlens_q[1:] - b.cu_seqlens_q[:-1]) * (b.num_q_heads // b.num_kv_heads) <= 16)[0]
+        if len(dec):
+            drows = np.concatenate([np.arange(b.cu_seqlens_q[s], b.cu_seqlens_q[s + 1]) for s in dec])
+            dql = (b.cu_seqlens_q[1:] - b.cu_seqlens_q[:-1])[dec]
+            qd = q[torch.from_numpy(drows).to(dev)].contiguous()
+            cud = up_i32(np.concatenate([[0], np.cumsum(dql)]))
+            kvd, btd = up_i32(b.kv_lens[dec]), up_i32(b.block_tables[dec])
+            outd = torch.empty((len(drows), b.num_q_heads, b.head_dim), dtype=torch.bfloat16, device=dev)
+            mqd, mkvd = int(dql.max()), int(b.kv_lens[dec].max())
+            wsd = cb.alloc_workspace(len(dec), len(drows), b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                     b.block_size, mqd, mkvd, 0, device=dev)
+
+            def dec_call(ev=None):
+                if ev is not None:
+                    ev[0].record(stream)
+                    cb.cb_time_next_kernel(cb.CB_KERNEL_DECODE, ev[2], ev[3], stream=stream)
+                cb.cb_paged_attention(qd, cud, kvd, btd, kc, vc, outd, b.scale, mqd, mkvd, wsd,
+                                      stream=stream)
+                if ev is not None:
+                    ev[1].record(stream)
+
+            for _ in range(max(2, warmup)):
+                dec_call()
+            dev_ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
+            for ev in dev_ev:
+                dec_call(ev)
+            torch.cuda.synchronize()
+            call_ms = [e[0].elapsed_time(e[1]) for e in dev_ev]
+            dk_ms = [e[2].elapsed_time(e[3]) for e in dev_ev]
+            r["decode_alone"] = {"sequences": int(len(dec)), "tokens": int(len(drows)),
+                                 "call_ms_median": pct(call_ms, 0.5), "kernel_ms_median": pct(dk_ms, 0.5),
+                                 "call_ms_p10": pct(call_ms, 0.1), "call_ms_p90": pct(call_ms, 0.9)}
+            log(f"[bench] {b.name} decode rows alone ({len(dec)} sequences): attention call median "
+                f"{r['decode_alone']['call_ms_median']:.4f} ms, decode kernel median "
+                f"{r['decode_alone']['kernel_ms_median']:.4f} ms")
     log(f"[bench] {b.name} {'decode' if kernel == cb.CB_KERNEL_DECODE else 'prefill'} kernel "
         f"p10 / median / p90 {r['kernel_ms_p10']:.4f} / {r['kernel_ms_median']:.4f} / "
         f"{r['kernel_ms_p90']:.4f} ms; after reading {FLUSH_BYTES >> 20} MiB to flush the caches (median of "
@@ -545,6 +584,8 @@ def sub_result(args, config, stream_gbs, cpu_budget_s):
     }
     if mixed:
         out["prefill_flops"] = w["prefill_flops"]
+        if m.get("decode_alone"):
+            out["decode_sub_batch"] = decode_sub_batch_of(m, stream_gbs)
     uniq = unique_kv_bytes(b)
     if uniq < w["kv_bytes"]:  # blocks shared by several sequences: bytes of distinct slots
         out["kv_bytes_logical"] = w["kv_bytes"]
@@ -553,6 +594,25 @@ def sub_result(args, config, stream_gbs, cpu_budget_s):
         log(f"[bench] timing the oracle on the host cores ({b.name}) ...")
         out["cpu_baseline"] = cpu_baseline(b, cpu_budget_s, mixed=mixed)
         log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+    return out
+
+
+def decode_sub_batch_of(r, stream_gbs=None):
+    """The decode KV rate of a mixed batch's decode rows alone (reported, no target): the decode
+    kernel's algorithmic bytes over the median time of the whole attention call (merge
+    included), and over the decode kernel's own median time."""
+    d, by = r["decode_alone"], r["work"]["decode_kernel_bytes"]
+    gbs = by / (d["call_ms_median"] / 1e3) / 1e9
+    kgbs = by / (d["kernel_ms_median"] / 1e3) / 1e9
+    out = {"metric": "decode KV GB/s of the batch's decode rows alone (same cache and tables)",
+           "sequences": d["sequences"], "tokens": d["tokens"], "bytes": by,
+           "call_ms_median": round(d["call_ms_median"], 5),
+           "call_ms_p10": round(d["call_ms_p10"], 5), "call_ms_p90": round(d["call_ms_p90"], 5),
+           "gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "kernel_ms_median": round(d["kernel_ms_median"], 5), "kernel_gbs": round(kgbs, 2),
+           "kernel_hbm_frac": round(kgbs / HBM_PEAK_GBS, 4)}
+    if stream_gbs:
+        out["kernel_frac_of_stream_ceiling"] = round(kgbs / stream_gbs, 4)
     return out
 
 
@@ -1145,6 +1205,8 @@ def main():
     }
     if w["prefill_flops"]:
         res["prefill_flops"] = w["prefill_flops"]
+    if r.get("decode_alone"):
+        res["decode_sub_batch"] = decode_sub_batch_of(r, stream["gbs"])
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores ...")
         res["cpu_baseline"] = cpu_baseline(b, mixed=args.config not in DECODE_CONFIGS)
