@@ -232,16 +232,24 @@ __device__ inline void prefill_split(int kend, int emax, int& ns, int& chunk) {
   ns = (kend + chunk - 1) / chunk;
 }
 
-__device__ inline int seq_items(const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_lens,
-                                int s, int num_seqs, int G, int P, int qmaxd, int max_splits,
-                                int bq, int bs, int max_blocks, int max_kv, int& nfull, int& rem,
-                                int& np) {
+// A sequence's inputs to the plan: first packed row, query rows and KV length (zeros past the
+// last sequence, which then has no work).
+struct SeqIn {
+  int c0, q, L;
+};
+__device__ __forceinline__ SeqIn seq_in(const int32_t* __restrict__ cu,
+                                        const int32_t* __restrict__ kv_lens, int s, int num_seqs) {
+  if (s >= num_seqs) return SeqIn{0, 0, 0};
+  const int c0 = cu[s];
+  return SeqIn{c0, cu[s + 1] - c0, kv_lens[s]};
+}
+
+__device__ inline int seq_items(const SeqIn& in, int G, int P, int qmaxd, int max_splits, int bq,
+                                int bs, int max_blocks, int max_kv, int& nfull, int& rem, int& np) {
   nfull = 0;
   rem = 0;
   np = 0;
-  if (s >= num_seqs) return 0;
-  const int q = cu[s + 1] - cu[s];
-  const int L = kv_lens[s];
+  const int q = in.q, L = in.L;
   if (q <= 0 || L < q || L > max_kv || (L + bs - 1) / bs > max_blocks) return 0;
   if (q * G <= 16) {
     if (q > qmaxd || (L + P - 1) / P > max_splits) return 0;
@@ -251,6 +259,17 @@ __device__ inline int seq_items(const int32_t* __restrict__ cu, const int32_t* _
     np = (q + bq - 1) / bq;
   }
   return 1;
+}
+
+// Sum over the wave's lanes (64-bit, as two 32-bit halves per shuffle).
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    v += (unsigned long long)hi << 32 | lo;
+  }
+  return v;
 }
 
 // Inclusive prefix sums of two values over the 1024 threads of the planning workgroup: within
@@ -301,14 +320,20 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
                                           int32_t* __restrict__ nsplit_tok, int32_t beside) {
   __shared__ int2 wsum[16];
   __shared__ int32_t first_item[1024];  // index of each thread's first full partition
+  __shared__ int32_t sh_c0[1024], sh_q[1024], sh_L[1024];  // this pass's sequences' inputs
   __shared__ int32_t base[2];
   __shared__ int32_t split_on;
+  __shared__ int32_t pre_tiles;            // prefill tiles of the batch
   __shared__ unsigned long long dec_keys;  // sum of decode sequences' lengths
   __shared__ unsigned long long pre_steps; // 32-key steps of all prefill tiles (one KV head)
   __shared__ int32_t max_pre_len;          // longest prefill sequence (its last tile's keys)
   __shared__ int32_t tail_count[kTailBuckets];
   __shared__ int32_t tail_next[kTailBuckets];
   const int tid = threadIdx.x;
+  // Up to 1024 sequences (one per thread) are planned in one pass, and each thread keeps its
+  // sequence's inputs and item counts in registers for the later passes; more take one pass per
+  // 1024 sequences, each reading its inputs again.
+  const bool one = num_seqs <= 1024;
   if (tid == 0) {
     base[0] = base[1] = 0;
     dec_keys = 0;
@@ -319,19 +344,24 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
   if (maxs > 1)  // split counts of prefill tokens: 0 until a split tile writes its own
     for (int t = tid; t < num_tokens; t += 1024) nsplit_tok[t] = 0;
   __syncthreads();
+  SeqIn in{0, 0, 0};
+  int nfull = 0, rem = 0, np = 0;
   // pass 1: full partitions by prefix sums; prefill tiles counted; tails counted per bucket
   for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
     const int s = s0 + tid;
-    int nfull, rem, np;
-    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull,
-              rem, np);
+    in = seq_in(cu, kv_lens, s, num_seqs);
+    seq_items(in, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull, rem, np);
+    sh_c0[tid] = in.c0;
+    sh_q[tid] = in.q;
+    sh_L[tid] = in.L;
     if (rem > 0) atomicAdd(&tail_count[(P - rem) * kTailBuckets / P], 1);
-    if (nfull + rem > 0) atomicAdd(&dec_keys, (unsigned long long)(nfull * P + rem));
+    // decode keys: a wave's sum, then one shared atomic per wave
+    const unsigned long long dk = wave_sum_u64((unsigned long long)(nfull * P + rem));
+    if ((tid & 63) == 0 && dk > 0) atomicAdd(&dec_keys, dk);
     if (np > 0) {
-      atomicMax(&max_pre_len, kv_lens[s]);
-      const int qn = cu[s + 1] - cu[s], L = kv_lens[s];
+      atomicMax(&max_pre_len, in.L);
       unsigned long long stp = 0;
-      for (int t = 0; t < np; ++t) stp += (L - qn + min(qn, (t + 1) * bq) + 31) / 32;
+      for (int t = 0; t < np; ++t) stp += (in.L - in.q + min(in.q, (t + 1) * bq) + 31) / 32;
       atomicAdd(&pre_steps, stp);
     }
     const int2 inc = block_scan2(nfull, np, wsum);
@@ -347,10 +377,9 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
         const int mid = (lo + hi + 1) >> 1;
         if (first_item[mid] <= i) lo = mid; else hi = mid - 1;
       }
-      const int sq = s0 + lo;
       const int64_t ed = (int64_t)base[0] + i;
       if (ed < dec_cap)
-        dec[ed] = DecWork{sq, i - first_item[lo], cu[sq], cu[sq + 1] - cu[sq], kv_lens[sq], 0, 0, 0};
+        dec[ed] = DecWork{s0 + lo, i - first_item[lo], sh_c0[lo], sh_q[lo], sh_L[lo], 0, 0, 0};
     }
     __syncthreads();
     if (tid == 1023) {
@@ -368,9 +397,12 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
     }
     counts[0] = (int32_t)min((int64_t)acc, dec_cap);
     counts[2] = 0;  // decode work-queue head
+    pre_tiles = base[1];
+    base[1] = 0;  // prefill item offset
+    if (pre_tiles == 0) counts[1] = 0;
     const float t_decode = (float)dec_keys * Hkv * kv_token_bytes / kDecodeBytesPerUs;
     const float t_longest = (float)((max_pre_len + 31) / 32) * kPrefillStepUs;
-    split_on = (maxs > 1 && (int64_t)base[1] * Hkv < 2 * (int64_t)cus && t_longest > t_decode)
+    split_on = (maxs > 1 && (int64_t)pre_tiles * Hkv < 2 * (int64_t)cus && t_longest > t_decode)
                    ? 1 : 0;  // split prefill tiles
     counts[3] = split_on;
     // Compute units for the decode kernel when it runs beside the prefill kernel (one workgroup
@@ -386,54 +418,54 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
   __syncthreads();
   const int emax = split_on ? maxs : 1;
   // prefill items (sequence, tile * kMaxPreSplits + part): a sequence's last tiles first
-  if (tid == 0) base[1] = 0;
-  __syncthreads();
-  for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
-    const int s = s0 + tid;
-    int nfull, rem, np;
-    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull,
-              rem, np);
-    int nit = np, qn = 0, L = 0;
-    if (np > 0) {
-      qn = cu[s + 1] - cu[s];
-      L = kv_lens[s];
-    }
-    if (np > 0 && emax > 1) {  // few tiles (splitting is on): count the parts
-      nit = 0;
-      for (int tl = 0; tl < np; ++tl) {
-        int ns, chunk;
-        prefill_split(L - qn + min(qn, (tl + 1) * bq), emax, ns, chunk);
-        nit += ns;
+  if (pre_tiles > 0) {
+    for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
+      const int s = s0 + tid;
+      SeqIn pin = in;
+      int pf, pr, pn = np;
+      if (!one) {
+        pin = seq_in(cu, kv_lens, s, num_seqs);
+        seq_items(pin, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, pf, pr, pn);
       }
-    }
-    const int incp = block_scan2(nit, 0, wsum).x;
-    int64_t ep = (int64_t)base[1] + incp - nit;
-    if (emax > 1) {
-      for (int tl = np - 1; tl >= 0; --tl) {
-        int ns, chunk;
-        prefill_split(L - qn + min(qn, (tl + 1) * bq), emax, ns, chunk);
-        for (int part = 0; part < ns; ++part, ++ep)
-          if (ep < pre_cap) pre[ep] = Work{s, tl * kMaxPreSplits + part, cu[s], qn, L, 0, 0, 0};
+      const int qn = pin.q, L = pin.L;
+      int nit = pn;
+      if (pn > 0 && emax > 1) {  // few tiles (splitting is on): count the parts
+        nit = 0;
+        for (int tl = 0; tl < pn; ++tl) {
+          int ns, chunk;
+          prefill_split(L - qn + min(qn, (tl + 1) * bq), emax, ns, chunk);
+          nit += ns;
+        }
       }
-    } else {
-      for (int k = 0; k < np; ++k)
-        if (ep + k < pre_cap) pre[ep + k] = Work{s, (np - 1 - k) * kMaxPreSplits, cu[s], qn, L, 0, 0, 0};
+      const int incp = block_scan2(nit, 0, wsum).x;
+      int64_t ep = (int64_t)base[1] + incp - nit;
+      if (emax > 1) {
+        for (int tl = pn - 1; tl >= 0; --tl) {
+          int ns, chunk;
+          prefill_split(L - qn + min(qn, (tl + 1) * bq), emax, ns, chunk);
+          for (int part = 0; part < ns; ++part, ++ep)
+            if (ep < pre_cap) pre[ep] = Work{s, tl * kMaxPreSplits + part, pin.c0, qn, L, 0, 0, 0};
+        }
+      } else {
+        for (int k = 0; k < pn; ++k)
+          if (ep + k < pre_cap) pre[ep + k] = Work{s, (pn - 1 - k) * kMaxPreSplits, pin.c0, qn, L, 0, 0, 0};
+      }
+      __syncthreads();
+      if (tid == 1023) base[1] += incp;
+      __syncthreads();
     }
-    __syncthreads();
-    if (tid == 1023) base[1] += incp;
-    __syncthreads();
+    if (tid == 0) counts[1] = (int32_t)min((int64_t)base[1], pre_cap);
   }
-  if (tid == 0) counts[1] = (int32_t)min((int64_t)base[1], pre_cap);
-  __syncthreads();
-  // pass 2: place the tails
+  // pass 2: place the tails (tail_next is set and visible since the barrier above)
   for (int s0 = 0; s0 < num_seqs; s0 += 1024) {
     const int s = s0 + tid;
-    int nfull, rem, np;
-    seq_items(cu, kv_lens, s, num_seqs, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull,
-              rem, np);
+    if (!one) {
+      in = seq_in(cu, kv_lens, s, num_seqs);
+      seq_items(in, G, P, qmaxd, max_splits, bq, bs, max_blocks, max_kv, nfull, rem, np);
+    }
     if (rem > 0) {
       const int64_t pos = atomicAdd(&tail_next[(P - rem) * kTailBuckets / P], 1);
-      if (pos < dec_cap) dec[pos] = DecWork{s, nfull, cu[s], cu[s + 1] - cu[s], kv_lens[s], 0, 0, 0};
+      if (pos < dec_cap) dec[pos] = DecWork{s, nfull, in.c0, in.q, in.L, 0, 0, 0};
     }
   }
 }
@@ -472,11 +504,25 @@ struct WriteArgs {
 };
 
 // The sequence of packed token t (0 <= t < cu[num_seqs], num_seqs >= 1): the last s < num_seqs
-// with cu[s] <= t. The lanes compare 64 evenly spaced entries of cu[0 .. num_seqs) at once and the
-// range shrinks 64-fold per round (two rounds up to 4096 sequences). cu is non-decreasing, so
-// the lanes that pass form a prefix; only cu[0 .. num_seqs) is read.
+// with cu[s] <= t. cu is non-decreasing and cu[0] = 0, so the entries <= t form a prefix and s is
+// their count minus one. Up to 1024 sequences: each lane loads up to 16 entries at once and the
+// wave counts them (one round of loads). More: the lanes compare 64 evenly spaced entries and the
+// range shrinks 64-fold per round. Only cu[0 .. num_seqs) is read.
 __device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int num_seqs, int t,
                                             int lane) {
+  if (num_seqs <= 1024) {
+    const int per = (num_seqs + 63) >> 6;  // entries per lane, 1..16
+    int v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = lane * per + j;
+      v[j] = (j < per && i < num_seqs) ? cu[i] : INT32_MAX;
+    }
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[j] <= t));
+    return n - 1;
+  }
   int lo = 0, len = num_seqs;  // cu[lo] <= t holds throughout (cu[0] = 0)
   while (len > 1) {
     const int step = (len + 63) / 64;
@@ -488,12 +534,45 @@ __device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int 
   return lo;
 }
 
+// The token's K and V rows are loaded first (they depend on t alone), so their latency overlaps
+// the sequence search and the table lookup that give the slot.
 __device__ __forceinline__ void write_body(const WriteArgs& w, const int32_t* __restrict__ cu,
                                            const int32_t* __restrict__ kv_lens, int32_t num_seqs,
                                            int32_t num_tokens, int32_t bs, int32_t max_blocks,
                                            int first_wave, int num_waves) {
   const int lane = threadIdx.x & 63;
   for (int t = first_wave; t < num_tokens; t += num_waves) {
+    if (w.chunks <= 256) {  // a row of at most 4 KiB: four 16-byte pieces per lane
+      const u32x4* kin = reinterpret_cast<const u32x4*>(w.k) + (int64_t)t * w.chunks;
+      const u32x4* vin = reinterpret_cast<const u32x4*>(w.v) + (int64_t)t * w.chunks;
+      u32x4 kr[4], vr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {  // pieces past the row end load its last piece (not stored)
+        const int c = min(lane + 64 * r, w.chunks - 1);
+        kr[r] = kin[c];
+        vr[r] = vin[c];
+      }
+      const int s = seq_of_token(cu, num_seqs, t, lane);
+      const int32_t q = cu[s + 1] - cu[s];
+      const int32_t p = kv_lens[s] - q + (t - cu[s]);
+      if (p < 0) continue;
+      const int32_t j = p / bs;
+      if (j >= max_blocks) continue;
+      const int32_t blk = w.tables[(int64_t)s * max_blocks + j];
+      const int64_t slot = (int64_t)blk * bs + p % bs;
+      if (blk < 0 || slot >= w.slots) continue;
+      u32x4* kout = reinterpret_cast<u32x4*>(w.k_cache) + slot * w.chunks;
+      u32x4* vout = reinterpret_cast<u32x4*>(w.v_cache) + slot * w.chunks;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = lane + 64 * r;
+        if (c < w.chunks) {
+          kout[c] = kr[r];
+          vout[c] = vr[r];
+        }
+      }
+      continue;
+    }
     const int s = seq_of_token(cu, num_seqs, t, lane);
     const int32_t q = cu[s + 1] - cu[s];
     const int32_t p = kv_lens[s] - q + (t - cu[s]);
