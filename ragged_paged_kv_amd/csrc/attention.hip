@@ -1082,6 +1082,7 @@ void prefill_kernel(
   const int lane_grp = __builtin_amdgcn_readfirstlane(lr >> 4);
   const uint32_t lane_off = ((lr & 15) * Hkv * D + lc * 8) * (uint32_t)sizeof(__bf16);
   const int64_t row_elems = (int64_t)Hkv * D;  // elements per cache row (token slot)
+  const uint32_t row_bytes = (uint32_t)(Hkv * D * sizeof(__bf16));
   const __bf16* k_head = k_cache + (int64_t)kvh * D;
   const __bf16* v_head = v_cache + (int64_t)kvh * D;
   auto blk_of = [&](int key) __attribute__((always_inline)) { return bdiv.div(key); };
@@ -1108,35 +1109,34 @@ void prefill_kernel(
   // one again, into a buffer nobody reads), so the number of loads in flight is the same on
   // every path.
   uint4 rk[2][PASSES], rv[2][PASSES];
-  // Load tile `step` into register set X. A group at or past kend reads the tile's first group
-  // instead (always valid); those rows are zeroed when stored.
+  // Load tile `step` into register set X, each 16-key group through a buffer descriptor whose
+  // record count ends at kend (groups wholly past it keep the tile's first group as their base
+  // and read nothing).
   auto fetch = [&](auto set_tag, int step) __attribute__((always_inline)) {
     constexpr int X = decltype(set_tag)::value;
     slide_window(step);
     const int t0 = kb + step * KS;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
-      int key = t0 + ps * RPP + 16 * lane_grp;
-      if (key >= kend) key = t0;
+      const int kg = t0 + ps * RPP + 16 * lane_grp;
+      const int key = kg < kend ? kg : t0;
       const int bi = blk_of(key);
       const int blk = __builtin_amdgcn_readlane(win, bi - w0);
       const int64_t row = (int64_t)(uint32_t)(blk * bs + (key - bi * bs)) * row_elems;
-      rk[X][ps] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(k_head + row) + lane_off);
-      rv[X][ps] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(v_head + row) + lane_off);
+      // records: the group's rows before kend (a max and a select, which stay scalar: a clamp
+      // becomes a vector median instruction); rows at or past kend load as zeros
+      const int rem = kend - kg;
+      const uint32_t nb = rem >= 16 ? 0xffffffffu : (uint32_t)max(rem, 0) * row_bytes;
+      rk[X][ps] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(group_rsrc(k_head + row, nb), lane_off, 0, 0));
+      rv[X][ps] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(group_rsrc(v_head + row, nb), lane_off, 0, 0));
     }
   };
-  // Store register set X (tile `step`) to LDS buffer buf. In the last tile, rows at or past kend
-  // are stored as zero, so that a masked probability (0) never meets an unwritten V value.
-  auto stash = [&](auto set_tag, int buf, int step) __attribute__((always_inline)) {
+  // Store register set X to LDS buffer buf. Rows at or past kend hold zeros (their
+  // loads read nothing), so that a masked probability (0) never meets an unwritten V value.
+  auto stash = [&](auto set_tag, int buf) __attribute__((always_inline)) {
     constexpr int X = decltype(set_tag)::value;
-    if (kb + (step + 1) * KS > kend) {  // wave-uniform
-#pragma unroll
-      for (int ps = 0; ps < PASSES; ++ps)
-        if (kb + step * KS + ps * RPP + lr >= kend) {
-          rk[X][ps] = make_uint4(0, 0, 0, 0);
-          rv[X][ps] = make_uint4(0, 0, 0, 0);
-        }
-    }
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       *reinterpret_cast<uint4*>(&sm.k[buf][lr + ps * RPP][lc * 8]) = rk[X][ps];
@@ -1199,8 +1199,8 @@ void prefill_kernel(
   const int last_tile = nsteps - 1;
   fetch(Int<0>{}, 0);
   fetch(Int<1>{}, min(1, last_tile));
-  stash(Int<0>{}, 0, 0);
-  stash(Int<1>{}, 1, min(1, last_tile));
+  stash(Int<0>{}, 0);
+  stash(Int<1>{}, 1);
   fetch(Int<0>{}, min(2, last_tile));
   fetch(Int<1>{}, min(3, last_tile));
   __syncthreads();
@@ -1245,7 +1245,7 @@ void prefill_kernel(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       kf[kk] = *reinterpret_cast<const bf16x8*>(&sm.k[nxt][n32][16 * kk + 8 * h]);
-    stash(Int<P>{}, fil, min(st + 2, last_tile));
+    stash(Int<P>{}, fil);
     fetch(Int<P>{}, min(st + 4, last_tile));
     __builtin_amdgcn_sched_barrier(0);
     // V^T read j of tile st: key half ks = j / (2 NDT), dim tile dt = (j / 2) % NDT, 8-key half
