@@ -101,19 +101,22 @@ def test_full_size_every_element():
 
 
 @pytest.mark.parametrize("split", [0, 64])
-def test_more_sequences_than_one_planning_pass(split):
-    """1102 sequences: the planning workgroup takes sequences 1024 at a time, and the fused write
-    searches 1102 sequences. Fused and separate paths agree bit for bit, every output row is
-    written, and rows on both sides of the 1024 boundary and the prefill chunks' rows match the
-    oracle (slot mapping and caches whole)."""
+@pytest.mark.parametrize("nseq", [1102, 1024])
+def test_more_sequences_than_one_planning_pass(nseq, split):
+    """1102 sequences: the planning workgroup takes sequences 1024 at a time and reads each
+    pass's inputs again, and the fused write searches the sequences in rounds of 64 evenly spaced
+    entries. 1024 sequences: the most that one planning pass holds in registers, and the most
+    the write's one-round search covers (16 entries per lane). Fused and separate paths agree bit
+    for bit, every output row is written, and rows on both sides of the 1024 boundary and the
+    prefill chunks' rows match the oracle (slot mapping and caches whole)."""
     rng = np.random.default_rng(77)
-    specs = [synth.SeqSpec(1, int(L)) for L in rng.integers(1, 200, 1100)]
+    specs = [synth.SeqSpec(1, int(L)) for L in rng.integers(1, 200, nseq - 2)]
     specs += [synth.SeqSpec(40, 300), synth.SeqSpec(70, 70)]
     b = tiny_batch(specs, 8, 2, 64, 16, seed=77)
-    say(f"[fused] 1102 sequences split {split}")
+    say(f"[fused] {nseq} sequences split {split}")
     out = same_as_separate(b, split)
     assert torch.isfinite(out.float()).all(), "an output row was not written"
     step = Step(b, kv_split_tokens=split).run()
-    toks = np.concatenate([np.arange(0, 40), np.arange(1000, 1100),
+    toks = np.concatenate([np.arange(0, 40), np.arange(nseq - 102, nseq - 2),
                            np.arange(b.num_tokens - 110, b.num_tokens)])
     check_full(b, step, tokens=toks)
