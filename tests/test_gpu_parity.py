@@ -306,6 +306,38 @@ def test_edge_cases(torch_cuda, name, split):
     check_full(b, step)
 
 
+def _random_batch(seed):
+    """A seeded random batch within the contract: KV heads 1-8, query heads per KV head 1-16
+    (at most 64 query heads), head_dim 64 or 128, block sizes 16, 32, 48 or 64, 1-20 sequences
+    mixing decode-type (q * G <= 16) and prefill-type chunks at random offsets into their
+    contexts; and a random KV partition request (0 = the library's choice)."""
+    rng = np.random.default_rng(seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8, 16) if g * Hkv <= 64]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 48, 64]))
+    specs = []
+    for _ in range(int(rng.integers(1, 21))):
+        if rng.random() < 0.6:
+            q = int(rng.integers(1, max(1, 16 // G) + 1))
+            L = int(rng.integers(q, 2601))
+        else:
+            q = int(rng.integers(16 // G + 1, 161))
+            L = q + int(rng.integers(0, 2401))
+        specs.append(synth.SeqSpec(q, L))
+    split = int(rng.choice([0, 32, 96, 256]))
+    return tiny_batch(specs, G * Hkv, Hkv, D, bs, seed=seed), split
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_batches(torch_cuda, seed):
+    b, split = _random_batch(5000 + seed)
+    say(f"[parity] random batch {seed}: S={b.num_seqs} T={b.num_tokens} Hq={b.num_q_heads} "
+        f"Hkv={b.num_kv_heads} D={b.head_dim} bs={b.block_size} split={split}")
+    step = Step(b, kv_split_tokens=split).run()
+    check_full(b, step)
+
+
 def test_loose_upper_bounds(torch_cuda):
     # host bounds larger than the real maxima only size grids and the workspace
     b = synth.make_config(3, small=True)
