@@ -750,15 +750,22 @@ void decode_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (4 * g + i) * row_bytes + n * (D / 16) * (uint32_t)sizeof(__bf16);
 
-  // Each wave takes (partition, KV head) items until they run out: the active wave w first takes
-  // item w, then items nwaves + k for k = 0, 1, ... from the shared counter, and leaves once its
-  // index passes `total`, so every item is taken once. The first items need no atomic: all
-  // waves starting at once on one counter serialise. (Taking the next index while the current
-  // item still streams was measured slower: near the end of the queue it binds short items to
-  // waves that are still busy.)
+  // Each wave takes (partition, KV head) items until they run out: every active wave first takes
+  // one of items 0 .. nwaves - 1, then items nwaves + k for k = 0, 1, ... from the shared
+  // counter, and leaves once its index passes `total`, so every item is taken once. The first
+  // items need no atomic: all waves starting at once on one counter serialise. (Taking the next
+  // index while the current item still streams was measured slower: near the end of the queue
+  // it binds short items to waves that are still busy.) The first items go to the waves of a
+  // workgroup in turn (the KV heads of a partition side by side on one CU, reading their
+  // cache slots together), except when there are fewer items than waves: they are then dealt
+  // across the workgroups, so that every CU streams (16 sequences of 256-2048 keys: 33.6 against
+  // 45.0 us; from about 1.3 items per wave the grouped order is as fast or faster).
   const int wpb = (int)(blockDim.x >> 6);
-  const int nwaves = min((int)gridDim.x, counts[4]) * wpb;
-  int idx = __builtin_amdgcn_readfirstlane((int)blockIdx.x * wpb + (int)(threadIdx.x >> 6));
+  const int nblk = min((int)gridDim.x, counts[4]);
+  const int nwaves = nblk * wpb;
+  const int wv = (int)(threadIdx.x >> 6);
+  int idx = __builtin_amdgcn_readfirstlane(total < nwaves ? wv * nblk + (int)blockIdx.x
+                                                          : (int)blockIdx.x * wpb + wv);
   for (;; ) {
     if (idx >= total) break;
     const int e = idx / Hkv;
