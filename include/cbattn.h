@@ -117,9 +117,10 @@ size_t cb_paged_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
  * KV partition size (tokens) cb_paged_attention uses for decode-type sequences with these
  * bounds (the same arguments as cb_paged_attention_workspace_size); kv_split_tokens > 0 requests
  * a size (rounded up to a multiple of 32, at most 2048). Automatic: about
- * max_kv_len * num_seqs * num_kv_heads / 5461 in steps of 256, within [256, 2048], with or
- * without prefill-type sequences (num_q_heads and max_q_len do not change it; they keep the
- * argument list of cb_paged_attention_workspace_size).
+ * max_kv_len * num_seqs * num_kv_heads / 5461 in steps of 256, within [256, 2048]; when that
+ * gives 256 and no prefill-type sequence is possible (max_q_len * num_q_heads / num_kv_heads <=
+ * 16), 256, 512 or 1024 for max_kv_len * num_seqs * num_kv_heads below 393216, below 786432, or
+ * above.
  */
 int32_t cb_paged_attention_split_tokens(int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t max_q_len,

@@ -1606,7 +1606,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kNoAllocScratchBytes = CB_NOALLOC_SCRATCH_BYTES;
 constexpr size_t kNoAllocPrefillBudget = kNoAllocScratchBytes / 4;
 
-int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t requested) {
+int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t requested,
+                     bool decode_only) {
   if (requested > 0) {
     int32_t p = (int32_t)cb::ceil_div(requested, 32) * 32;
     return p > kMaxSplitTokens ? kMaxSplitTokens : p;
@@ -1619,8 +1620,14 @@ int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t 
   // and 2048 against 1536's 5% better at 128 of up to 16K (the 2048 cap). The same rule holds
   // beside prefill work: over four draws of the 8B-shaped mixed 2048-token batch its 768 took
   // the fused step 0.6-3% less time than partitions 1.5 times larger.
+  // Smaller decode-only batches, where that rule gives its 256-key floor, start too many short
+  // items: each item's start costs several memory round trips, and few items per wave leave
+  // nothing to hide them. There the size follows the upper-bound keys instead: 256 below 384K,
+  // 512 below 768K, else 1024 (on 27 draws of 8-192 sequences of up to 2K-8K keys this took the
+  // fused step 3-17% less time where it changed the size, and never more).
   const int64_t keys = (int64_t)max_kv_len * num_seqs * Hkv;
-  const int64_t p = (keys / 5461 + 128) / 256 * 256;
+  int64_t p = (keys / 5461 + 128) / 256 * 256;
+  if (decode_only && p <= 256) p = keys < 393216 ? 256 : (keys < 786432 ? 512 : 1024);
   return (int32_t)std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(256, p));
 }
 
@@ -1630,7 +1637,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t Hq, int32_t Hkv, in
   Plan p;
   p.G = Hq / Hkv;
   const int32_t dec_q = 16 / p.G;  // longest decode-type chunk
-  p.P = choose_split(num_seqs, Hkv, max_kv_len, kv_split_tokens);
+  p.P = choose_split(num_seqs, Hkv, max_kv_len, kv_split_tokens, (int64_t)max_q_len * p.G <= 16);
   p.max_splits = (int32_t)cb::ceil_div(max_kv_len, p.P);
   p.qmaxd = max_q_len < dec_q ? max_q_len : dec_q;
   p.bq = kPrefillRows / p.G;
@@ -1737,9 +1744,9 @@ Aux aux_stream(hipStream_t st, AuxStream* out) {
 extern "C" int32_t cb_paged_attention_split_tokens(int32_t num_seqs, int32_t num_q_heads,
                                                    int32_t num_kv_heads, int32_t max_q_len,
                                                    int32_t max_kv_len, int32_t kv_split_tokens) {
-  (void)num_q_heads;
-  (void)max_q_len;
-  return choose_split(num_seqs, num_kv_heads, max_kv_len, kv_split_tokens);
+  const int32_t G = num_kv_heads > 0 && num_q_heads >= num_kv_heads ? num_q_heads / num_kv_heads : 1;
+  return choose_split(num_seqs, num_kv_heads, max_kv_len, kv_split_tokens,
+                      (int64_t)max_q_len * G <= 16);
 }
 
 extern "C" size_t cb_paged_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,

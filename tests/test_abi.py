@@ -130,6 +130,12 @@ def test_workspace_size_and_split_choice():
     for S, L in ((1, 100000), (300, 3000), (2048, 512), (7, 65536)):
         p = cb.cb_paged_attention_split_tokens(S, 32, 8, 1, L)
         assert p % 256 == 0 and 256 <= p <= 2048
+    # decode-only batches where that gives its floor: by the upper-bound keys
+    assert cb.cb_paged_attention_split_tokens(16, 32, 8, 1, 2048) == 256     # 262144 keys
+    assert cb.cb_paged_attention_split_tokens(8, 32, 8, 1, 8192) == 512      # 524288
+    assert cb.cb_paged_attention_split_tokens(32, 32, 8, 1, 4096) == 1024    # 1048576
+    assert cb.cb_paged_attention_split_tokens(32, 32, 8, 64, 4096) == 256    # prefill possible
+    assert cb.cb_paged_attention_split_tokens(64, 32, 8, 1, 8192) == 768     # above the floor
     # the same rule with prefill-type sequences possible (q > 16 / G)
     assert cb.cb_paged_attention_split_tokens(68, 32, 8, 1024, 8192) == 768
     assert cb.cb_paged_attention_split_tokens(68, 32, 8, 4, 8192) == 768      # q = 4: decode-type
