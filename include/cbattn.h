@@ -119,8 +119,10 @@ size_t cb_paged_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
  * a size (rounded up to a multiple of 32, at most 2048). Automatic: about
  * max_kv_len * num_seqs * num_kv_heads / 5461 in steps of 256, within [256, 2048]; when that
  * gives 256 and no prefill-type sequence is possible (max_q_len * num_q_heads / num_kv_heads <=
- * 16), 256, 512 or 1024 for max_kv_len * num_seqs * num_kv_heads below 393216, below 786432, or
- * above.
+ * 16): with K = max_kv_len * num_seqs * num_kv_heads, the larger of K / 640 and max_kv_len / 24,
+ * at most the larger of 768 and max_kv_len / 8, rounded up to a multiple of 64 within
+ * [128, 2048]; and max_kv_len rounded up to a multiple of 32 (one partition per sequence) when
+ * twice that size reaches max_kv_len.
  */
 int32_t cb_paged_attention_split_tokens(int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t max_q_len,

@@ -1620,14 +1620,26 @@ int32_t choose_split(int32_t num_seqs, int32_t Hkv, int32_t max_kv_len, int32_t 
   // and 2048 against 1536's 5% better at 128 of up to 16K (the 2048 cap). The same rule holds
   // beside prefill work: over four draws of the 8B-shaped mixed 2048-token batch its 768 took
   // the fused step 0.6-3% less time than partitions 1.5 times larger.
-  // Smaller decode-only batches, where that rule gives its 256-key floor, start too many short
-  // items: each item's start costs several memory round trips, and few items per wave leave
-  // nothing to hide them. There the size follows the upper-bound keys instead: 256 below 384K,
-  // 512 below 768K, else 1024 (on 27 draws of 8-192 sequences of up to 2K-8K keys this took the
-  // fused step 3-17% less time where it changed the size, and never more).
+  // Below that rule's 256-key floor a decode-only batch has too few keys to fill the launch
+  // with balanced items, and the size trades other costs: shorter partitions spread a small
+  // batch's keys over more waves, longer ones pay fewer item starts (each several memory round
+  // trips) and fewer partials to merge. Measured on 34 draws of 1-120 sequences of up to 700 to
+  // 131072 keys (fused step, 8B-shaped heads, sizes 128-2048), the fastest size tracked about
+  // one 640th of the upper-bound keys (at least a 24th of the longest sequence), but no more
+  // than 768 unless the longest sequence is over 8 times that (a few long sequences stream best
+  // in long items); one partition per sequence (no merge) won wherever it needed at most twice
+  // that size. This choice came within 1.8% of the fastest measured size on average (8.5% at
+  // worst).
   const int64_t keys = (int64_t)max_kv_len * num_seqs * Hkv;
-  int64_t p = (keys / 5461 + 128) / 256 * 256;
-  if (decode_only && p <= 256) p = keys < 393216 ? 256 : (keys < 786432 ? 512 : 1024);
+  const int64_t p = (keys / 5461 + 128) / 256 * 256;
+  if (decode_only && p <= 256) {
+    const int64_t L = max_kv_len;
+    int64_t d = std::max<int64_t>((keys + 639) / 640, (L + 23) / 24);
+    d = std::min<int64_t>(d, std::max<int64_t>(768, L / 8));
+    d = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(128, (d + 63) / 64 * 64));
+    if (2 * d >= L) d = std::max<int64_t>(32, (L + 31) / 32 * 32);
+    return (int32_t)d;
+  }
   return (int32_t)std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(256, p));
 }
 
@@ -1960,13 +1972,17 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
   {
     // Persistent, 2 waves per SIMD. Beside prefill work: one 8-wave workgroup per compute unit
     // (the whole register file, so a compute unit holds either decode or prefill work and none is
-    // left over), of which the plan lets counts[4] work. Otherwise two 4-wave workgroups per
-    // compute unit, which spreads small batches over more units. Never more waves than items.
+    // left over), of which the plan lets counts[4] work; never more waves than items. Otherwise
+    // 4-wave workgroups, one or two per compute unit for every unit: a batch with fewer items
+    // than waves has them dealt across the workgroups, and a grid between one and two per unit
+    // would give some units twice the others' share (measured on 22 small decode-only batches:
+    // up to 15% less time with whole rounds, never more than 2% more).
     const int64_t items = p.dec_cap * num_kv_heads;
     const int waves = dst != st ? kDecodeWaves : kDecodeWaves / 2;
     const int64_t per_cu = dst != st ? 1 : 2;
-    const unsigned grid = (unsigned)std::max<int64_t>(
-        1, std::min<int64_t>((items + waves - 1) / waves, per_cu * (int64_t)cus));
+    int64_t groups = std::max<int64_t>(1, std::min<int64_t>((items + waves - 1) / waves, per_cu * (int64_t)cus));
+    if (dst == st) groups = std::min<int64_t>(per_cu * (int64_t)cus, (groups + cus - 1) / cus * cus);
+    const unsigned grid = (unsigned)groups;
     int32_t* queue = counts + 2;
     if (!record_if(tm, CB_KERNEL_DECODE, true, dst)) return fail(CB_ERR_HIP, "hipEventRecord failed");
     if (head_dim == 128)

@@ -126,14 +126,27 @@ def test_workspace_size_and_split_choice():
     assert cb.cb_paged_attention_split_tokens(256, 32, 8, 1, 4096) == 1536
     assert cb.cb_paged_attention_split_tokens(64, 32, 8, 1, 8192) == 768
     assert cb.cb_paged_attention_split_tokens(16, 32, 8, 1, 131072) == 2048     # the cap
-    assert cb.cb_paged_attention_split_tokens(4, 4, 2, 1, 40) == 256          # the floor
-    for S, L in ((1, 100000), (300, 3000), (2048, 512), (7, 65536)):
-        p = cb.cb_paged_attention_split_tokens(S, 32, 8, 1, L)
+    assert cb.cb_paged_attention_split_tokens(4, 4, 2, 24, 40) == 256         # the floor
+    for S, L in ((1, 100000), (300, 3000), (2048, 512), (7, 65536), (1, 40), (16, 2048)):
+        p = cb.cb_paged_attention_split_tokens(S, 32, 8, 64, L)
         assert p % 256 == 0 and 256 <= p <= 2048
-    # decode-only batches where that gives its floor: by the upper-bound keys
-    assert cb.cb_paged_attention_split_tokens(16, 32, 8, 1, 2048) == 256     # 262144 keys
-    assert cb.cb_paged_attention_split_tokens(8, 32, 8, 1, 8192) == 512      # 524288
-    assert cb.cb_paged_attention_split_tokens(32, 32, 8, 1, 4096) == 1024    # 1048576
+        p = cb.cb_paged_attention_split_tokens(S, 32, 8, 1, L)
+        assert p % 32 == 0 and 32 <= p <= 2048
+    # decode-only batches where that gives its floor: about upper-bound keys / 640, at least
+    # max_kv_len / 24, at most max(768, max_kv_len / 8), in steps of 64 within [128, 2048]; the
+    # longest sequence rounded up to 32 when twice that covers it (one partition each)
+    assert cb.cb_paged_attention_split_tokens(8, 32, 8, 1, 583) == 128       # the floor
+    assert cb.cb_paged_attention_split_tokens(3, 32, 8, 1, 1816) == 128      # L / 24 = 76
+    assert cb.cb_paged_attention_split_tokens(16, 32, 8, 1, 2048) == 448     # 262144 keys / 640
+    assert cb.cb_paged_attention_split_tokens(40, 32, 8, 1, 3867) == 768     # capped at 768
+    assert cb.cb_paged_attention_split_tokens(8, 32, 8, 1, 16310) == 1664    # cap L / 8 = 2038
+    assert cb.cb_paged_attention_split_tokens(1, 32, 8, 1, 116544) == 2048   # L / 24, at most 2048
+    assert cb.cb_paged_attention_split_tokens(64, 32, 8, 1, 699) == 704      # one partition each
+    assert cb.cb_paged_attention_split_tokens(96, 32, 8, 1, 1500) == 1504    # 2 x 768 >= 1500
+    assert cb.cb_paged_attention_split_tokens(4, 4, 2, 1, 40) == 64          # one partition each
+    assert cb.cb_paged_attention_split_tokens(1, 32, 8, 1, 0) == 32
+    assert cb.cb_paged_attention_split_tokens(64, 32, 8, 1, 4095) == 768     # 2096640 keys
+    assert cb.cb_paged_attention_split_tokens(64, 32, 8, 1, 4096) == 512     # the rule above
     assert cb.cb_paged_attention_split_tokens(32, 32, 8, 64, 4096) == 256    # prefill possible
     assert cb.cb_paged_attention_split_tokens(64, 32, 8, 1, 8192) == 768     # above the floor
     # the same rule with prefill-type sequences possible (q > 16 / G)

@@ -338,6 +338,35 @@ def test_random_batches(torch_cuda, seed):
     check_full(b, step)
 
 
+# Decode-only batches whose automatic KV partition takes each branch of the size rule for small
+# batches (the expected size is asserted first), compared with the oracle on every element:
+# name -> (sequences, longest KV length, Hq, Hkv, head_dim, block size, expected partition).
+AUTO_SPLIT = {
+    "floor-128": (8, 583, 32, 8, 128, 16, 128),
+    "keys-over-640": (16, 2048, 32, 8, 128, 32, 448),
+    "cap-768": (40, 3867, 32, 8, 128, 48, 768),
+    "long-sequence-cap": (8, 16310, 32, 8, 128, 64, 1664),
+    "largest-2048": (1, 65536, 32, 8, 128, 16, 2048),
+    "one-partition": (64, 699, 32, 8, 128, 16, 704),
+    "one-partition-ends-mid-block": (96, 1500, 32, 8, 128, 64, 1504),
+    "head-dim-64": (4, 900, 16, 8, 64, 16, 128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(AUTO_SPLIT))
+def test_automatic_split_of_small_decode_batches(torch_cuda, name):
+    import ragged_paged_kv_amd as cb
+    S, L, Hq, Hkv, D, bs, want = AUTO_SPLIT[name]
+    assert cb.cb_paged_attention_split_tokens(S, Hq, Hkv, 1, L, 0) == want
+    seed = zlib.crc32(name.encode()) % 100000
+    rng = np.random.default_rng(seed)
+    lens = [L] + [int(x) for x in rng.integers(max(1, L // 8), L + 1, S - 1)]
+    b = tiny_batch([synth.SeqSpec(1, n) for n in lens], Hq, Hkv, D, bs, seed=seed)
+    say(f"[parity] automatic split {name}: S={S} max_kv_len={b.max_kv_len} bs={bs} P={want}")
+    step = Step(b).run()
+    check_full(b, step)
+
+
 def test_loose_upper_bounds(torch_cuda):
     # host bounds larger than the real maxima only size grids and the workspace
     b = synth.make_config(3, small=True)
