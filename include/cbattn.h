@@ -166,10 +166,15 @@ int cb_paged_attention(const void* q_packed, const int32_t* cu_seqlens_q, const 
  * slots the slot mapping would give ("3.3 Batching & Memory Management", PagedAttention: block
  * tables), then attention runs as in cb_paged_attention. The write's slots are computed in place
  * (no slot array), and it runs in the first launch beside the planning workgroup, which reads
- * no cache, instead of in two launches before it. Results are those of the three calls, bit for
- * bit; rows whose position or slot the slot mapping would mark -1 (and slots past the pool) are
- * not written. Arguments, preconditions and errors as cb_paged_attention's, plus
- * num_blocks * block_size < 2^31.
+ * no cache, instead of in two launches before it. A decode-only batch of at most 64 sequences
+ * with fewer (partition, KV head) items than decode waves has no planning launch: the decode
+ * kernel plans itself, its spare waves write the step's rows and each item's wave writes the
+ * new rows of its own partition before reading them. Results are those of the three calls, bit
+ * for bit; rows whose position or slot the slot mapping would mark -1 (and slots past the pool)
+ * are not written. Arguments, preconditions and errors as cb_paged_attention's, plus
+ * num_blocks * block_size < 2^31 and: no sequence reads, at a position below its kv_len, a slot
+ * that this call writes for another sequence (blocks shared between sequences are copied
+ * before they are written, as copy-on-write does).
  */
 int cb_paged_attention_write(const void* q_packed, const void* k_new, const void* v_new,
                              const int32_t* cu_seqlens_q, const int32_t* kv_lens,

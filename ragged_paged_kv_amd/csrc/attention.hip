@@ -723,7 +723,22 @@ __device__ inline int block_of(const int (&bt)[3], int jj) {
   return jj < 64 ? b0 : (jj < 128 ? b1 : b2);
 }
 
-template <int D>
+// Small decode-only batches (at most 64 sequences, fewer (partition, KV head) items than waves)
+// skip the planning launch: every wave derives the work list from the sequence inputs itself
+// (one lane per sequence, the same validity rules and partition counts as the plan, a wave-wide
+// scan) and takes the item that the first-round order across workgroups gives it; no queue. With
+// the fused cache write, the waves left without an item write the step's K/V rows exactly as the
+// write launch does, and each item's wave first writes the new rows inside its own partition at
+// its KV head, then loads: the only rows of this step that an item reads are ones its own wave
+// wrote (one wave's accesses to an address reach memory in issue order, and a fence keeps the
+// compiler from moving the loads above the stores), so no wave waits for another. A row written
+// twice gets the same bytes both times.
+struct SelfPlan {
+  WriteArgs w;  // w.k == nullptr: no cache write
+  int32_t num_seqs, num_tokens, max_kv, max_blocks;
+};
+
+template <int D, bool SELF>
 __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_kernel(
     const __bf16* __restrict__ q, const int32_t* __restrict__ cu,
@@ -733,16 +748,44 @@ void decode_kernel(
     const DecWork* __restrict__ items, const int32_t* __restrict__ counts,
     int32_t* __restrict__ queue, int32_t Hq, int32_t Hkv, BlockDiv bdiv,
     int32_t max_blocks_per_seq, int32_t P, int32_t max_splits, int32_t qmaxd,
-    float scale_log2) {
+    float scale_log2, SelfPlan sp) {
   constexpr int KSTEPS = D / 32;
   constexpr int NO = D / 16;  // output tiles (dims) per row
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int G = Hq / Hkv;
-  const int total = counts[0] * Hkv;
   const int bs = bdiv.bs;
-  // beside prefill work, only the first counts[4] workgroups (one per compute unit) take items
-  if ((int)blockIdx.x >= counts[4]) return;
+  // self-planned, in the plan's order: every full partition (by sequence), then the sequences'
+  // last partial partitions by decreasing length (the short ones land beside full ones when
+  // workgroups take two). Lane s holds sequence s's inputs, its full partitions nf, the length
+  // rm of its partial one (0: none), the inclusive scan of nf and the rank of its partial one.
+  SeqIn sin{0, 0, 0};
+  int nf = 0, rm = 0, incl = 0, rank = 0, nfull_all = 0;
+  int total;
+  if constexpr (SELF) {
+    sin = seq_in(cu, kv_lens, lane, sp.num_seqs);
+    int nfull, rem, np;
+    const int ok = seq_items(sin, G, P, qmaxd, max_splits, 1, bs, sp.max_blocks, sp.max_kv, nfull,
+                             rem, np);
+    nf = ok && np == 0 ? nfull : 0;
+    rm = ok && np == 0 ? rem : 0;
+    incl = nf;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    nfull_all = __builtin_amdgcn_readlane(incl, 63);
+    for (int t = 0; t < sp.num_seqs; ++t) {
+      const int rt = __builtin_amdgcn_readlane(rm, t);
+      rank += (rt > rm || (rt == rm && t < lane)) ? 1 : 0;
+    }
+    total = (nfull_all + (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(rm > 0))) * Hkv;
+  } else {
+    total = counts[0] * Hkv;
+    // beside prefill work, only the first counts[4] workgroups (one per compute unit) take items
+    if ((int)blockIdx.x >= counts[4]) return;
+  }
   // per-lane byte offsets from a group's first cache row (see load_k, load_v)
   const uint32_t row_bytes = (uint32_t)Hkv * D * (uint32_t)sizeof(__bf16);
   const uint32_t koff = n * row_bytes + 16 * g;
@@ -761,20 +804,44 @@ void decode_kernel(
   // across the workgroups, so that every CU streams (16 sequences of 256-2048 keys: 33.6 against
   // 45.0 us; from about 1.3 items per wave the grouped order is as fast or faster).
   const int wpb = (int)(blockDim.x >> 6);
-  const int nblk = min((int)gridDim.x, counts[4]);
+  const int nblk = SELF ? (int)gridDim.x : min((int)gridDim.x, counts[4]);
   const int nwaves = nblk * wpb;
   const int wv = (int)(threadIdx.x >> 6);
-  int idx = __builtin_amdgcn_readfirstlane(total < nwaves ? wv * nblk + (int)blockIdx.x
-                                                          : (int)blockIdx.x * wpb + wv);
+  int idx = __builtin_amdgcn_readfirstlane(SELF || total < nwaves ? wv * nblk + (int)blockIdx.x
+                                                                  : (int)blockIdx.x * wpb + wv);
+  if constexpr (SELF) {
+    // the host launches more waves than items: the rest write the step's K/V rows
+    if (idx >= total) {
+      if (sp.w.k)
+        write_body(sp.w, cu, kv_lens, sp.num_seqs, sp.num_tokens, bs, sp.max_blocks, idx - total,
+                   nwaves - total);
+      return;
+    }
+  }
   for (;; ) {
     if (idx >= total) break;
     const int e = idx / Hkv;
     const int kvh = idx - e * Hkv;
-    const DecWork w = items[e];
-    const int s = w.seq, split = w.split;
-    const int q0 = w.q0;
-    const int qn = w.qn;
-    const int L = w.L;
+    int s, split, q0, qn, L;
+    if constexpr (SELF) {
+      if (e < nfull_all) {  // full partition: the first lane whose inclusive count passes e
+        s = __builtin_popcountll(__builtin_amdgcn_ballot_w64(incl <= e));
+        split = e - (__builtin_amdgcn_readlane(incl, s) - __builtin_amdgcn_readlane(nf, s));
+      } else {  // partial partition of rank e - nfull_all
+        s = __builtin_ctzll(__builtin_amdgcn_ballot_w64(rm > 0 && rank == e - nfull_all));
+        split = __builtin_amdgcn_readlane(nf, s);
+      }
+      q0 = __builtin_amdgcn_readlane(sin.c0, s);
+      qn = __builtin_amdgcn_readlane(sin.q, s);
+      L = __builtin_amdgcn_readlane(sin.L, s);
+    } else {
+      const DecWork w = items[e];
+      s = w.seq;
+      split = w.split;
+      q0 = w.q0;
+      qn = w.qn;
+      L = w.L;
+    }
     const int kb = split * P;
     const int ke = min(L, kb + P);
     const int nsplit = (L + P - 1) / P;
@@ -803,6 +870,28 @@ void decode_kernel(
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(pq + 32 * kk);
         qf[kk] = __builtin_bit_cast(bf16x8, qrow ? x : u32x4{0u, 0u, 0u, 0u});
+      }
+    }
+
+    if constexpr (SELF) {
+      // this step's new rows inside the partition, at this KV head (row p is token
+      // q0 + p - (L - qn)), skipped where the slot mapping gives none; stored before any load
+      if (sp.w.k) {
+        constexpr int CPR = D / 8;    // 16-byte chunks of a row at one KV head
+        constexpr int RPP = 64 / CPR;  // rows per pass of the wave
+        const int c = lane % CPR;
+        for (int p = max(kb, L - qn) + lane / CPR; p < ke; p += RPP) {
+          const int j = bdiv.div(p);
+          const int32_t blk = bt_row[j];
+          const int64_t slot = (int64_t)blk * bs + (p - j * bs);
+          if (blk >= 0 && slot < sp.w.slots) {
+            const int64_t src = ((int64_t)(q0 + p - (L - qn)) * Hkv + kvh) * CPR + c;
+            const int64_t dst = (slot * Hkv + kvh) * CPR + c;
+            sp.w.k_cache[dst] = sp.w.k[src];
+            sp.w.v_cache[dst] = sp.w.v[src];
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       }
     }
 
@@ -886,6 +975,7 @@ void decode_kernel(
         if (g == 0) lse_part[base] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
       }
     }
+    if constexpr (SELF) break;  // every item is taken in the first round
     int next = 0;
     if (lane == 0) next = atomicAdd(queue, 1);
     idx = nwaves + __builtin_amdgcn_readfirstlane(next);
@@ -1912,18 +2002,25 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
   }
   const int32_t beside = dst != st ? 1 : 0;
 
-  if (k_new) {
-    WriteArgs w{static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
-                static_cast<uint4*>(const_cast<void*>(k_cache)), static_cast<uint4*>(const_cast<void*>(v_cache)),
-                block_tables, (int32_t)((int64_t)num_kv_heads * head_dim * 2 / 16),
-                num_blocks * block_size};
+  WriteArgs w{};
+  if (k_new)
+    w = WriteArgs{static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                  static_cast<uint4*>(const_cast<void*>(k_cache)), static_cast<uint4*>(const_cast<void*>(v_cache)),
+                  block_tables, (int32_t)((int64_t)num_kv_heads * head_dim * 2 / 16),
+                  num_blocks * block_size};
+  // A decode-only batch of at most 64 sequences whose (partition, KV head) items stay below the
+  // waves of two 4-wave workgroups per compute unit plans itself inside the decode kernel (see
+  // SelfPlan): no planning launch.
+  const bool self_plan = p.pre_cap == 0 && num_seqs >= 1 && num_seqs <= 64 &&
+                         p.dec_cap * num_kv_heads < 2LL * (kDecodeWaves / 2) * cus;
+  if (!self_plan && k_new) {
     // one wave per token, 16 waves per workgroup
     const int64_t nw = std::min<int64_t>(cb::ceil_div(num_tokens, 16), 4 * (int64_t)cus);
     plan_write_kernel<<<(unsigned)(1 + nw), 1024, 0, st>>>(
         cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd, p.max_splits, p.bq, block_size,
         max_blocks_per_seq, max_kv_len, dec, p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus,
         p.pre_splits, num_tokens, 4 * head_dim, nsplit_tok, beside, w);
-  } else {
+  } else if (!self_plan) {
     plan_kernel<<<1, 1024, 0, st>>>(cu_seqlens_q, kv_lens, num_seqs, p.G, p.P, p.qmaxd,
                                     p.max_splits, p.bq, block_size, max_blocks_per_seq, max_kv_len, dec,
                                     p.dec_cap, pre, p.pre_cap, counts, num_kv_heads, cus, p.pre_splits,
@@ -1977,7 +2074,8 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
     // than waves has them dealt across the workgroups, and a grid between one and two per unit
     // would give some units twice the others' share (measured on 22 small decode-only batches:
     // up to 15% less time with whole rounds, never more than 2% more).
-    const int64_t items = p.dec_cap * num_kv_heads;
+    // (self-planned: at least one wave more than items, for the cache write)
+    const int64_t items = p.dec_cap * num_kv_heads + (self_plan ? 1 : 0);
     const int waves = dst != st ? kDecodeWaves : kDecodeWaves / 2;
     const int64_t per_cu = dst != st ? 1 : 2;
     int64_t groups = std::max<int64_t>(1, std::min<int64_t>((items + waves - 1) / waves, per_cu * (int64_t)cus));
@@ -1985,16 +2083,19 @@ int attention_impl(const void* q_packed, const int32_t* cu_seqlens_q, const int3
     const unsigned grid = (unsigned)groups;
     int32_t* queue = counts + 2;
     if (!record_if(tm, CB_KERNEL_DECODE, true, dst)) return fail(CB_ERR_HIP, "hipEventRecord failed");
-    if (head_dim == 128)
-      decode_kernel<128><<<grid, waves * 64, 0, dst>>>(
-          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
-          queue, num_q_heads, num_kv_heads, block_div(block_size), max_blocks_per_seq, p.P, p.max_splits,
-          p.qmaxd, scale_log2);
-    else
-      decode_kernel<64><<<grid, waves * 64, 0, dst>>>(
-          qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts,
-          queue, num_q_heads, num_kv_heads, block_div(block_size), max_blocks_per_seq, p.P, p.max_splits,
-          p.qmaxd, scale_log2);
+    const SelfPlan sp{w, num_seqs, num_tokens, max_kv_len, max_blocks_per_seq};
+    const BlockDiv bdiv = block_div(block_size);
+#define CB_DECODE_LAUNCH(DIM, SELF_)                                                             \
+  decode_kernel<DIM, SELF_><<<grid, waves * 64, 0, dst>>>(                                       \
+      qp, cu_seqlens_q, kv_lens, block_tables, kc, vc, op, o_part, lse_part, dec, counts, queue, \
+      num_q_heads, num_kv_heads, bdiv, max_blocks_per_seq, p.P, p.max_splits, p.qmaxd,          \
+      scale_log2, sp)
+    if (head_dim == 128) {
+      if (self_plan) CB_DECODE_LAUNCH(128, true); else CB_DECODE_LAUNCH(128, false);
+    } else {
+      if (self_plan) CB_DECODE_LAUNCH(64, true); else CB_DECODE_LAUNCH(64, false);
+    }
+#undef CB_DECODE_LAUNCH
     if (!record_if(tm, CB_KERNEL_DECODE, false, dst)) return fail(CB_ERR_HIP, "hipEventRecord failed");
   }
   if (dst != st) {

@@ -7,8 +7,9 @@ import zlib
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from gpu_helpers import Step, dev_bf16, host_u16, oracle_step, assert_close, say
+from gpu_helpers import Step, dev_bf16, dev_i32, host_u16, oracle_step, assert_close, say
 from pins import tiny_batch
 from test_gpu_parity import EDGE, _sample_tokens, check_full
 
@@ -120,3 +121,64 @@ def test_more_sequences_than_one_planning_pass(nseq, split):
     toks = np.concatenate([np.arange(0, 40), np.arange(nseq - 102, nseq - 2),
                            np.arange(b.num_tokens - 110, b.num_tokens)])
     check_full(b, step, tokens=toks)
+
+
+def _decode_call(b, cu, kv_lens, tables, max_kv_len, split, write):
+    """One attention call (with the cache write when ``write``) on fresh device copies of the
+    batch's caches; returns (k cache, v cache, out) as host bit patterns."""
+    kc, vc = dev_bf16(b.k_cache, "cuda"), dev_bf16(b.v_cache, "cuda")
+    q, k, v = dev_bf16(b.q, "cuda"), dev_bf16(b.k, "cuda"), dev_bf16(b.v, "cuda")
+    cu_d, kv_d = dev_i32(cu, "cuda"), dev_i32(kv_lens, "cuda")
+    tb_d = dev_i32(tables, "cuda")
+    out = torch.full((b.num_tokens, b.num_q_heads, b.head_dim), float("nan"),
+                     dtype=torch.bfloat16, device="cuda")
+    S = len(kv_lens)
+    ws = cb.alloc_workspace(S, b.num_tokens, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                            b.block_size, 1, max_kv_len, split, device="cuda")
+    if write:
+        cb.cb_paged_attention_write(q, k, v, cu_d, kv_d, tb_d, kc, vc, out, b.scale, 1, max_kv_len,
+                                    ws, kv_split_tokens=split)
+    else:
+        cb.cb_paged_attention(q, cu_d, kv_d, tb_d, kc, vc, out, b.scale, 1, max_kv_len, ws,
+                              kv_split_tokens=split)
+    torch.cuda.synchronize()
+    return host_u16(kc), host_u16(vc), host_u16(out)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("write", [True, False])
+def test_self_planned_decode_matches_planned(D, write):
+    """A decode-only batch of 64 sequences plans inside the decode kernel (no planning launch);
+    the same batch with a 65th sequence holding no tokens takes the planned path. Same partition
+    size: caches and every output row must match bit for bit. One sequence is longer than the
+    max_kv_len bound (by more than the partitions cover): no attention item in either path
+    (its output row stays as it was), but its token is still written to the cache."""
+    Hq, Hkv, bs, split, bound = 16, 4, 16, 128, 600
+    rng = np.random.default_rng(4100 + D)
+    lens = [int(x) for x in rng.integers(1, bound + 1, 64)]
+    lens[5] = 690  # ceil(690 / 128) = 6 partitions > ceil(600 / 128) = 5: nothing merges it
+    b = tiny_batch([synth.SeqSpec(1, n) for n in lens], Hq, Hkv, D, bs, seed=4100 + D)
+    assert cb.cb_paged_attention_split_tokens(64, Hq, Hkv, 1, bound, split) == split
+    say(f"[fused] self-planned vs planned D={D} write={write}")
+    mine = _decode_call(b, b.cu_seqlens_q, b.kv_lens, b.block_tables, bound, split, write)
+    cu65 = np.append(b.cu_seqlens_q, b.cu_seqlens_q[-1]).astype(np.int32)
+    kv65 = np.append(b.kv_lens, 0).astype(np.int32)
+    tb65 = np.concatenate([b.block_tables, np.full((1, b.block_tables.shape[1]), -1, np.int32)])
+    ref = _decode_call(b, cu65, kv65, tb65, bound, split, write)
+    for name, x, y in zip(("k cache", "v cache", "out"), mine, ref):
+        assert np.array_equal(x, y), f"{name} differs between the self-planned and planned paths"
+    # the long sequence's row was not written by attention; the other rows were, and (with the
+    # write) agree with the oracle
+    nan = host_u16(torch.full((1,), float("nan"), dtype=torch.bfloat16))[0]
+    out = mine[2].reshape(b.num_tokens, Hq, D)
+    assert np.all(out[5] == nan)
+    rest = [t for t in range(b.num_tokens) if t != 5]
+    assert not np.any(out[rest] == nan)
+    if write:
+        got = oracle.bf16_to_f64(out[rest])
+        assert_close(got, oracle_step(b, tokens=rest)[2][rest], "self-planned decode")
+        # the long sequence's token reached the cache at its slot
+        kc0 = b.k_cache.reshape(-1, Hkv, D)
+        slot = int(b.block_tables[5][(690 - 1) // bs]) * bs + (690 - 1) % bs
+        got = mine[0].reshape(-1, Hkv, D)[slot]
+        assert np.array_equal(got, b.k[5]) and not np.array_equal(got, kc0[slot])
