@@ -12,6 +12,8 @@
 // one 16-row MFMA tile (q * G <= 16) is decode-type: its KV range is cut into partitions of P
 // tokens, and each (partition, KV head) item is streamed by one wave of a persistent decode
 // grid that takes items from a queue; several partitions are merged afterwards by log-sum-exp.
+// A small decode-only batch has no planning launch: the decode waves derive their items (and
+// write the step's K/V rows) themselves.
 // Longer chunks are prefill-type: one 8-wave workgroup per (256-row query tile, KV head) over
 // the tile's causal key range (split along the keys into parts when the batch has too few
 // tiles to fill the GPU), with 32-key K/V tiles staged in LDS and read by all 8 waves.

@@ -182,3 +182,22 @@ def test_self_planned_decode_matches_planned(D, write):
         slot = int(b.block_tables[5][(690 - 1) // bs]) * bs + (690 - 1) % bs
         got = mine[0].reshape(-1, Hkv, D)[slot]
         assert np.array_equal(got, b.k[5]) and not np.array_equal(got, kc0[slot])
+
+
+@pytest.mark.parametrize("G,q", [(4, 4), (2, 8), (1, 16)])
+def test_self_planned_write_across_partitions(G, q):
+    """Decode-type chunks of q > 1 tokens (q * G = 16) whose new rows straddle a partition
+    boundary (P = 32), 16 sequences: a self-planned batch, where the wave of each partition
+    stores its own share of the new rows before reading them. Caches bit-exact and outputs within
+    the tolerance, against the oracle."""
+    Hkv, D, bs, P = 4, 128, 16, 32
+    rng = np.random.default_rng(4300 + q)
+    lens = [P * int(rng.integers(1, 20)) + int(rng.integers(1, q)) for _ in range(16)]
+    b = tiny_batch([synth.SeqSpec(q, L) for L in lens], G * Hkv, Hkv, D, bs, seed=4300 + q)
+    say(f"[fused] self-planned write across partitions G={G} q={q}")
+    step = Step(b, kv_split_tokens=P)
+    kc, vc, out = fused(step, b, P)
+    _, (okc, ovc), oout, _ = oracle_step(b)
+    assert np.array_equal(host_u16(kc), okc), "k cache differs from the oracle"
+    assert np.array_equal(host_u16(vc), ovc), "v cache differs from the oracle"
+    assert_close(oracle.bf16_to_f64(host_u16(out)), oout, f"spec decode G={G} q={q}")
