@@ -201,3 +201,40 @@ def test_self_planned_write_across_partitions(G, q):
     assert np.array_equal(host_u16(kc), okc), "k cache differs from the oracle"
     assert np.array_equal(host_u16(vc), ovc), "v cache differs from the oracle"
     assert_close(oracle.bf16_to_f64(host_u16(out)), oout, f"spec decode G={G} q={q}")
+
+
+def _random_small_decode_batch(seed):
+    """A seeded decode-only batch within the self-planned bounds: 1-64 sequences, KV heads 1-8,
+    query heads per KV head 1-16, head_dim 64 or 128, block sizes 16-80, 1 to 16 / G query
+    tokens each, KV lengths up to 1500; a random partition request (0 = the library's choice),
+    dropped to the library's choice when the items would reach the waves."""
+    rng = np.random.default_rng(seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8, 16) if g * Hkv <= 64]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 48, 64, 80]))
+    S = int(rng.integers(1, 65))
+    specs = []
+    for _ in range(S):
+        q = int(rng.integers(1, 16 // G + 1))
+        specs.append(synth.SeqSpec(q, q + int(rng.integers(0, 1500))))
+    split = int(rng.choice([0, 64, 160, 512]))
+    max_kv = max(sp.L for sp in specs)
+    if split and S * -(-max_kv // split) * Hkv >= 1024:
+        split = 0
+    return tiny_batch(specs, G * Hkv, Hkv, D, bs, seed=seed), split
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_self_planned_random_batches(seed):
+    """Seeded small decode-only batches through the fused call against the oracle: caches bit
+    exact, outputs within the tolerance on every element."""
+    b, split = _random_small_decode_batch(6000 + seed)
+    say(f"[fused] self-planned random batch {seed}: S={b.num_seqs} Hq={b.num_q_heads} "
+        f"Hkv={b.num_kv_heads} D={b.head_dim} bs={b.block_size} split={split}")
+    step = Step(b, kv_split_tokens=split)
+    kc, vc, out = fused(step, b, split)
+    _, (okc, ovc), oout, _ = oracle_step(b)
+    assert np.array_equal(host_u16(kc), okc), "k cache differs from the oracle"
+    assert np.array_equal(host_u16(vc), ovc), "v cache differs from the oracle"
+    assert_close(oracle.bf16_to_f64(host_u16(out)), oout, f"random small decode batch {seed}")
