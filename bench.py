@@ -15,6 +15,8 @@ and the log-sum-exp merge) and "mixed_batch_70b" (64 q-heads / 8 KV heads, block
 128 decodes + chunked prefills, a 2048-token prefix shared by a quarter of the sequences).
 The mixed workloads also carry "decode_sub_batch": the decode KV rate of their decode rows
 alone (same cache and tables), over the whole attention call and over the decode kernel.
+"executor_step" is the --graphs measurement below (a 16-sequence decode step through the native
+step executor, waited for and back to back, with direct launches and with graph replay).
 "stream_read" is the measured streaming-read rate of this GPU (cb_stream_read over 2 GiB), which
 the decode rooflines are also reported against. The headline step runs the given W warm-up and
 K timed steps; the further workloads, and the prefill roofline's chunks-alone launches, are timed
@@ -876,6 +878,12 @@ GRAPHS_SHAPE = dict(seqs=16, q_heads=32, kv_heads=8, head_dim=128, block_size=16
 
 def bench_graphs(args):
     """Eager vs recorded steps on a launch-bound decode batch; prints one JSON line."""
+    print(json.dumps(graphs_result(args)), flush=True)
+
+
+def graphs_result(args):
+    """The step-graph measurement as a dict (its own JSON line, or the default run's
+    "executor_step" sub-object)."""
     import numpy as np
     import torch
     import ragged_paged_kv_amd as cb
@@ -1006,7 +1014,7 @@ def bench_graphs(args):
         "roofline": None,
         "cpu_baseline": None,
     }
-    print(json.dumps(res), flush=True)
+    return res
 
 
 ASYNC_SHAPE = dict(seqs=64, q_heads=32, kv_heads=8, head_dim=128, block_size=16, kv_lo=512,
@@ -1216,6 +1224,8 @@ def main():
         res["mixed_batch"] = sub_result(args, 3, stream["gbs"], 8.0)
         res["long_context_decode"] = sub_result(args, 4, stream["gbs"], 8.0)
         res["mixed_batch_70b"] = sub_result(args, 5, stream["gbs"], 8.0)
+        # the small launch-bound decode step through the native step executor
+        res["executor_step"] = graphs_result(args)
     print(json.dumps(res), flush=True)
 
 
