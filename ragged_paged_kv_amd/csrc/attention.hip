@@ -362,8 +362,18 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
     if ((tid & 63) == 0 && dk > 0) atomicAdd(&dec_keys, dk);
     if (np > 0) {
       atomicMax(&max_pre_len, in.L);
+      // 32-key steps of the sequence's query tiles: tile t sees keys [0, L - q + min(q, (t + 1) bq)).
+      // With bq a multiple of 32 the full tiles 0 .. np - 2 add bq / 32 steps each to the first
+      // one's ceil((L - q) / 32) + bq / 32 (closed form instead of a loop over the tiles, which
+      // took microseconds for long chunks); the last tile sees all L keys.
       unsigned long long stp = 0;
-      for (int t = 0; t < np; ++t) stp += (in.L - in.q + min(in.q, (t + 1) * bq) + 31) / 32;
+      if ((bq & 31) == 0) {
+        const unsigned long long m = (unsigned long long)(np - 1);
+        stp = m * (unsigned long long)((in.L - in.q + 31) / 32) +
+              (unsigned long long)(bq / 32) * m * (m + 1) / 2 + (unsigned long long)((in.L + 31) / 32);
+      } else {
+        for (int t = 0; t < np; ++t) stp += (in.L - in.q + min(in.q, (t + 1) * bq) + 31) / 32;
+      }
       atomicAdd(&pre_steps, stp);
     }
     const int2 inc = block_scan2(nfull, np, wsum);
@@ -441,7 +451,7 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
       }
       const int incp = block_scan2(nit, 0, wsum).x;
       int64_t ep = (int64_t)base[1] + incp - nit;
-      if (emax > 1) {
+      if (emax > 1) {  // few tiles: each sequence's thread writes its tiles' parts
         for (int tl = pn - 1; tl >= 0; --tl) {
           int ns, chunk;
           prefill_split(L - qn + min(qn, (tl + 1) * bq), emax, ns, chunk);
@@ -449,8 +459,28 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ cu,
             if (ep < pre_cap) pre[ep] = Work{s, tl * kMaxPreSplits + part, pin.c0, qn, L, 0, 0, 0};
         }
       } else {
-        for (int k = 0; k < pn; ++k)
-          if (ep + k < pre_cap) pre[ep + k] = Work{s, (pn - 1 - k) * kMaxPreSplits, pin.c0, qn, L, 0, 0, 0};
+        // one item per tile, written by all threads as the full decode partitions are: item i
+        // belongs to the last thread t with first_item[t] <= i, as tile pn_t - 1 - (i -
+        // first_item[t]) of its sequence (a long chunk's tiles, one thread each, took
+        // microseconds)
+        first_item[tid] = incp - nit;
+        sh_c0[tid] = pin.c0;
+        sh_q[tid] = qn;
+        sh_L[tid] = L;
+        __syncthreads();
+        const int pass_items = wsum[15].x;
+        for (int i = tid; i < pass_items; i += 1024) {
+          int lo = 0, hi = 1023;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (first_item[mid] <= i) lo = mid; else hi = mid - 1;
+          }
+          const int pn_lo = (sh_q[lo] + bq - 1) / bq;
+          const int64_t ed = (int64_t)base[1] + i;
+          if (ed < pre_cap)
+            pre[ed] = Work{s0 + lo, (pn_lo - 1 - (i - first_item[lo])) * kMaxPreSplits, sh_c0[lo],
+                           sh_q[lo], sh_L[lo], 0, 0, 0};
+        }
       }
       __syncthreads();
       if (tid == 1023) base[1] += incp;
